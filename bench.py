@@ -1,0 +1,210 @@
+"""Benchmark of one device's forward ring pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A "step" here is one whole ring pass of the hot path for one device: N ring steps, each a
+fused attention-step kernel (QK^T, mask, online softmax, PV, merge into the running
+(O, LSE)), the double-buffered KV staging copies on the side stream, and the final cast.
+Inputs are seeded synthetic N(0, 1) bf16 tensors resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is useful attention TFLOP/s (4 h d FLOPs per allowed
+(query, key) pair; causal pairs above the diagonal do not count).  `roofline` reports the
+step kernel (the dominant kernel) against the bf16 dense MFMA peak, from per-launch HIP
+events on the compute stream; `cpu_baseline` times the fp64 oracle on a bounded sample of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOADS = {
+    # name: (description, sizes, layout, causal, shard, seed)
+    "striped_causal_32k": ("ring_fwd striped causal, S=262144 N=8 L=32768 h=32 n_kv=8 d=128 "
+                           "bf16, shard 0", dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8),
+                           "striped", True, 0, 1004),
+    "zigzag_causal_32k": ("ring_fwd zigzag causal, S=262144 N=8 L=32768 h=32 n_kv=8 d=128 bf16, "
+                          "shard 0", dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8),
+                          "zigzag", True, 0, 1004),
+    "noncausal_32k": ("ring_fwd non-causal, S=262144 N=8 L=32768 h=32 n_kv=8 d=128 bf16, shard 0",
+                      dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "contiguous", False, 0, 1003),
+    "contiguous_causal_32k_shard7": ("ring_fwd contiguous causal, S=262144 N=8 L=32768 h=32 "
+                                     "n_kv=8 d=128 bf16, shard 7",
+                                     dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8),
+                                     "contiguous", True, 7, 1003),
+    "noncausal_gqa_8k": ("ring_fwd non-causal GQA, S=65536 N=8 L=8192 h=32 n_kv=8 d=128 bf16, "
+                         "shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
+                         "contiguous", False, 0, 1002),
+}
+DEFAULT_WORKLOAD = "striped_causal_32k"
+METRIC = "ring-step attention TFLOP/s (bf16, causal) and % of MI355X MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0):
+    """Time the fp64 oracle on whole query rows (all heads, every key of the sequence)
+    until about budget_s seconds of CPU work; report useful TFLOP/s of that sample."""
+    from oracle import allowed_pairs, shard_attention, shard_tokens  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q = inp["q"].astype(np.float64)
+    k_all = inp["k_all"].astype(np.float64)
+    v_all = inp["v_all"].astype(np.float64)
+    N, L, h, d = cfg["N"], cfg["L"], cfg["h"], cfg["d"]
+    toks = shard_tokens(layout, N, L)
+    all_pos = np.sort(np.concatenate(toks))
+    rng = np.random.default_rng(99)
+    rows_done, pairs, elapsed = [], 0, 0.0
+    chunk = 16
+    while elapsed < budget_s and len(rows_done) < L:
+        rows = rng.choice(L, size=chunk, replace=False)
+        t0 = time.perf_counter()
+        shard_attention(q, k_all, v_all, N=N, shard=shard, layout=layout, causal=causal, rows=rows)
+        elapsed += time.perf_counter() - t0
+        rows_done.extend(rows.tolist())
+        if causal:
+            pairs += int(np.searchsorted(all_pos, toks[shard][rows], side="right").sum())
+        else:
+            pairs += chunk * N * L
+    flops = 4.0 * h * d * pairs * cfg["b"]
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(rows_done)} random query rows of shard {shard} x all {h} heads against "
+                      f"all {N * L} keys (fp64 numpy, {elapsed:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
+              "(the ring's other devices are emulated on the one GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ring_attention_long_amd as ra
+    import synth
+    from ring_attention_long_amd import accounting
+
+    desc, cfg, layout, causal, shard, seed = WORKLOADS[args.workload]
+    b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
+    log(f"[bench] workload {args.workload}: {desc}")
+    inp = synth.shard_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16")
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"]).to(dev, torch.bfloat16)
+    k_all = torch.from_numpy(inp["k_all"]).to(dev, torch.bfloat16)
+    v_all = torch.from_numpy(inp["v_all"]).to(dev, torch.bfloat16)
+    ws = torch.empty(ra.ring_workspace_bytes(q, k_all, causal=causal, layout=layout),
+                     device=dev, dtype=torch.uint8)
+    o = torch.empty_like(q)
+    lse = torch.empty((b, h, L), device=dev, dtype=torch.float32)
+    pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+    flops = accounting.flops_from_pairs(pairs, h, d)
+    compute = torch.cuda.current_stream()
+
+    def one_pass():
+        ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws,
+                    out=o, lse_out=lse)
+
+    for i in range(args.warmup):
+        one_pass()
+        log(f"[bench] warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(compute)
+    for _ in range(args.steps):
+        one_pass()
+    t1.record(compute)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+
+    # Per-launch durations of the step kernel, from HIP events on the compute stream.
+    step_ms, live_flops, timings = [], 0, []
+    for _ in range(3):
+        _, _, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
+                                     workspace=ws, out=o, lse_out=lse)
+        timings.append(tm)
+    tm = timings[-1]
+    for k in range(N):
+        src = (shard - k) % N
+        if tm["step_begin_ms"][k] >= 0:
+            step_ms.append(tm["step_end_ms"][k] - tm["step_begin_ms"][k])
+            live_flops += accounting.flops_from_pairs(
+                ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal,
+                                 layout=layout), h, d)
+    kern_ms = sum(step_ms)
+    achieved = live_flops / (kern_ms * 1e-3) / 1e12
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    # copy / compute overlap per ring step: fraction of the copy staging step k+1 that ran
+    # while step k's kernel ran
+    overlap = []
+    for k in range(1, N):
+        cb, ce = tm["copy_begin_ms"][k], tm["copy_end_ms"][k]
+        sb, se = tm["step_begin_ms"][k - 1], tm["step_end_ms"][k - 1]
+        if cb < 0 or sb < 0 or ce <= cb:
+            continue
+        overlap.append(max(0.0, min(ce, se) - max(cb, sb)) / (ce - cb))
+    kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
+    copy_ms = [tm["copy_end_ms"][k] - tm["copy_begin_ms"][k] for k in range(1, N)
+               if tm["copy_begin_ms"][k] >= 0]
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) bf16 Q/K/V from seeded numpy PCG64",
+        "config": {"workload": desc, "S": N * L, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv,
+                   "d": d, "layout": layout, "causal": causal, "q_shard": shard,
+                   "useful_tflop_per_pass": round(flops / 1e12, 4),
+                   "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "step_fwd_bf16_kernel<MODE_MERGE/MODE_PART>",
+                     "launches": len(step_ms),
+                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4)},
+        "staging": {"kv_bytes_per_step": kv_bytes,
+                    "copy_ms": [round(x, 4) for x in copy_ms],
+                    "copy_GBps": [round(2 * kv_bytes / (x * 1e-3) / 1e9, 1) for x in copy_ms if x > 0],
+                    "overlap_fraction_per_step": [round(x, 4) for x in overlap],
+                    "step_kernel_ms": [round(x, 4) for x in step_ms]},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, layout, causal, shard, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

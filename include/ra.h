@@ -1,0 +1,164 @@
+/*
+ * ra.h — C-ABI of libra: one device's share of Ring Attention on an AMD Instinct MI355X
+ * (gfx950), in hand-written HIP.
+ *
+ * The method (Ring Attention with Blockwise Transformers):
+ *   Device i of an N-device ring keeps its query shard Q_i (L = S/N tokens) resident while
+ *   the N key/value shards pass by in ring order; at ring step k it holds the KV shard of
+ *   device (i - k) mod N (page 4, "The Ring Communication Protocol").  It attends Q_i to
+ *   each shard as it arrives, carrying the online-softmax state across steps (page 1,
+ *   "Blockwise Attention and Online Softmax Formulations"), and the result equals plain
+ *   softmax attention over the whole sequence.  Causal masking is by global token
+ *   position, under one of three sequence layouts (page 1, "Causal Masking Dynamics:
+ *   Striped Attention and Zig-Zag Topologies").  Grouped-query attention shares each KV
+ *   head between h / n_kv consecutive query heads (page 3, section 2).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named q, k, v, o, lse, ws, ... are DEVICE pointers owned by the caller,
+ *     16-byte aligned.  The library never allocates or frees device memory.
+ *   - Streams are hipStream_t values passed as ra_stream (NULL = the null stream).  Calls
+ *     only enqueue work and return; they never synchronise (except ra_ring_fwd_timed).
+ *   - Every argument is validated before anything is enqueued; on any error nothing is
+ *     written and a negative ra_status is returned, with detail in ra_last_error().
+ *   - Tensor layouts (row-major, innermost last), matching the pages' (batch, seq_block,
+ *     heads, head_dim) layout (page 1, "Practical Implementation Patterns"):
+ *         q, o, dout           [b][L][h][d]
+ *         k, v (one shard)     [b][L][n_kv][d]
+ *         k_all, v_all         [N][b][L][n_kv][d]   shard j in its own local order
+ *         lse, delta           [b][h][L]            fp32
+ *   - LSE is the natural-log softmax denominator of each query row, in units of the scaled
+ *     logit: LSE = m + ln(sum_j exp(s_j - m)), s_j = scale * q.k_j.  A row with no
+ *     allowed key has LSE = -inf and O = 0.
+ *   - Thread safety: the library holds no mutable global state; calls are reentrant.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ra_status;
+#define RA_OK 0
+#define RA_ERR_INVALID_ARG (-1) /* bad shape, index, enum, null or misaligned pointer   */
+#define RA_ERR_UNSUPPORTED (-2) /* valid problem with no kernel (e.g. bf16 with d != 128) */
+#define RA_ERR_WORKSPACE (-3)   /* workspace smaller than ra_ring_fwd_workspace()        */
+#define RA_ERR_HIP (-4)         /* a HIP call or launch failed                            */
+
+/* Sequence layouts (page 1, "Causal Masking Dynamics"; page 3, section 6). */
+#define RA_LAYOUT_CONTIGUOUS 0 /* shard p holds tokens [pL, pL+L)                             */
+#define RA_LAYOUT_STRIPED 1    /* token t lives on shard t mod N (local index t div N)          */
+#define RA_LAYOUT_ZIGZAG 2     /* 2N chunks of L/2; shard p holds chunk p then chunk 2N-1-p     */
+
+/* Element types of q, k, v, o (and dout). */
+#define RA_F32 0
+#define RA_BF16 1
+
+/* The problem, after the pages' problem statement: Q/K/V shapes, ring size N, causal
+ * flag and sharding layout.  All sizes are per shard; the sequence length is S = N * L. */
+typedef struct ra_problem {
+  int32_t b;      /* batch                                                        */
+  int32_t L;      /* tokens per shard (>= 1; even for zigzag)                      */
+  int32_t h;      /* query heads                                                   */
+  int32_t n_kv;   /* key/value heads; h % n_kv == 0; query head hq reads hq/(h/n_kv) */
+  int32_t d;      /* head dimension: bf16 supports 128; fp32 supports 64 and 128    */
+  int32_t N;      /* ring size = number of shards (>= 1)                           */
+  int32_t causal; /* 0 or 1                                                        */
+  int32_t layout; /* RA_LAYOUT_*; only matters when causal = 1                      */
+  int32_t dtype;  /* RA_F32 or RA_BF16                                             */
+  float scale;    /* softmax scale on q.k; <= 0 selects 1/sqrt(d)                   */
+} ra_problem;
+
+typedef void* ra_stream; /* a hipStream_t */
+
+/* ---------------------------------------------------------------------------------------
+ * ra_step_fwd — one ring step.
+ * Attends shard q_shard's queries to the single KV shard kv_shard (the block a device
+ * holds at one step of the ring; page 1, "The Ring Attention Protocol"), masked by global
+ * positions when causal.  Writes the step's normalised partial: o_part [b][L][h][d] fp32
+ * and lse_part [b][h][L] fp32; rows with no allowed key in this shard get (0, -inf).
+ * q is [b][L][h][d] and k, v are [b][L][n_kv][d] in p->dtype.
+ * ------------------------------------------------------------------------------------- */
+ra_status ra_step_fwd(const ra_problem* p, int32_t q_shard, int32_t kv_shard, const void* q,
+                      const void* k, const void* v, float* o_part, float* lse_part,
+                      ra_stream stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ra_merge_lse — combine a step's partial into the running result, in place.
+ * Page 2, "FlashAttention Integration": partial outputs are rescaled to the new maximum
+ * and summed; page 3, section 3: the whole state must be carried, not O alone.  In
+ * (O, LSE) form:  lse = ln(exp(lse_acc) + exp(lse_part)) (computed around the maximum),
+ * o_acc = exp(lse_acc - lse) o_acc + exp(lse_part - lse) o_part.  (0, -inf) is the
+ * identity: start the accumulator at o_acc = 0, lse_acc = -inf.  All fp32;
+ * o_acc, o_part [b][L][h][d]; lse_acc, lse_part [b][h][L].  p->dtype is ignored.
+ * ------------------------------------------------------------------------------------- */
+ra_status ra_merge_lse(const ra_problem* p, float* o_acc, float* lse_acc, const float* o_part,
+                       const float* lse_part, ra_stream stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ra_finalize — write the merged fp32 output o_acc [b][L][h][d] in p->dtype (bf16 round to
+ * nearest even, or an fp32 copy) to o (page 1: the final output after the last step).
+ * ------------------------------------------------------------------------------------- */
+ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_stream stream);
+
+/* Bytes of device workspace ra_ring_fwd needs: two KV staging buffers (the double buffer of
+ * page 1, "Practical Implementation Patterns") plus, unless dtype is fp32, an fp32 output
+ * accumulator.  Returns 0 if p is invalid. */
+size_t ra_ring_fwd_workspace(const ra_problem* p);
+
+/* ---------------------------------------------------------------------------------------
+ * ra_ring_fwd — the whole forward ring pass of device q_shard.
+ * Step k = 0..N-1 attends q to KV shard (q_shard - k) mod N and merges the partial into the
+ * running (O, LSE); the final o [b][L][h][d] (p->dtype) and lse [b][h][L] (fp32) equal
+ * plain softmax attention of q over the whole sequence.  The KV shard of step k+1 is
+ * copied into the idle half of a double buffer on the `copy` stream while step k computes
+ * on `compute` (the ring's receive from the previous device, emulated on one GPU; page 1,
+ * "The Ring Attention Protocol and Overlapped Communication").  Step 0 reads the local
+ * shard in place.  Steps whose KV shard is entirely in the causal future are skipped
+ * (their copy still runs).  `copy` may be NULL or equal to `compute` (copies then run in
+ * order on `compute`).  All work has finished when work queued on `compute` after this
+ * call runs.  ws must hold ra_ring_fwd_workspace(p) bytes.
+ * ------------------------------------------------------------------------------------- */
+ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                      const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
+                      ra_stream compute, ra_stream copy);
+
+/* Per-step timings reported by ra_ring_fwd_timed, in milliseconds from an event recorded
+ * on `compute` at entry; -1 where a step was skipped or no copy ran. */
+#define RA_MAX_TIMED_STEPS 64
+typedef struct ra_ring_timing {
+  int32_t n_steps;
+  float step_begin_ms[RA_MAX_TIMED_STEPS];
+  float step_end_ms[RA_MAX_TIMED_STEPS];
+  float copy_begin_ms[RA_MAX_TIMED_STEPS]; /* copy that stages the KV of step k */
+  float copy_end_ms[RA_MAX_TIMED_STEPS];
+  float total_ms;
+} ra_ring_timing;
+
+/* ra_ring_fwd_timed — ra_ring_fwd with timing events around every step kernel (on
+ * `compute`) and every staging copy (on `copy`).  Same results as ra_ring_fwd; unlike every
+ * other entry point it synchronises `compute` before returning.  Requires N <= 64.  For
+ * measurement (per-step compute time, copy/compute overlap); t is a host pointer. */
+ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
+                            const void* k_all, const void* v_all, void* o, float* lse, void* ws,
+                            size_t ws_bytes, ra_stream compute, ra_stream copy,
+                            ra_ring_timing* t);
+
+/* Host-only (no GPU work): number of (query, key) pairs shard q_shard may attend to in KV
+ * shard kv_shard (or the whole sequence when kv_shard = -1), summed over the batch.  Useful
+ * FLOPs of the forward are 4 * d * h * pairs (page 3, section 2: two GEMMs, 2 FLOPs per
+ * multiply-add).  Returns -1 on invalid arguments. */
+int64_t ra_allowed_pairs(const ra_problem* p, int32_t q_shard, int32_t kv_shard);
+
+/* Static text for a status code, and the detail of the calling thread's last error. */
+const char* ra_status_string(ra_status s);
+const char* ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

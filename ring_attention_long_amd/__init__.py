@@ -1,0 +1,202 @@
+"""ring_attention_long_amd — one device's share of Ring Attention on MI355X (gfx950).
+
+A thin torch-facing binding over libra.so (include/ra.h).  Every step of the computation
+runs in the library's HIP kernels; this module only checks tensor shapes, allocates the
+outputs with torch and passes device pointers and HIP streams through ctypes.
+
+Entry points (same names as the C-ABI, without the ``ra_`` prefix):
+    step_fwd      one ring step: queries of one shard against one KV shard -> (O, LSE) partial
+    merge_lse     in-place merge of a partial into a running (O, LSE)
+    finalize      fp32 accumulator -> output dtype
+    ring_fwd      the whole forward ring pass of one device (double-buffered KV staging on a
+                  side stream)
+    ring_fwd_timed  ring_fwd plus per-step kernel and copy timings
+    allowed_pairs   host-side count of allowed (query, key) pairs (useful-FLOP accounting)
+
+Tensor layouts (page 1, "Practical Implementation Patterns": batch, sequence, heads, dim):
+    q, o [b, L, h, d];  k, v [b, L, n_kv, d];  k_all, v_all [N, b, L, n_kv, d];
+    lse [b, h, L] fp32 (natural log, scaled-logit units).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, check
+
+__all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
+           "make_problem", "RaError", "library_path"]
+
+_DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
+_copy_streams: dict[int, torch.cuda.Stream] = {}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def make_problem(*, b, L, h, n_kv, d, N, causal=False, layout="contiguous",
+                 dtype=torch.bfloat16, scale=None) -> RaProblem:
+    if layout not in RA_LAYOUT:
+        raise ValueError(f"layout must be one of {sorted(RA_LAYOUT)}")
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    return RaProblem(b, L, h, n_kv, d, N, int(bool(causal)), RA_LAYOUT[layout], _DTYPES[dtype],
+                     0.0 if scale is None else float(scale))
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s) -> ctypes.c_void_p:
+    if s is None:
+        s = torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes_from_q(q, kv):
+    b, L, h, d = q.shape
+    n_kv = kv.shape[-2]
+    return b, L, h, n_kv, d
+
+
+def step_fwd(q, k, v, *, N, q_shard, kv_shard, causal=False, layout="contiguous", scale=None,
+             stream=None):
+    """One ring step: shard q_shard's queries q [b, L, h, d] against the keys/values of shard
+    kv_shard (k, v [b, L, n_kv, d]).  Returns the normalised partial (o_part [b, L, h, d]
+    fp32, lse_part [b, h, L] fp32); rows with no allowed key get (0, -inf)."""
+    b, L, h, n_kv, d = _shapes_from_q(q, k)
+    _need(q, "q", (b, L, h, d), q.dtype)
+    _need(k, "k", (b, L, n_kv, d), q.dtype)
+    _need(v, "v", (b, L, n_kv, d), q.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    o = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
+    lse = torch.empty((b, h, L), device=q.device, dtype=torch.float32)
+    check(_lib.lib().ra_step_fwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(o), _ptr(lse), _stream(stream)), "ra_step_fwd")
+    return o, lse
+
+
+def merge_lse(o_acc, lse_acc, o_part, lse_part, *, stream=None):
+    """In place: (o_acc, lse_acc) <- merge of (o_acc, lse_acc) and (o_part, lse_part).
+    All fp32; o [b, L, h, d], lse [b, h, L]."""
+    b, L, h, d = o_acc.shape
+    for t, n, shp in ((o_acc, "o_acc", (b, L, h, d)), (o_part, "o_part", (b, L, h, d)),
+                      (lse_acc, "lse_acc", (b, h, L)), (lse_part, "lse_part", (b, h, L))):
+        _need(t, n, shp, torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=torch.float32)
+    check(_lib.lib().ra_merge_lse(ctypes.byref(p), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
+                                  _ptr(lse_part), _stream(stream)), "ra_merge_lse")
+    return o_acc, lse_acc
+
+
+def finalize(o_acc, dtype=torch.bfloat16, *, stream=None):
+    """fp32 accumulator [b, L, h, d] -> new tensor of `dtype` (bf16: round to nearest even)."""
+    b, L, h, d = o_acc.shape
+    _need(o_acc, "o_acc", (b, L, h, d), torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=dtype)
+    o = torch.empty((b, L, h, d), device=o_acc.device, dtype=dtype)
+    check(_lib.lib().ra_finalize(ctypes.byref(p), _ptr(o_acc), _ptr(o), _stream(stream)),
+          "ra_finalize")
+    return o
+
+
+def copy_stream_for(device) -> torch.cuda.Stream:
+    """The side stream (default priority) used for KV staging on `device`."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _copy_streams:
+        _copy_streams[idx] = torch.cuda.Stream(device=idx)
+    return _copy_streams[idx]
+
+
+def ring_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None) -> int:
+    N, b, L, n_kv, d = k_all.shape
+    p = make_problem(b=b, L=L, h=q.shape[2], n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    return int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
+
+
+def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out):
+    N, b, L, n_kv, d = k_all.shape
+    h = q.shape[2]
+    _need(q, "q", (b, L, h, d), q.dtype)
+    _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
+    _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    need = int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_INVALID_ARG), "ra_ring_fwd_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    o = out if out is not None else torch.empty((b, L, h, d), device=q.device, dtype=q.dtype)
+    lse = lse_out if lse_out is not None else torch.empty((b, h, L), device=q.device,
+                                                          dtype=torch.float32)
+    _need(o, "o", (b, L, h, d), q.dtype)
+    _need(lse, "lse", (b, h, L), torch.float32)
+    return p, workspace, o, lse
+
+
+def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
+             stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None):
+    """Forward ring pass of device q_shard: q [b, L, h, d] against all N KV shards
+    k_all, v_all [N, b, L, n_kv, d] in ring order.  Returns (o [b, L, h, d] in q's dtype,
+    lse [b, h, L] fp32).  copy_stream="auto" stages KV on a side stream; None stages on
+    the compute stream."""
+    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    check(_lib.lib().ra_ring_fwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                 _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream),
+                                 ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
+          "ra_ring_fwd")
+    return o, lse
+
+
+def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
+                   stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None):
+    """ring_fwd plus timings (ms from entry): returns (o, lse, dict).  Synchronises."""
+    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    tm = RaRingTiming()
+    check(_lib.lib().ra_ring_fwd_timed(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all),
+                                       _ptr(v_all), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                       _stream(stream),
+                                       ctypes.c_void_p(cs.cuda_stream) if cs is not None else None,
+                                       ctypes.byref(tm)), "ra_ring_fwd_timed")
+    n = tm.n_steps
+    timing = {
+        "step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
+        "copy_begin_ms": list(tm.copy_begin_ms[:n]), "copy_end_ms": list(tm.copy_end_ms[:n]),
+        "total_ms": tm.total_ms,
+    }
+    return o, lse, timing
+
+
+def allowed_pairs(*, b=1, L, N, q_shard, kv_shard=-1, causal=True, layout="contiguous") -> int:
+    """Allowed (query, key) pairs of shard q_shard against kv_shard (-1: all shards), summed
+    over the batch.  Host-only; forward useful FLOPs = 4 * d * h * pairs."""
+    p = make_problem(b=b, L=L, h=1, n_kv=1, d=128, N=N, causal=causal, layout=layout,
+                     dtype=torch.bfloat16)
+    n = int(_lib.lib().ra_allowed_pairs(ctypes.byref(p), q_shard, kv_shard))
+    if n < 0:
+        raise ValueError("invalid arguments to allowed_pairs")
+    return n

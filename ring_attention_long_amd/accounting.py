@@ -1,0 +1,43 @@
+"""Work and traffic accounting for the ring pass (host-side arithmetic only).
+
+Formulas follow page 3 (section 2, invariants; section 4, arithmetic intensity; section 4.1,
+the per-step example) and page 1 ("Overlapping Arithmetic and Communication Ratios"):
+  * one non-causal step of L queries against L keys: 4 b L^2 h d FLOPs (two GEMMs,
+    2 FLOPs per multiply-add);
+  * with a causal mask only allowed pairs count: 4 h d FLOPs per allowed (query, key) pair;
+  * KV bytes received per step: 2 b L n_kv d p (K and V, p bytes per element);
+  * step intensity I_step = (h / n_kv) * L and whole-layer intensity
+    I = (h / n_kv) * S / (N - 1) FLOPs per received byte.
+"""
+from __future__ import annotations
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6    # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense
+MI355X_HBM_GBPS = 8000.0
+
+
+def step_flops_noncausal(b: int, L: int, h: int, d: int) -> int:
+    return 4 * b * L * L * h * d
+
+
+def flops_from_pairs(pairs: int, h: int, d: int) -> int:
+    """Useful forward FLOPs for `pairs` allowed (query, key) pairs per query head
+    (pairs already summed over the batch)."""
+    return 4 * h * d * pairs
+
+
+def kv_bytes_per_step(b: int, L: int, n_kv: int, d: int, elem_bytes: int) -> int:
+    return 2 * b * L * n_kv * d * elem_bytes
+
+
+def step_intensity(h: int, n_kv: int, S: int, N: int) -> float:
+    return (h / n_kv) * (S / N)
+
+
+def layer_intensity(h: int, n_kv: int, S: int, N: int) -> float:
+    return (h / n_kv) * S / (N - 1)
+
+
+def merge_bytes(b: int, L: int, h: int, d: int) -> int:
+    """HBM bytes of one standalone merge: read O_acc, O_part, write O_acc (fp32) plus the
+    same three passes over the LSE rows."""
+    return 3 * 4 * b * L * h * d + 3 * 4 * b * h * L

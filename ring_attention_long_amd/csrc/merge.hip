@@ -1,0 +1,113 @@
+// Bandwidth-bound kernels around the ring: the (O, LSE) merge of two partial results and
+// the final cast of the fp32 accumulator to the output type.
+//
+// Merge (page 2, "FlashAttention Integration"; page 3, section 3): the two partials are
+// normalised outputs over disjoint key sets with denominators exp(lse_acc) and
+// exp(lse_part).  Around M = max(lse_acc, lse_part) the weights are
+// wa = exp(lse_acc - M), wb = exp(lse_part - M); the merged row is (wa O_acc + wb O_part)
+// / (wa + wb) with LSE M + ln(wa + wb).  (0, -inf) is the identity and a pair of empty
+// rows stays (0, -inf).
+//
+// Each thread owns 4 consecutive floats (16-byte loads and stores); the d/4 threads of a
+// row sit in one wave, so every lane reads the row's old LSE before the lane holding the
+// row's first column overwrites it.
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void merge_kernel(float* __restrict__ o_acc,
+                                                    float* __restrict__ lse_acc,
+                                                    const float* __restrict__ o_part,
+                                                    const float* __restrict__ lse_part,
+                                                    int L, int h, int d4, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t row = i / d4;                 // row = (bi * L + t) * h + hq
+  const int col4 = (int)(i - row * d4);
+  const int hq = (int)(row % h);
+  const int64_t bt = row / h;
+  const int t = (int)(bt % L);
+  const int64_t bi = bt / L;
+  const int64_t li = (bi * h + hq) * L + t;
+  const float la = lse_acc[li], lb = lse_part[li];
+  const float M = fmaxf(la, lb);
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float wa = expf(la - M), wb = expf(lb - M);
+    const float tot = wa + wb;
+    const float fa = wa / tot, fb = wb / tot;
+    const f32x4 x = ((const f32x4*)o_acc)[i];
+    const f32x4 y = ((const f32x4*)o_part)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = fa * x[e] + fb * y[e];
+    lse = M + logf(tot);
+  }
+  ((f32x4*)o_acc)[i] = out;
+  if (col4 == 0) lse_acc[li] = lse;
+}
+
+__global__ __launch_bounds__(256) void finalize_bf16_kernel(const float* __restrict__ src,
+                                                            __bf16* __restrict__ dst,
+                                                            int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = ((const f32x4*)src)[2 * i];
+  const f32x4 b = ((const f32x4*)src)[2 * i + 1];
+  __bf16 r[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)a[e];       // round to nearest even
+    r[4 + e] = (__bf16)b[e];
+  }
+  ((u32x4*)dst)[i] = __builtin_bit_cast(u32x4, r);
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src,
+                                                       float* __restrict__ dst, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) ((f32x4*)dst)[i] = ((const f32x4*)src)[i];
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                        int b, int L, int h, int d, hipStream_t s) {
+  const int64_t n4 = (int64_t)b * L * h * d / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(n4)), dim3(256), 0, s, o_acc, lse_acc, o_part,
+                     lse_part, L, h, d / 4, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dtype == RA_BF16) {
+    hipLaunchKernelGGL(finalize_bf16_kernel, dim3(blocks_for(n / 8)), dim3(256), 0, s, o_acc,
+                       (__bf16*)o, n / 8);
+  } else {
+    if ((const void*)o_acc == o) return hipSuccess;
+    hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(n / 4)), dim3(256), 0, s, o_acc,
+                       (float*)o, n / 4);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(n)), dim3(256), 0, s, lse, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace ra

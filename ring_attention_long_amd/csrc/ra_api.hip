@@ -1,0 +1,358 @@
+// C-ABI of libra (declared in include/ra.h): argument validation, kernel launches and the
+// ring driver.
+//
+// The ring driver (page 1, "The Ring Attention Protocol and Overlapped Communication";
+// page 4, "The Ring Communication Protocol"): at step k device i attends its resident
+// queries to the KV shard of device (i - k) mod N and folds the partial into its running
+// (O, LSE).  On one GPU the other devices' shards are resident buffers and the receive
+// from the upstream neighbour is a device-to-device copy on a second stream into the idle
+// half of a double buffer (page 1, "Practical Implementation Patterns": a current and an
+// incoming KV buffer), overlapped with the current step's kernel.  Events order the two
+// streams: the copy that fills a buffer waits for the step that last read it, and a step
+// waits for the copy that filled its buffer.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ra_status fail(ra_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ra_status fail(ra_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+float effective_scale(const ra_problem* p) {
+  return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d);
+}
+
+constexpr int kMaxRing = 128;   // largest N the ring driver accepts
+
+// Shape and enum checks that do not depend on which kernels exist.
+ra_status check_shape(const ra_problem* p) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->b < 1 || p->L < 1 || p->h < 1 || p->n_kv < 1 || p->d < 1 || p->N < 1)
+    return fail(RA_ERR_INVALID_ARG, "sizes must be >= 1 (b=%d L=%d h=%d n_kv=%d d=%d N=%d)", p->b,
+                p->L, p->h, p->n_kv, p->d, p->N);
+  if (p->h % p->n_kv) return fail(RA_ERR_INVALID_ARG, "h=%d is not a multiple of n_kv=%d", p->h, p->n_kv);
+  if (p->causal != 0 && p->causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->layout < RA_LAYOUT_CONTIGUOUS || p->layout > RA_LAYOUT_ZIGZAG)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", p->layout);
+  if (p->dtype != RA_F32 && p->dtype != RA_BF16) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->layout == RA_LAYOUT_ZIGZAG && (p->L % 2))
+    return fail(RA_ERR_INVALID_ARG, "zigzag layout needs an even L (got %d)", p->L);
+  if (isnan(p->scale) || isinf(p->scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  const int64_t seq = (int64_t)p->N * p->L;
+  const int64_t q_elems = (int64_t)p->b * p->L * p->h * p->d;
+  if (seq > (int64_t)1 << 31 || q_elems > (int64_t)1 << 40)
+    return fail(RA_ERR_INVALID_ARG, "problem too large (S=%lld)", (long long)seq);
+  return RA_OK;
+}
+
+ra_status check_problem(const ra_problem* p) {
+  const ra_status s = check_shape(p);
+  if (s != RA_OK) return s;
+  if (p->dtype == RA_BF16 && p->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "bf16 kernels support d = 128 only (got %d)", p->d);
+  if (p->dtype == RA_F32 && p->d != 64 && p->d != 128)
+    return fail(RA_ERR_UNSUPPORTED, "fp32 kernels support d = 64 or 128 (got %d)", p->d);
+  return RA_OK;
+}
+
+ra_status check_shard(const ra_problem* p, int32_t s, const char* name) {
+  if (s < 0 || s >= p->N) return fail(RA_ERR_INVALID_ARG, "%s=%d outside [0, N=%d)", name, s, p->N);
+  return RA_OK;
+}
+
+ra_status check_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(RA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(RA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return RA_OK;
+}
+
+#define RA_TRY(x)                   \
+  do {                              \
+    const ra_status _s = (x);       \
+    if (_s != RA_OK) return _s;     \
+  } while (0)
+
+size_t elem_size(const ra_problem* p) { return p->dtype == RA_BF16 ? 2 : 4; }
+
+ra::StepArgs step_args(const ra_problem* p, int32_t qs, int32_t ks, const void* q, const void* k,
+                       const void* v, float* o, float* lse) {
+  ra::StepArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.b = p->b;
+  a.L = p->L;
+  a.h = p->h;
+  a.n_kv = p->n_kv;
+  a.d = p->d;
+  a.N = p->N;
+  a.causal = p->causal;
+  a.layout = p->layout;
+  a.q_shard = qs;
+  a.kv_shard = ks;
+  a.scale = effective_scale(p);
+  return a;
+}
+
+hipError_t launch_step(const ra_problem* p, const ra::StepArgs& a, int mode, hipStream_t s) {
+  return p->dtype == RA_BF16 ? ra::launch_step_bf16(a, mode, s) : ra::launch_step_f32(a, mode, s);
+}
+
+bool step_is_live(const ra_problem* p, int32_t qs, int32_t ks) {
+  return ra::kv_limit(p->causal, p->layout, p->N, p->L, qs, ks, p->L - 1) > 0;
+}
+
+// Event set of one ring pass; destroyed on every exit path.
+struct Events {
+  hipEvent_t e[2 + 2 * kMaxRing + 4 * RA_MAX_TIMED_STEPS] = {};
+  int n = 0;
+  ~Events() {
+    for (int i = 0; i < n; ++i)
+      if (e[i]) (void)hipEventDestroy(e[i]);
+  }
+  hipError_t make(hipEvent_t* out, bool timing) {
+    hipEvent_t ev = nullptr;
+    const hipError_t r = hipEventCreateWithFlags(&ev, timing ? hipEventDefault : hipEventDisableTiming);
+    if (r == hipSuccess) {
+      e[n++] = ev;
+      *out = ev;
+    }
+    return r;
+  }
+};
+
+ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
+                        const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
+                        ra_stream compute, ra_stream copy, ra_ring_timing* tm) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_shard(p, qs, "q_shard"));
+  RA_TRY(check_ptr(q, "q", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o, "o", 16));
+  RA_TRY(check_ptr(lse, "lse", 4));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const size_t need = ra_ring_fwd_workspace(p);
+  if (ws_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const int N = p->N;
+  if (tm && N > RA_MAX_TIMED_STEPS)
+    return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
+  if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
+
+  const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
+  const size_t A = align_up(shard_bytes, 256);
+  char* wsc = (char*)ws;
+  char* kbuf[2] = {wsc, wsc + 2 * A};
+  char* vbuf[2] = {wsc + A, wsc + 3 * A};
+  float* o_acc = p->dtype == RA_F32 ? (float*)o : (float*)(wsc + 4 * A);
+  float* lse_acc = lse;
+  const hipStream_t cs = (hipStream_t)compute;
+  const hipStream_t ps = copy ? (hipStream_t)copy : cs;
+  const bool split = ps != cs;
+  const bool timing = tm != nullptr;
+
+  Events ev;
+  hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
+  hipEvent_t t_sb[RA_MAX_TIMED_STEPS], t_se[RA_MAX_TIMED_STEPS], t_cb[RA_MAX_TIMED_STEPS],
+      t_ce[RA_MAX_TIMED_STEPS];
+  hipError_t e;
+  if ((e = ev.make(&entry, timing)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  for (int k = 0; k < N; ++k) {
+    if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (timing) {
+    tm->n_steps = N;
+    for (int k = 0; k < N; ++k) {
+      tm->step_begin_ms[k] = tm->step_end_ms[k] = tm->copy_begin_ms[k] = tm->copy_end_ms[k] = -1.f;
+      if ((e = ev.make(&t_sb[k], true)) != hipSuccess || (e = ev.make(&t_se[k], true)) != hipSuccess ||
+          (e = ev.make(&t_cb[k], true)) != hipSuccess || (e = ev.make(&t_ce[k], true)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+    }
+  }
+  bool live[kMaxRing];
+
+  // The copy stream must not read k_all / v_all before work the caller queued on `compute`.
+  if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (split && (e = hipStreamWaitEvent(ps, entry, 0)) != hipSuccess)
+    return hip_fail(e, "hipStreamWaitEvent");
+
+  bool have_acc = false;
+  const char* kc = (const char*)k_all;
+  const char* vc = (const char*)v_all;
+  for (int k = 0; k < N; ++k) {
+    // Stage the KV shard of step k+1 into buffer (k+1) % 2, last read by step k-1.
+    if (k + 1 < N) {
+      const int dst = (k + 1) & 1;
+      const int src = ((qs - (k + 1)) % N + N) % N;
+      if (split && k - 1 >= 1 && (e = hipStreamWaitEvent(ps, consumed[k - 1], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      if (timing && (e = hipEventRecord(t_cb[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipMemcpyAsync(kbuf[dst], kc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(K)");
+      if ((e = hipMemcpyAsync(vbuf[dst], vc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(V)");
+      if (timing && (e = hipEventRecord(t_ce[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipEventRecord(staged[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    // Step k on the shard of device (qs - k) mod N.
+    if (split && k >= 1 && (e = hipStreamWaitEvent(cs, staged[k], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    const int src = ((qs - k) % N + N) % N;
+    const void* kp = k == 0 ? (const void*)(kc + (size_t)qs * shard_bytes) : (const void*)kbuf[k & 1];
+    const void* vp = k == 0 ? (const void*)(vc + (size_t)qs * shard_bytes) : (const void*)vbuf[k & 1];
+    live[k] = step_is_live(p, qs, src);
+    if (live[k]) {
+      if (timing && (e = hipEventRecord(t_sb[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, o_acc, lse_acc);
+      if ((e = launch_step(p, a, have_acc ? ra::MODE_MERGE : ra::MODE_PART, cs)) != hipSuccess)
+        return hip_fail(e, "step kernel launch");
+      have_acc = true;
+      if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  const int64_t n_out = (int64_t)p->b * p->L * p->h * p->d;
+  if (!have_acc) {
+    // unreachable for valid problems (a shard always sees itself), kept for completeness
+    if ((e = ra::launch_fill_lse(o_acc, n_out, 0.f, cs)) != hipSuccess) return hip_fail(e, "fill kernel launch");
+    if ((e = ra::launch_fill_lse(lse_acc, (int64_t)p->b * p->h * p->L, -INFINITY, cs)) != hipSuccess)
+      return hip_fail(e, "fill kernel launch");
+  }
+  if (p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess)
+    return hip_fail(e, "finalize kernel launch");
+
+  if (timing) {
+    hipEvent_t done;
+    if ((e = ev.make(&done, true)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventRecord(done, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipEventSynchronize(done)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    (void)hipEventElapsedTime(&tm->total_ms, entry, done);
+    for (int k = 0; k < N; ++k) {
+      if (live[k]) {
+        (void)hipEventElapsedTime(&tm->step_begin_ms[k], entry, t_sb[k]);
+        (void)hipEventElapsedTime(&tm->step_end_ms[k], entry, t_se[k]);
+      }
+      if (k >= 1) {
+        (void)hipEventElapsedTime(&tm->copy_begin_ms[k], entry, t_cb[k]);
+        (void)hipEventElapsedTime(&tm->copy_end_ms[k], entry, t_ce[k]);
+      }
+    }
+  }
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK: return "ok";
+    case RA_ERR_INVALID_ARG: return "invalid argument";
+    case RA_ERR_UNSUPPORTED: return "unsupported problem";
+    case RA_ERR_WORKSPACE: return "workspace too small";
+    case RA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* ra_last_error(void) { return g_last_error.c_str(); }
+
+ra_status ra_step_fwd(const ra_problem* p, int32_t q_shard, int32_t kv_shard, const void* q,
+                      const void* k, const void* v, float* o_part, float* lse_part, ra_stream stream) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_shard(p, q_shard, "q_shard"));
+  RA_TRY(check_shard(p, kv_shard, "kv_shard"));
+  RA_TRY(check_ptr(q, "q", 16));
+  RA_TRY(check_ptr(k, "k", 16));
+  RA_TRY(check_ptr(v, "v", 16));
+  RA_TRY(check_ptr(o_part, "o_part", 16));
+  RA_TRY(check_ptr(lse_part, "lse_part", 4));
+  const ra::StepArgs a = step_args(p, q_shard, kv_shard, q, k, v, o_part, lse_part);
+  const hipError_t e = launch_step(p, a, ra::MODE_PART, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "step kernel launch");
+}
+
+ra_status ra_merge_lse(const ra_problem* p, float* o_acc, float* lse_acc, const float* o_part,
+                       const float* lse_part, ra_stream stream) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_ptr(o_acc, "o_acc", 16));
+  RA_TRY(check_ptr(lse_acc, "lse_acc", 4));
+  RA_TRY(check_ptr(o_part, "o_part", 16));
+  RA_TRY(check_ptr(lse_part, "lse_part", 4));
+  const hipError_t e =
+      ra::launch_merge(o_acc, lse_acc, o_part, lse_part, p->b, p->L, p->h, p->d, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "merge kernel launch");
+}
+
+ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_stream stream) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_ptr(o_acc, "o_acc", 16));
+  RA_TRY(check_ptr(o, "o", 16));
+  const hipError_t e = ra::launch_finalize(o_acc, o, p->dtype, (int64_t)p->b * p->L * p->h * p->d,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "finalize kernel launch");
+}
+
+size_t ra_ring_fwd_workspace(const ra_problem* p) {
+  if (check_problem(p) != RA_OK) return 0;
+  const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
+  size_t n = 4 * align_up(shard_bytes, 256);
+  if (p->dtype != RA_F32) n += align_up((size_t)p->b * p->L * p->h * p->d * 4, 256);
+  return n;
+}
+
+ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                      const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
+                      ra_stream compute, ra_stream copy) {
+  return ring_fwd_impl(p, q_shard, q, k_all, v_all, o, lse, ws, ws_bytes, compute, copy, nullptr);
+}
+
+ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
+                            const void* k_all, const void* v_all, void* o, float* lse, void* ws,
+                            size_t ws_bytes, ra_stream compute, ra_stream copy, ra_ring_timing* t) {
+  if (!t) return fail(RA_ERR_INVALID_ARG, "timing output is NULL");
+  return ring_fwd_impl(p, q_shard, q, k_all, v_all, o, lse, ws, ws_bytes, compute, copy, t);
+}
+
+int64_t ra_allowed_pairs(const ra_problem* p, int32_t q_shard, int32_t kv_shard) {
+  if (check_shape(p) != RA_OK) return -1;
+  if (q_shard < 0 || q_shard >= p->N || kv_shard < -1 || kv_shard >= p->N) return -1;
+  int64_t total = 0;
+  for (int ks = 0; ks < p->N; ++ks) {
+    if (kv_shard >= 0 && ks != kv_shard) continue;
+    for (int t = 0; t < p->L; ++t) total += ra::kv_limit(p->causal, p->layout, p->N, p->L, q_shard, ks, t);
+  }
+  return total * p->b;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP sources of libra.  Not part of the C-ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra.h"
+
+namespace ra {
+
+// ---------------------------------------------------------------------------------------
+// Global position of local token t of shard p (page 1, "Causal Masking Dynamics: Striped
+// Attention and Zig-Zag Topologies"; page 3, section 6):
+//   contiguous: shard p holds the consecutive tokens [pL, pL + L)
+//   striped:    token g lives on shard g mod N, so local t of shard p is global tN + p
+//   zigzag:     2N chunks of C = L/2 tokens; shard p holds chunk p, then chunk 2N-1-p
+// In every layout a shard's positions increase with t.
+// ---------------------------------------------------------------------------------------
+__host__ __device__ inline int64_t global_pos(int layout, int N, int L, int p, int t) {
+  if (layout == RA_LAYOUT_STRIPED) return (int64_t)t * N + p;
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int C = L / 2;
+    return t < C ? (int64_t)p * C + t : (int64_t)(2 * N - 1 - p) * C + (t - C);
+  }
+  return (int64_t)p * L + t;
+}
+
+__host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// ---------------------------------------------------------------------------------------
+// Key limit of query row t of shard qs against KV shard ks.
+//
+// The causal mask allows key u of shard ks for query t of shard qs iff
+// pos(ks, u) <= pos(qs, t) (inclusive; page 1, a token attends to positions j <= i).
+// Because positions increase with the local index in every layout, the allowed keys of a
+// row always form a prefix [0, limit) of the KV shard.  The mask of a whole (q-tile,
+// k-tile) pair therefore reduces to integer comparisons of key indices against per-row
+// limits: a k-tile is skipped when it starts at or beyond the largest limit of the
+// q-tile, needs no mask when it ends at or below the smallest one, and is masked only in
+// between (the diagonal).  Non-causal: every key is allowed.
+// ---------------------------------------------------------------------------------------
+__host__ __device__ inline int kv_limit(int causal, int layout, int N, int L, int qs, int ks,
+                                        int t) {
+  if (!causal) return L;
+  const int64_t P = global_pos(layout, N, L, qs, t);
+  if (layout == RA_LAYOUT_STRIPED) {
+    // keys of shard ks sit at uN + ks; count u >= 0 with uN + ks <= P
+    if (P < ks) return 0;
+    return (int)clamp64((P - ks) / N + 1, 0, L);
+  }
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int C = L / 2;
+    const int64_t a = clamp64(P - (int64_t)ks * C + 1, 0, C);
+    const int64_t b = clamp64(P - (int64_t)(2 * N - 1 - ks) * C + 1, 0, C);
+    return (int)(a + b);
+  }
+  return (int)clamp64(P - (int64_t)ks * L + 1, 0, L);
+}
+
+// Epilogue of a forward step kernel.
+enum StepMode : int {
+  MODE_PART = 0,   // write this step's normalised (O, LSE) partial
+  MODE_MERGE = 1,  // merge this step's partial into (O_acc, LSE_acc) in place
+};
+
+struct StepArgs {
+  const void* q;       // [b][L][h][d]
+  const void* k;       // [b][L][n_kv][d]
+  const void* v;       // [b][L][n_kv][d]
+  float* o;            // [b][L][h][d] fp32: partial (MODE_PART) or accumulator (MODE_MERGE)
+  float* lse;          // [b][h][L]    fp32
+  int b, L, h, n_kv, d, N;
+  int causal, layout;
+  int q_shard, kv_shard;
+  float scale;         // softmax scale on q.k
+};
+
+hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t s);
+hipError_t launch_step_f32(const StepArgs& a, int mode, hipStream_t s);
+hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
+                        const float* lse_part, int b, int L, int h, int d, hipStream_t s);
+hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n_elems,
+                           hipStream_t s);
+hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s);
+
+}  // namespace ra
