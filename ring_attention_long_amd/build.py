@@ -24,11 +24,13 @@ ARCH = os.environ.get("RA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
-# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.  Strict IEEE (no fast-math):
+# -packed-fp32-ops: no packed fp32 add/mul/fma in device code.  Strict IEEE (no fast-math):
 # the kernels rely on -inf for masked scores and empty rows.
 FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in VGPRs: the softmax reads the score accumulators directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
