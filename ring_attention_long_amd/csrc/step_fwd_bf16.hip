@@ -132,11 +132,13 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
 
   // ---- Q^T operand, resident for the whole kernel -------------------------------------
+  // Rows past the shard end read row L-1 instead: they are never stored, and their key
+  // limit of 0 masks every score.  (All global loads of this kernel are branch-free.)
   bf16x8 qop[D / 16];
   {
-    const __bf16* row = qp + (((int64_t)bi * L + t) * a.h + hq) * D + lg * 8;
+    const __bf16* row = qp + (((int64_t)bi * L + min(t, L - 1)) * a.h + hq) * D + lg * 8;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qop[kk] = t < L ? *(const bf16x8*)(row + kk * 16) : bf16x8{};
+    for (int kk = 0; kk < D / 16; ++kk) qop[kk] = *(const bf16x8*)(row + kk * 16);
   }
 
   f32x16 acc[D / 32];
@@ -154,19 +156,20 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const int st = tid & (STAGERS - 1);
   const int kq = st & 15, dc = st >> 4;
   u32x4 sreg[4];
+  // Rows past the shard end are clamped to row L-1: those keys are always masked, so any
+  // finite values will do, and the loads need no per-lane guard.
   auto load_tile = [&](int j) {
     if (group == 0) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int idx = st + STAGERS * it;
-        const int u = j * BN + (idx >> 4);
-        sreg[it] = u < L ? load16(kp + kv_base + (int64_t)u * kv_row + (idx & 15) * 8) : u32x4{};
+        const int u = min(j * BN + (st >> 4) + 16 * it, L - 1);
+        sreg[it] = load16(kp + kv_base + (int64_t)u * kv_row + (st & 15) * 8);
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int u = j * BN + kq * 4 + r;
-        sreg[r] = u < L ? load16(vp + kv_base + (int64_t)u * kv_row + dc * 8) : u32x4{};
+        const int u = min(j * BN + kq * 4 + r, L - 1);
+        sreg[r] = load16(vp + kv_base + (int64_t)u * kv_row + dc * 8);
       }
     }
   };
@@ -195,34 +198,66 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   };
 
   // ---- the two phases of one wave ------------------------------------------------------
-  // Matrix phase of step j: O^T += V(j-1)^T P(j-1)^T, then S^T(j) = K(j) Q^T.
+  // Operands of the two products, read from LDS.  V^T operand of chunk c (16 keys), d-tile
+  // e: Vt[32e + lq][16c + 4lg .. +4] and [.. + 8 .. +4].  K operand of d-step kk, key
+  // sub-tile jj: K[32jj + lq][16kk + 8lg .. +8].
+  auto v_operand = [&](const __bf16* vt, int c, int e) {
+    const __bf16* vr = vt + (32 * e + lq) * VPITCH + 16 * c + 4 * lg;
+    const u32x2 lo = *(const u32x2*)vr;
+    const u32x2 hi = *(const u32x2*)(vr + 8);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  auto k_operand = [&](const __bf16* kt, int kk, int jj) {
+    return *(const bf16x8*)(kt + (32 * jj + lq) * KPITCH + kk * 16 + lg * 8);
+  };
+  // Matrix phase of step j: O^T += V(j-1)^T P(j-1)^T and S^T(j) = K(j) Q^T.  In the steady
+  // state both run interleaved, one MFMA of each per slot (6 independent accumulators),
+  // with each slot's two LDS operands fetched two slots ahead.
   auto matrix_phase = [&](int j) {
-    if (j >= 1 && j - 1 < wave_tiles) {
-      const __bf16* vt = vt_lds[(j - 1) & 1];
+    const bool do_pv = j >= 1 && j - 1 < wave_tiles;
+    const bool do_qk = j < wave_tiles;
+    const __bf16* vt = vt_lds[(j - 1) & 1];
+    const __bf16* kt = k_lds[j & 1];
+    if (do_pv && do_qk) {
+      sc[0] = f32x16{};
+      sc[1] = f32x16{};
+      bf16x8 va[3], ka[3];
+      va[0] = v_operand(vt, 0, 0);
+      ka[0] = k_operand(kt, 0, 0);
+      va[1] = v_operand(vt, 0, 1);
+      ka[1] = k_operand(kt, 0, 1);
 #pragma unroll
-      for (int e = 0; e < D / 32; ++e) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const __bf16* vr = vt + (32 * e + lq) * VPITCH + 16 * c + 4 * lg;
-          const u32x2 lo = *(const u32x2*)vr;
-          const u32x2 hi = *(const u32x2*)(vr + 8);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[e], 0, 0, 0);
+      for (int x = 0; x < 16; ++x) {
+        if (x + 2 < 16) {
+          va[(x + 2) % 3] = v_operand(vt, (x + 2) >> 2, (x + 2) & 3);
+          ka[(x + 2) % 3] = k_operand(kt, (x + 2) >> 1, (x + 2) & 1);
         }
+        acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % 3], pb[x >> 2], acc[x & 3], 0, 0, 0);
+        sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qop[x >> 1], sc[x & 1], 0, 0, 0);
       }
+#pragma unroll
+      for (int x = 0; x < 14; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next slot's LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // this slot's two MFMAs
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      return;
     }
-    if (j < wave_tiles) {
-      const __bf16* kt = k_lds[j & 1];
+    if (do_pv) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(vt, c, e), pb[c], acc[e], 0, 0, 0);
+    }
+    if (do_qk) {
       sc[0] = f32x16{};
       sc[1] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+      for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const bf16x8 ka = *(const bf16x8*)(kt + (32 * jj + lq) * KPITCH + kk * 16 + lg * 8);
-          sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[kk], sc[jj], 0, 0, 0);
-        }
-      }
+        for (int jj = 0; jj < 2; ++jj)
+          sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kt, kk, jj), qop[kk], sc[jj], 0, 0, 0);
     }
   };
   // Softmax phase of step j: mask, running max, lazy rescale, P = exp2(S c - m), row sum.
@@ -289,8 +324,9 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   if (n_tiles > 0) {          // prologue: K(0) and V(0) in LDS, K(1) and V(1) in flight
     load_tile(0);
     store_tile(0);
-    if (n_tiles > 1) load_tile(1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q is in registers before the loop
+  if (n_tiles > 1) load_tile(1);
   __syncthreads();
   if (group == 1) __syncthreads();
   for (int j = 0; j <= n_tiles; ++j) {
