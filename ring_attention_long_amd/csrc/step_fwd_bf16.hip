@@ -26,8 +26,7 @@
 //    per-lane reductions plus one exchange with lane l ^ 32 (v_permlane32_swap).
 //  * The probabilities never leave registers: the score accumulator, rounded to bf16, is
 //    exactly the B operand (P^T) of the second product O^T += V^T P^T, because the order
-//    in which the contraction visits keys is free as long as A and B agree.  V is staged
-//    into LDS transposed (Vt[d][key]) so its A operand is two 8-byte LDS reads.
+//    in which the contraction visits keys is free as long as A and B agree.
 //  * Online softmax in base 2 with scale * log2(e) folded into one FMA per score, and a
 //    lazy rescale: the running maximum used for exponentiation moves only when a row's new
 //    maximum exceeds it by more than TAU (= 8, so P <= 2^8); the final O / l is unchanged
@@ -36,10 +35,11 @@
 //    every shard, the allowed keys of a row are a prefix [0, limit) of the KV shard, so a
 //    wave skips every key tile at or beyond its largest limit, runs maskless below its
 //    smallest limit, and masks only the diagonal tiles in between.
-//  * K/V tiles are double-buffered in LDS and staged during the softmax halves: group 0
-//    writes K tiles, group 1 writes V tiles (transposed), each into the buffer the other
-//    group has finished reading, and each then issues the global loads of its next tile a
-//    full step before that tile is written.
+//  * K/V tiles are double-buffered in LDS and staged by DMA (global_load_lds): no VGPRs
+//    and no vector instructions.  Group 0 starts the loads of the next K and V tiles at
+//    the end of its matrix phase, into the buffers the other group finished reading, a
+//    full step before they are read.  V is stored row-major and read with the gfx950
+//    transposing LDS load, which yields the V^T operand directly.
 //  * Workgroups are launched heaviest query block first (causal work grows with the query
 //    position), with the KV head as the fastest-varying index so that neighbouring
 //    workgroups, dispatched round-robin over the 8 XCDs, put each KV head's tiles into
@@ -60,11 +60,8 @@ constexpr int BN = 64;            // keys per tile
 constexpr int QW = 32;            // query rows per wave
 constexpr int WAVES = 8;          // two per SIMD
 constexpr int THREADS = 64 * WAVES;
-constexpr int STAGERS = 256;      // threads per group; each group stages one of K, V
-constexpr int KPITCH = D + 8;     // bf16 per K row in LDS: 272 B, rows shift by 4 banks
-constexpr int VPITCH = BN + 4;    // bf16 per Vt row in LDS: 136 B, rows shift by 2 banks
-constexpr int K_TILE = BN * KPITCH;
-constexpr int V_TILE = D * VPITCH;
+constexpr int ROW_BYTES = D * 2;  // one key's K or V row: 256 B, sixteen 16-byte chunks
+constexpr int TILE_BYTES = BN * ROW_BYTES;   // 16 KB; written by 16 DMA loads of 1 KB
 constexpr float TAU = 8.0f;       // lazy-rescale threshold, log2 units
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -79,13 +76,21 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ u32x4 load16(const __bf16* p) { return *(const u32x4*)p; }
+// Workgroup barrier without a memory fence: the compiler may not move memory operations
+// across it, but no wait for outstanding loads is emitted.  Every LDS read issued before
+// it has been consumed by a matrix instruction (so has completed), and DMA writes into
+// LDS are waited for explicitly by the waves that issued them.
+__device__ __forceinline__ void barrier_no_fence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 template <int MODE>
 __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, int heads_per_wg,
                                                                   int n_qb, int inner_count) {
-  __shared__ __bf16 k_lds[2][K_TILE];
-  __shared__ __bf16 vt_lds[2][V_TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds[2][TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -145,124 +150,114 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) acc[e] = f32x16{};
   f32x16 sc[2];
-  bf16x8 pb[4];
+  bf16x8 pb[4] = {bf16x8{}, bf16x8{}, bf16x8{}, bf16x8{}};
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale * LOG2E;
 
-  // ---- tile staging: global -> registers -> LDS ----------------------------------------
-  // Group 0 stages K tiles: 64 keys x 16 chunks of 16 B, a straight copy.  Group 1 stages
-  // V tiles: thread (kq, dc) loads 4 keys x 8 d and writes 8 transposed 8-byte rows
-  // Vt[d][4 keys].  Each group keeps one tile in flight in `sreg`.
-  const int st = tid & (STAGERS - 1);
-  const int kq = st & 15, dc = st >> 4;
-  u32x4 sreg[4];
-  // Rows past the shard end are clamped to row L-1: those keys are always masked, so any
-  // finite values will do, and the loads need no per-lane guard.
-  auto load_tile = [&](int j) {
-    if (group == 0) {
+  // ---- tile staging: global -> LDS by DMA (buffer_load ... lds, 16 B per lane) -----------
+  // A K or V tile is 64 rows of 256 B; DMA load i (1 KB) fills rows 4i..4i+3, lane l
+  // writing slot l: row 4i + l/16, slot position l%16.  Each lane picks which global
+  // 16-byte chunk lands in its slot, which gives the swizzles the readers need:
+  //   K: chunk c of row r sits at position c ^ (r & 15)   (16 rows, same chunk: 16 banks)
+  //   V: chunk c of row r sits at position c ^ 4 (r & 3)  (transposed reads, see below)
+  // Group 0 issues the loads, wave w taking loads i = w, w+4, w+8, w+12, so the row bits
+  // that enter the swizzle are fixed per lane and the lane's byte offset is one register.
+  // The buffer descriptor covers exactly rows 0..L-1 of this (batch, KV head), so rows
+  // past the shard end fail the hardware range check and arrive as zeros (always masked).
+  const unsigned row_stride = (unsigned)a.n_kv * D * 2;   // bytes between keys in HBM
+  const int num_records = (int)((unsigned)(L - 1) * row_stride + ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kp + kv_base), 0, num_records, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vp + kv_base), 0, num_records, 0x00020000);
+  const int ws = wave & 3;
+  const unsigned lrow = lane >> 4;                       // row within a 1 KB load
+  const unsigned k_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ ((4 * ws + lrow) & 15)) * 16;
+  const unsigned v_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow)) * 16;
+  auto issue_tile_dma = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, unsigned off, int j) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int u = min(j * BN + (st >> 4) + 16 * it, L - 1);
-        sreg[it] = load16(kp + kv_base + (int64_t)u * kv_row + (st & 15) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = min(j * BN + kq * 4 + r, L - 1);
-        sreg[r] = load16(vp + kv_base + (int64_t)u * kv_row + dc * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (group == 0) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = st + STAGERS * it;
-        *(u32x4*)&k_lds[buf][(idx >> 4) * KPITCH + (idx & 15) * 8] = sreg[it];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int w = i >> 1;
-        unsigned lo, hi;
-        if (i & 1) {
-          lo = (sreg[0][w] >> 16) | (sreg[1][w] & 0xffff0000u);
-          hi = (sreg[2][w] >> 16) | (sreg[3][w] & 0xffff0000u);
-        } else {
-          lo = (sreg[0][w] & 0xffffu) | (sreg[1][w] << 16);
-          hi = (sreg[2][w] & 0xffffu) | (sreg[3][w] << 16);
-        }
-        *(u32x2*)&vt_lds[buf][(dc * 8 + i) * VPITCH + kq * 4] = u32x2{lo, hi};
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int i = ws + 4 * t;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off,
+          (unsigned)(j * BN + 4 * i) * row_stride, 0, 0);
     }
   };
 
   // ---- the two phases of one wave ------------------------------------------------------
-  // Operands of the two products, read from LDS.  V^T operand of chunk c (16 keys), d-tile
-  // e: Vt[32e + lq][16c + 4lg .. +4] and [.. + 8 .. +4].  K operand of d-step kk, key
-  // sub-tile jj: K[32jj + lq][16kk + 8lg .. +8].
-  auto v_operand = [&](const __bf16* vt, int c, int e) {
-    const __bf16* vr = vt + (32 * e + lq) * VPITCH + 16 * c + 4 * lg;
-    const u32x2 lo = *(const u32x2*)vr;
-    const u32x2 hi = *(const u32x2*)(vr + 8);
-    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  // K operand of d-step kk, key sub-tile jj: row 32jj + lq, chunk 2kk + lg (16 B).  The
+  // swizzled position depends on kk and the lane only, so the eight offsets are kept.
+  unsigned k_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    k_off[kk] = (unsigned)lq * ROW_BYTES + (unsigned)(((2 * kk + lg) ^ (lq & 15)) * 16);
+  auto k_operand = [&](const char* kt, int kk, int jj) {
+    return *(const bf16x8*)(kt + k_off[kk] + jj * 32 * ROW_BYTES);
   };
-  auto k_operand = [&](const __bf16* kt, int kk, int jj) {
-    return *(const bf16x8*)(kt + (32 * jj + lq) * KPITCH + kk * 16 + lg * 8);
+  // V^T operand of key chunk c (16 keys) and d-tile e, read with ds_read_b64_tr_b16: in
+  // each 16-lane group the lanes' 8-byte pieces form a 4 x 16 array whose column i goes
+  // to lane i.  Lane j of a group points at row k0 + j/4, d = d0 + 4 (j%4); lane i then
+  // receives V[k0 .. k0+3][d0 + i], i.e. four consecutive keys of one d, which is the A
+  // operand of O^T = V^T P^T (m = d, k = key).  Two reads give the lane's eight keys,
+  // 16c + 4lg + {0..3} and 16c + 8 + 4lg + {0..3}: the same key order as the lane's P
+  // values in the score accumulator.  With the V swizzle the 16-lane group's four rows
+  // (r & 3 = j/4) land in disjoint bank ranges.
+  const int g16 = lane >> 4, j16 = lane & 15, jq = j16 >> 2;
+  unsigned v_off[D / 32];
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) {
+    const int low = 2 * (g16 & 1) + ((j16 & 3) >> 1);            // chunk within the 4 of tile e
+    v_off[e] = (unsigned)(4 * lg + jq) * ROW_BYTES + (unsigned)((4 * (e ^ jq) + low) * 16) +
+               (unsigned)((j16 & 1) * 8);
+  }
+  auto v_operand = [&](const char* vt, int c, int e) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const char* base = vt + v_off[e] + 16 * c * ROW_BYTES;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(base));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(base + 8 * ROW_BYTES));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  // Matrix phase of step j: O^T += V(j-1)^T P(j-1)^T and S^T(j) = K(j) Q^T.  In the steady
-  // state both run interleaved, one MFMA of each per slot (6 independent accumulators),
-  // with each slot's two LDS operands fetched two slots ahead.
+  // Matrix phase of step j: O^T += V(j-1)^T P(j-1)^T and S^T(j) = K(j) Q^T, interleaved one
+  // MFMA of each per slot (6 independent accumulators), each slot's two LDS operands
+  // fetched two slots ahead.  The same code runs at every step so that the accumulators
+  // keep one home: where the wave has no tile j-1, P is zero (the V buffer holds finite
+  // data: a real tile, or zeros before the first); where it has no tile j, the scores
+  // are computed from whatever K buffer is there and never used.
   auto matrix_phase = [&](int j) {
-    const bool do_pv = j >= 1 && j - 1 < wave_tiles;
-    const bool do_qk = j < wave_tiles;
-    const __bf16* vt = vt_lds[(j - 1) & 1];
-    const __bf16* kt = k_lds[j & 1];
-    if (do_pv && do_qk) {
-      sc[0] = f32x16{};
-      sc[1] = f32x16{};
-      bf16x8 va[3], ka[3];
-      va[0] = v_operand(vt, 0, 0);
-      ka[0] = k_operand(kt, 0, 0);
-      va[1] = v_operand(vt, 0, 1);
-      ka[1] = k_operand(kt, 0, 1);
+    const char* vt = v_lds[(j - 1) & 1];
+    const char* kt = k_lds[j & 1];
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+    bf16x8 va[3], ka[3];
+    va[0] = v_operand(vt, 0, 0);
+    ka[0] = k_operand(kt, 0, 0);
+    va[1] = v_operand(vt, 0, 1);
+    ka[1] = k_operand(kt, 0, 1);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        if (x + 2 < 16) {
-          va[(x + 2) % 3] = v_operand(vt, (x + 2) >> 2, (x + 2) & 3);
-          ka[(x + 2) % 3] = k_operand(kt, (x + 2) >> 1, (x + 2) & 1);
-        }
-        acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % 3], pb[x >> 2], acc[x & 3], 0, 0, 0);
-        sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qop[x >> 1], sc[x & 1], 0, 0, 0);
+    for (int x = 0; x < 16; ++x) {
+      if (x + 2 < 16) {
+        va[(x + 2) % 3] = v_operand(vt, (x + 2) >> 2, (x + 2) & 3);
+        ka[(x + 2) % 3] = k_operand(kt, (x + 2) >> 1, (x + 2) & 1);
       }
-#pragma unroll
-      for (int x = 0; x < 14; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next slot's LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // this slot's two MFMAs
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      return;
+      acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % 3], pb[x >> 2], acc[x & 3], 0, 0, 0);
+      sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qop[x >> 1], sc[x & 1], 0, 0, 0);
     }
-    if (do_pv) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e)
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(vt, c, e), pb[c], acc[e], 0, 0, 0);
+    for (int x = 0; x < 14; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next slot's LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // this slot's two MFMAs
     }
-    if (do_qk) {
-      sc[0] = f32x16{};
-      sc[1] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kt, kk, jj), qop[kk], sc[jj], 0, 0, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // Softmax phase of step j: mask, running max, lazy rescale, P = exp2(S c - m), row sum.
   auto softmax_phase = [&](int j) {
-    if (j < 0 || j >= wave_tiles) return;
+    if (j >= wave_tiles) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pb[c] = bf16x8{};
+      return;
+    }
     if (j >= wave_full) {
       // keep this a real (scalar) branch: only diagonal and ragged tiles pay for the mask
       __asm__ volatile("" ::: "memory");
@@ -313,33 +308,34 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   };
   // ---- main loop -------------------------------------------------------------------------
   // Every wave runs the same sequence: matrix phase of step j, barrier, softmax phase of
-  // step j (plus its share of the staging: group 0 writes K(j+1), group 1 writes V(j+1),
-  // each then fetching the tile after), barrier.  Group 1 executes one extra barrier before
-  // the loop and group 0 one after it, so group 1 runs half a step behind group 0 and the
-  // two groups of each SIMD alternate between matrix and vector work.  Buffer lifetimes,
-  // counted in half steps h (group 0 runs phase h, group 1 phase h - 1):
-  //   K(j) is read at h = 2j, 2j+1 and written (by group 0) at h = 2j-1;
-  //   V(j) is read at h = 2j+2, 2j+3 and written (by group 1) at h = 2j;
-  // so a write never touches the buffer of the other parity being read.
-  if (n_tiles > 0) {          // prologue: K(0) and V(0) in LDS, K(1) and V(1) in flight
-    load_tile(0);
-    store_tile(0);
+  // step j, barrier.  Group 1 executes one extra barrier before the loop and group 0 one
+  // after it, so group 1 runs half a step behind group 0 and the two waves of each SIMD
+  // alternate between matrix and vector work.  Numbering the intervals between barriers,
+  // interval 2j+1 holds group 0's matrix phase j and group 1's softmax phase j-1, interval
+  // 2j+2 group 0's softmax phase j and group 1's matrix phase j.  K(j) is read in
+  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4.  At the end of its matrix phase j
+  // (interval 2j+1) group 0 starts the DMA of K(j+1) and V(j) into the buffers last read
+  // in interval 2j, and waits for it before the barrier that closes interval 2j+2.
+  if (group == 0 && n_tiles > 0) issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);
+  {
+    u32x4* z = (u32x4*)v_lds[1];        // read by the (zero-P) PV of step 0
+    for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q is in registers before the loop
-  if (n_tiles > 1) load_tile(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q and K(0) are in place
   __syncthreads();
-  if (group == 1) __syncthreads();
+  if (group == 1) barrier_no_fence();
   for (int j = 0; j <= n_tiles; ++j) {
     matrix_phase(j);
-    __syncthreads();
-    softmax_phase(j);
-    if (j + 1 < n_tiles) {
-      store_tile((j + 1) & 1);
-      if (j + 2 < n_tiles) load_tile(j + 2);
+    if (group == 0) {
+      if (j + 1 < n_tiles) issue_tile_dma(k_rsrc, k_lds[(j + 1) & 1], k_dma_off, j + 1);
+      if (j < n_tiles) issue_tile_dma(v_rsrc, v_lds[j & 1], v_dma_off, j);
     }
-    __syncthreads();
+    barrier_no_fence();
+    softmax_phase(j);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    barrier_no_fence();
   }
-  if (group == 0) __syncthreads();
+  if (group == 0) barrier_no_fence();
 
   // ---- epilogue ------------------------------------------------------------------------
   const float l_tot = lane_pair_sum(l_run);
