@@ -36,9 +36,9 @@
 //    wave skips every key tile at or beyond its largest limit, runs maskless below its
 //    smallest limit, and masks only the diagonal tiles in between.
 //  * K/V tiles are double-buffered in LDS and staged by DMA (global_load_lds): no VGPRs
-//    and no vector instructions.  Group 0 starts the loads of the next K and V tiles at
-//    the end of its matrix phase, into the buffers the other group finished reading, a
-//    full step before they are read.  V is stored row-major and read with the gfx950
+//    and no vector instructions.  Group 1 starts the loads of the next K and V tiles at
+//    the end of its softmax phase (the shorter phase), into buffers both groups have
+//    finished reading, a full step before they are read.  V is stored row-major and read with the gfx950
 //    transposing LDS load, which yields the V^T operand directly.
 //  * Workgroups are launched heaviest query block first (causal work grows with the query
 //    position), with the KV head as the fastest-varying index so that neighbouring
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // 16-byte chunk lands in its slot, which gives the swizzles the readers need:
   //   K: chunk c of row r sits at position c ^ (r & 15)   (16 rows, same chunk: 16 banks)
   //   V: chunk c of row r sits at position c ^ 4 (r & 3)  (transposed reads, see below)
-  // Group 0 issues the loads, wave w taking loads i = w, w+4, w+8, w+12, so the row bits
+  // Group 1 issues the loads, wave w taking loads i = w, w+4, w+8, w+12, so the row bits
   // that enter the swizzle are fixed per lane and the lane's byte offset is one register.
   // The buffer descriptor covers exactly rows 0..L-1 of this (batch, KV head), so rows
   // past the shard end fail the hardware range check and arrive as zeros (always masked).
@@ -313,26 +313,36 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // alternate between matrix and vector work.  Numbering the intervals between barriers,
   // interval 2j+1 holds group 0's matrix phase j and group 1's softmax phase j-1, interval
   // 2j+2 group 0's softmax phase j and group 1's matrix phase j.  K(j) is read in
-  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4.  At the end of its matrix phase j
-  // (interval 2j+1) group 0 starts the DMA of K(j+1) and V(j) into the buffers last read
-  // in interval 2j, and waits for it before the barrier that closes interval 2j+2.
-  if (group == 0 && n_tiles > 0) issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);
+  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4.
+  // Group 1 stages: at the end of its softmax phase j (interval 2j+3) it starts the DMA of
+  // K(j+2) into the buffer of K(j) and of V(j+1) into the buffer of V(j-1), both last read
+  // in interval 2j+2, and waits for it at the end of its next matrix phase (interval
+  // 2j+4), one interval before the data is first read.  The first tiles come from the
+  // prologue: K(0) fully loaded, K(1) and V(0) in flight until group 1's first matrix
+  // phase ends.
+  if (group == 1 && n_tiles > 0) {
+    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);
+  }
   {
     u32x4* z = (u32x4*)v_lds[1];        // read by the (zero-P) PV of step 0
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q and K(0) are in place
   __syncthreads();
-  if (group == 1) barrier_no_fence();
+  if (group == 1) {
+    if (n_tiles > 1) issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, 1);
+    if (n_tiles > 0) issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, 0);
+    barrier_no_fence();
+  }
   for (int j = 0; j <= n_tiles; ++j) {
     matrix_phase(j);
-    if (group == 0) {
-      if (j + 1 < n_tiles) issue_tile_dma(k_rsrc, k_lds[(j + 1) & 1], k_dma_off, j + 1);
-      if (j < n_tiles) issue_tile_dma(v_rsrc, v_lds[j & 1], v_dma_off, j);
-    }
+    if (group == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
     barrier_no_fence();
     softmax_phase(j);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    if (group == 1) {
+      if (j + 2 < n_tiles) issue_tile_dma(k_rsrc, k_lds[j & 1], k_dma_off, j + 2);
+      if (j + 1 < n_tiles) issue_tile_dma(v_rsrc, v_lds[(j + 1) & 1], v_dma_off, j + 1);
+    }
     barrier_no_fence();
   }
   if (group == 0) barrier_no_fence();
