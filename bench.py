@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -87,6 +88,40 @@ def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0):
                       f"all {N * L} keys (fp64 numpy, {elapsed:.1f} s)"}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_fwd_bf16_striped_causal_32k_hbm_bytes.md")
+
+
+def measured_traffic():
+    """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        fields = dict(re.findall(r"^\s+([a-z_0-9]+): (\S+)$", text, flags=re.M))
+        src = os.path.join(ROOT, fields["kernel_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, steps):
+    """Run the library's fp32 copy kernel (reads and writes mib MiB each) `steps` times."""
+    import torch
+
+    import ring_attention_long_amd as ra
+    n = mib * (1 << 20) // 4
+    d = 128
+    rows = n // d
+    src = torch.randn(1, rows, 1, d, device="cuda:0", dtype=torch.float32)
+    for _ in range(steps):
+        ra.finalize(src, torch.float32)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": rows * d * 4, "bytes_written": rows * d * 4,
+                                           "dispatches": steps, "kernel": "copy_f32_kernel"}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +130,13 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="instead of the ring pass, run the library's plain fp32 copy kernel "
+                         "(ra_finalize, fp32) over this many MiB: the known-size reference for "
+                         "scaling HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration_mb:
+        return copy_calibration(args.copy_calibration_mb, args.steps)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
               "(the ring's other devices are emulated on the one GPU)", file=sys.stderr)
@@ -190,7 +231,8 @@ def main():
                    "useful_tflop_per_pass": round(flops / 1e12, 4),
                    "pct_of_bf16_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic() if args.workload == DEFAULT_WORKLOAD else None,
                      "kernel": "step_fwd_bf16_kernel<MODE_MERGE/MODE_PART>",
                      "launches": len(step_ms),
                      "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4)},
