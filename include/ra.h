@@ -45,7 +45,7 @@ typedef int32_t ra_status;
 #define RA_OK 0
 #define RA_ERR_INVALID_ARG (-1) /* bad shape, index, enum, null or misaligned pointer   */
 #define RA_ERR_UNSUPPORTED (-2) /* valid problem with no kernel (e.g. bf16 with d != 128) */
-#define RA_ERR_WORKSPACE (-3)   /* workspace smaller than ra_ring_fwd_workspace()        */
+#define RA_ERR_WORKSPACE (-3)   /* workspace smaller than ra_ring_{fwd,bwd}_workspace()  */
 #define RA_ERR_HIP (-4)         /* a HIP call or launch failed                            */
 
 /* Sequence layouts (page 1, "Causal Masking Dynamics"; page 3, section 6). */
@@ -146,6 +146,43 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
                             const void* k_all, const void* v_all, void* o, float* lse, void* ws,
                             size_t ws_bytes, ra_stream compute, ra_stream copy,
                             ra_ring_timing* t);
+
+/* ---------------------------------------------------------------------------------------
+ * Backward (page 1, "The Backward Pass and Gradient Exchange"; page 4, "The Backward Pass:
+ * Symmetric Ring Operation": P is recomputed from the saved statistics, dQ accumulates on
+ * the query's device, dK and dV accumulate per KV block).  The gradients are the textbook
+ * ones of softmax attention; with P = exp(s - LSE) (0 where masked), D = rowsum(dO * O):
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
+ * dK and dV summed over the query heads of each KV group.  bf16 with d = 128 only
+ * (RA_ERR_UNSUPPORTED otherwise).  Gradients are fp32.
+ * ------------------------------------------------------------------------------------- */
+
+/* ra_bwd_preprocess — delta [b][h][L] fp32 = rowsum(dout * o); o, dout [b][L][h][d]. */
+ra_status ra_bwd_preprocess(const ra_problem* p, const void* o, const void* dout, float* delta,
+                            ra_stream stream);
+
+/* ra_step_bwd — one ring step of the backward: adds the contributions of shard q_shard's
+ * queries against KV shard kv_shard to dq_acc [b][L][h][d] (this device's queries) and to
+ * dk_acc, dv_acc [b][L][n_kv][d] (that KV shard), all fp32 and accumulated in place.  lse
+ * is the forward's [b][h][L] output (natural log), delta from ra_bwd_preprocess. */
+ra_status ra_step_bwd(const ra_problem* p, int32_t q_shard, int32_t kv_shard, const void* q,
+                      const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
+                      ra_stream stream);
+
+/* Bytes of device workspace ra_ring_bwd needs: two KV staging buffers plus delta.
+ * Returns 0 if p is invalid. */
+size_t ra_ring_bwd_workspace(const ra_problem* p);
+
+/* ra_ring_bwd — the backward ring pass of device q_shard: given its q, o, dout [b][L][h][d]
+ * and lse [b][h][L] from the forward, and every shard's k_all, v_all [N][b][L][n_kv][d],
+ * writes dq [b][L][h][d] and dk_all, dv_all [N][b][L][n_kv][d] (fp32): this device's
+ * share of the gradients, dK and dV kept per KV shard (on a real ring they travel with
+ * K and V).  KV staging as in ra_ring_fwd; steps with no allowed pair are skipped. */
+ra_status ra_ring_bwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                      const void* v_all, const void* o, const void* dout, const float* lse,
+                      float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
+                      ra_stream compute, ra_stream copy);
 
 /* Host-only (no GPU work): number of (query, key) pairs shard q_shard may attend to in KV
  * shard kv_shard (or the whole sequence when kv_shard = -1), summed over the batch.  Useful

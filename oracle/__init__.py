@@ -5,6 +5,7 @@ package.  The product path never does.
 """
 from .ring_oracle import (  # noqa: F401
     LAYOUTS, allowed_pairs, attend, attention_over_shards, brute_force_row, merge,
-    online_blocks, positions, ring_order, shard_attention, shard_grads, shard_tokens,
+    online_blocks, positions, ring_order, shard_attention, shard_dq_rows, shard_grads,
+    shard_tokens,
     step_attention,
 )

@@ -308,6 +308,41 @@ def shard_grads(q, k_all, v_all, dout, *, N, shard, layout="contiguous", causal=
     return dq, dk, dv
 
 
+def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous", causal=False,
+                  scale=None):
+    """dQ of selected query rows only (same definition as shard_grads, evaluated for the
+    given rows; a row's dQ needs only its own P, O and D).  Returns dq [b, R, h, d]."""
+    Nk, b, L, n_kv, d = k_all.shape
+    h = q.shape[2]
+    group = _gqa_group(h, n_kv)
+    sc = _default_scale(d, scale)
+    toks = shard_tokens(layout, N, L)
+    rows = np.asarray(rows, dtype=np.int64)
+    pos_q = toks[shard][rows]
+    pos_k = np.concatenate(toks)
+    k_cat = np.concatenate([k_all[j] for j in range(N)], axis=1)
+    v_cat = np.concatenate([v_all[j] for j in range(N)], axis=1)
+    dq = np.zeros((b, rows.size, h, d))
+    for bi in range(b):
+        for hq in range(h):
+            g = hq // group
+            Qh, Kh, Vh, dOh = q[bi, rows, hq], k_cat[bi, :, g], v_cat[bi, :, g], dout[bi, rows, hq]
+            s = (Qh @ Kh.T) * sc
+            allowed = (pos_k[None, :] <= pos_q[:, None]) if causal else np.ones(s.shape, bool)
+            s = np.where(allowed, s, -np.inf)
+            m = s.max(axis=1, initial=-np.inf)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+            den = e.sum(axis=1)
+            P = np.where(den[:, None] > 0, e / np.where(den > 0, den, 1.0)[:, None], 0.0)
+            Oh = P @ Vh
+            dP = dOh @ Vh.T
+            D = np.sum(dOh * Oh, axis=1)
+            dS = P * (dP - D[:, None])
+            dq[bi, :, hq] = sc * (dS @ Kh)
+    return dq
+
+
 # --------------------------------------------------------------------------------------
 # Work accounting by direct count (page 3, section 6: work is the number of allowed
 # query-key pairs; page 3, section 2: total FLOPs 4 b S^2 h d non-causal)

@@ -11,6 +11,9 @@ Entry points (same names as the C-ABI, without the ``ra_`` prefix):
     ring_fwd      the whole forward ring pass of one device (double-buffered KV staging on a
                   side stream)
     ring_fwd_timed  ring_fwd plus per-step kernel and copy timings
+    bwd_preprocess  delta = rowsum(dO * O)
+    step_bwd      one backward ring step (accumulates dQ, dK, dV)
+    ring_bwd      the whole backward ring pass of one device
     allowed_pairs   host-side count of allowed (query, key) pairs (useful-FLOP accounting)
 
 Tensor layouts (page 1, "Practical Implementation Patterns": batch, sequence, heads, dim):
@@ -27,7 +30,7 @@ from . import _lib
 from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, check
 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
-           "make_problem", "RaError", "library_path"]
+           "bwd_preprocess", "step_bwd", "ring_bwd", "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 _copy_streams: dict[int, torch.cuda.Stream] = {}
@@ -189,6 +192,77 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
         "total_ms": tm.total_ms,
     }
     return o, lse, timing
+
+
+def bwd_preprocess(o, dout, *, stream=None):
+    """delta [b, h, L] fp32 = rowsum(dout * o) for o, dout [b, L, h, d] bf16."""
+    b, L, h, d = o.shape
+    _need(o, "o", (b, L, h, d), o.dtype)
+    _need(dout, "dout", (b, L, h, d), o.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=o.dtype)
+    delta = torch.empty((b, h, L), device=o.device, dtype=torch.float32)
+    check(_lib.lib().ra_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta),
+                                       _stream(stream)), "ra_bwd_preprocess")
+    return delta
+
+
+def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
+             layout="contiguous", scale=None, dq_acc=None, dk_acc=None, dv_acc=None,
+             stream=None):
+    """One backward ring step: adds this (query shard, KV shard) pair's contributions to
+    dq_acc [b, L, h, d] and dk_acc, dv_acc [b, L, n_kv, d] (fp32; zeros when not given).
+    Returns (dq_acc, dk_acc, dv_acc)."""
+    b, L, h, n_kv, d = _shapes_from_q(q, k)
+    for t, n, shp in ((q, "q", (b, L, h, d)), (k, "k", (b, L, n_kv, d)), (v, "v", (b, L, n_kv, d)),
+                      (dout, "dout", (b, L, h, d))):
+        _need(t, n, shp, q.dtype)
+    _need(lse, "lse", (b, h, L), torch.float32)
+    _need(delta, "delta", (b, h, L), torch.float32)
+    z = lambda shp: torch.zeros(shp, device=q.device, dtype=torch.float32)  # noqa: E731
+    dq_acc = z((b, L, h, d)) if dq_acc is None else dq_acc
+    dk_acc = z((b, L, n_kv, d)) if dk_acc is None else dk_acc
+    dv_acc = z((b, L, n_kv, d)) if dv_acc is None else dv_acc
+    _need(dq_acc, "dq_acc", (b, L, h, d), torch.float32)
+    _need(dk_acc, "dk_acc", (b, L, n_kv, d), torch.float32)
+    _need(dv_acc, "dv_acc", (b, L, n_kv, d), torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    check(_lib.lib().ra_step_bwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
+                                 _ptr(dv_acc), _stream(stream)), "ra_step_bwd")
+    return dq_acc, dk_acc, dv_acc
+
+
+def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",
+             scale=None, stream=None, copy_stream="auto", workspace=None):
+    """Backward ring pass of device q_shard.  q, o, dout [b, L, h, d] (bf16), lse [b, h, L]
+    from the forward, k_all, v_all [N, b, L, n_kv, d].  Returns fp32 (dq [b, L, h, d],
+    dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d])."""
+    N, b, L, n_kv, d = k_all.shape
+    h = q.shape[2]
+    _need(q, "q", (b, L, h, d), q.dtype)
+    _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
+    _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
+    _need(o, "o", (b, L, h, d), q.dtype)
+    _need(dout, "dout", (b, L, h, d), q.dtype)
+    _need(lse, "lse", (b, h, L), torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    need = int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p)))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ring_bwd_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    dq = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
+    dk = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
+    dv = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
+    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    check(_lib.lib().ra_ring_bwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                 _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel(), _stream(stream),
+                                 ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
+          "ra_ring_bwd")
+    return dq, dk, dv
 
 
 def allowed_pairs(*, b=1, L, N, q_shard, kv_shard=-1, causal=True, layout="contiguous") -> int:

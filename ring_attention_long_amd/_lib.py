@@ -53,6 +53,10 @@ SIGNATURES = [
     ("ra_ring_fwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_ring_fwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V,
                                ctypes.POINTER(RaRingTiming)]),
+    ("ra_bwd_preprocess", _I, [_P, _V, _V, _V, _V]),
+    ("ra_step_bwd", _I, [_P, _I, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
+    ("ra_ring_bwd_workspace", _S, [_P]),
+    ("ra_ring_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_allowed_pairs", ctypes.c_int64, [_P, _I, _I]),
     ("ra_status_string", ctypes.c_char_p, [_I]),
     ("ra_last_error", ctypes.c_char_p, []),

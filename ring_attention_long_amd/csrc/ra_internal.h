@@ -84,5 +84,10 @@ hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
 hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n_elems,
                            hipStream_t s);
 hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s);
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
+                                 hipStream_t s);
+// Adds this step's contributions: dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32).
+hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float* lse,
+                                const float* delta, float* dq, float* dk, float* dv, hipStream_t s);
 
 }  // namespace ra

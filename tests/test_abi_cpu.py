@@ -156,3 +156,45 @@ def test_kv_limit_host_matches_oracle_prefix_property():
         tot = sum(ra.allowed_pairs(L=L, N=N, q_shard=i, causal=True, layout=layout) for i in range(N))
         S = N * L
         assert tot == S * (S + 1) // 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), _lib.RA_ERR_UNSUPPORTED),          # fp32 backward has no kernel
+    (dict(d=64, dtype=0), _lib.RA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.RA_ERR_UNSUPPORTED),
+    (dict(h=3, n_kv=2), _lib.RA_ERR_INVALID_ARG),
+    (dict(L=0), _lib.RA_ERR_INVALID_ARG),
+    (dict(b=1, L=1 << 20, h=8192), _lib.RA_ERR_UNSUPPORTED),   # slice above 2 GiB
+])
+def test_backward_entry_points_reject_bad_problems(kw, status):
+    lib = _lib.lib()
+    p = _prob(**kw)
+    assert lib.ra_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, None) == status
+    assert lib.ra_step_bwd(ctypes.byref(p), 0, 0, *([FAKE] * 9), None) == status
+    assert lib.ra_ring_bwd_workspace(ctypes.byref(p)) == 0
+    assert lib.ra_ring_bwd(ctypes.byref(p), 0, *([FAKE] * 10), 1 << 40, None, None) == status
+
+
+def test_backward_rejects_bad_shards_pointers_and_workspace():
+    lib = _lib.lib()
+    p = _prob()
+    assert lib.ra_step_bwd(ctypes.byref(p), 4, 0, *([FAKE] * 9), None) == _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_step_bwd(ctypes.byref(p), 0, -1, *([FAKE] * 9), None) == _lib.RA_ERR_INVALID_ARG
+    mis = ctypes.c_void_p(0x10008)
+    args = [FAKE] * 9
+    args[7] = mis                                        # dk_acc misaligned
+    assert lib.ra_step_bwd(ctypes.byref(p), 0, 0, *args, None) == _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_bwd_preprocess(ctypes.byref(p), FAKE, None, FAKE, None) == _lib.RA_ERR_INVALID_ARG
+    need = lib.ra_ring_bwd_workspace(ctypes.byref(p))
+    st = lib.ra_ring_bwd(ctypes.byref(p), 0, *([FAKE] * 10), need - 1, None, None)
+    assert st == _lib.RA_ERR_WORKSPACE
+    assert lib.ra_ring_bwd(ctypes.byref(p), -1, *([FAKE] * 10), need, None, None) == _lib.RA_ERR_INVALID_ARG
+
+
+def test_backward_workspace_is_two_kv_buffers_plus_delta():
+    """Double-buffered K and V staging (as in the forward) plus D = rowsum(dO * O)."""
+    lib = _lib.lib()
+    p = _prob(L=1000, b=2)
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = 4 * pad(2 * 1000 * 2 * 128 * 2) + pad(2 * 4 * 1000 * 4)
+    assert lib.ra_ring_bwd_workspace(ctypes.byref(p)) == want

@@ -1,0 +1,138 @@
+"""GPU parity of the backward (ra_ring_bwd / ra_step_bwd) against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's own O and LSE; the oracle computes the exact
+gradients from the same seeded q, k, v, dO.  Tolerance per gradient tensor (the pages give
+none): max abs error <= 2e-2 * max(1, rms(ref)) and mean abs error <= 2e-3 * max(1, rms(ref)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import ring_attention_long_amd as ra
+from gpu_helpers import announce, f64, make_inputs, to_gpu
+from oracle import LAYOUTS, ring_order, shard_dq_rows, shard_grads, shard_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def check_grad(got, ref, what):
+    got = f64(got) if isinstance(got, torch.Tensor) else got
+    scale = max(1.0, float(np.sqrt(np.mean(ref ** 2))))
+    err = np.abs(got - ref)
+    announce(f"{what}: max abs {err.max():.3e} mean abs {err.mean():.3e} (rms ref {scale:.3f})")
+    assert err.max() <= 2e-2 * scale, what
+    assert err.mean() <= 2e-3 * scale, what
+
+
+def _run(cfg, layout, causal, shard, seed, copy_stream="auto"):
+    N = cfg["N"]
+    inp = make_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16", with_dout=True)
+    q, k_all, v_all = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all"))
+    dout = to_gpu(inp["dout"], "bf16")
+    o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+    dq, dk, dv = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal,
+                             layout=layout, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    return inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("layout,causal", [("contiguous", False), ("contiguous", True),
+                                           ("striped", True), ("zigzag", True)])
+@pytest.mark.parametrize("h,n_kv", [(8, 2), (4, 4), (6, 2)])
+def test_ring_bwd_small(layout, causal, h, n_kv):
+    cfg = dict(b=1, L=200, h=h, n_kv=n_kv, d=128, N=3)
+    for shard in (0, 2):
+        announce("ring_bwd", layout, "causal", causal, "shard", shard, cfg)
+        inp, _, (dq, dk, dv) = _run(cfg, layout, causal, shard, seed=81 + shard)
+        x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
+        rdq, rdk, rdv = shard_grads(x["q"], x["k_all"], x["v_all"], x["dout"], N=3, shard=shard,
+                                    layout=layout, causal=causal)
+        check_grad(dq, rdq, f"dq {layout} {causal} shard {shard}")
+        check_grad(dk, rdk, f"dk {layout} {causal} shard {shard}")
+        check_grad(dv, rdv, f"dv {layout} {causal} shard {shard}")
+
+
+def test_ring_bwd_batch_and_tiny_shards():
+    for cfg, layout in ((dict(b=2, L=70, h=4, n_kv=1, d=128, N=2), "striped"),
+                        (dict(b=1, L=2, h=4, n_kv=2, d=128, N=3), "zigzag")):
+        for shard in range(cfg["N"]):
+            announce("ring_bwd edge", layout, cfg, "shard", shard)
+            inp, _, (dq, dk, dv) = _run(cfg, layout, True, shard, seed=91)
+            x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
+            rdq, rdk, rdv = shard_grads(x["q"], x["k_all"], x["v_all"], x["dout"], N=cfg["N"],
+                                        shard=shard, layout=layout, causal=True)
+            check_grad(dq, rdq, "dq edge")
+            check_grad(dk, rdk, "dk edge")
+            check_grad(dv, rdv, "dv edge")
+
+
+def test_step_bwd_sums_to_ring_bwd():
+    """ra_step_bwd over the ring order, with ra_bwd_preprocess, equals ra_ring_bwd."""
+    cfg = dict(b=1, L=160, h=8, n_kv=2, d=128, N=4)
+    shard = 1
+    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=95)
+    delta = ra.bwd_preprocess(o, dout)
+    dq2 = torch.zeros_like(dq)
+    dk2 = torch.zeros_like(dk)
+    dv2 = torch.zeros_like(dv)
+    for src in ring_order(4, shard):
+        ra.step_bwd(q, k_all[src], v_all[src], dout, lse, delta, N=4, q_shard=shard, kv_shard=src,
+                    causal=True, layout="striped", dq_acc=dq2, dk_acc=dk2[src], dv_acc=dv2[src])
+    torch.cuda.synchronize()
+    announce("step_bwd vs ring_bwd")
+    for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.allclose(a_, b_, rtol=1e-5, atol=1e-5)
+
+
+def test_bwd_preprocess_is_rowsum_of_products():
+    g = torch.Generator().manual_seed(3)
+    o = torch.randn(2, 37, 3, 128, generator=g).to(torch.bfloat16)
+    do = torch.randn(2, 37, 3, 128, generator=g).to(torch.bfloat16)
+    want = (o.double() * do.double()).sum(-1).permute(0, 2, 1).numpy()
+    announce("bwd_preprocess")
+    got = ra.bwd_preprocess(o.cuda(), do.cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f64(got), want, rtol=1e-5, atol=1e-4)
+
+
+# ------------------------------------------------------------------ full size (config 5)
+@pytest.mark.parametrize("shard", [0, 7])
+def test_config5_full_size(shard):
+    """S = 65536, N = 8 (L = 8192), h = 32, n_kv = 8, d = 128, bf16, causal striped."""
+    cfg = dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8)
+    N, L, h, n_kv = 8, 8192, 32, 8
+    announce("config5 ring_bwd full size, shard", shard)
+    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=1005)
+    # (1) dQ of sampled rows against the oracle
+    rows = np.array([0, 1, 63, 64, 4095, L - 1])
+    x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
+    rdq = shard_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard,
+                        layout="striped", causal=True)
+    check_grad(dq[:, torch.as_tensor(rows, device="cuda")], rdq, "config5 dq sampled rows")
+    # (2) identities over all keys: sum dK = 0 per KV head (key-shift invariance); sum dV =
+    #     sum of dO over the group's query rows (softmax rows sum to one)
+    dk_sum = f64(dk.sum(dim=(0, 2)))                       # [b, n_kv, d]
+    dv_sum = f64(dv.sum(dim=(0, 2)))
+    do_sum = inp["dout"].astype(np.float64).sum(axis=1).reshape(1, n_kv, h // n_kv, 128).sum(axis=2)
+    announce(f"sum dK max abs {np.abs(dk_sum).max():.3e}; sum dV err {np.abs(dv_sum - do_sum).max():.3e}")
+    assert np.abs(dk_sum).max() <= 2e-2 * np.sqrt(L)
+    assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.sqrt(L)
+    # (3) Q = 0: uniform weights 1/n_r; dK = 0 exactly and dV_c = sum over rows r that see
+    #     key c of dO_r / n_r (summed over the group's heads), every key of every shard
+    q0 = torch.zeros_like(q)
+    o0, lse0 = ra.ring_fwd(q0, k_all, v_all, q_shard=shard, causal=True, layout="striped")
+    dq0, dk0, dv0 = ra.ring_bwd(q0, k_all, v_all, o0, dout, lse0, q_shard=shard, causal=True,
+                                layout="striped")
+    torch.cuda.synchronize()
+    assert float(dk0.abs().max()) == 0.0
+    toks = shard_tokens("striped", N, L)
+    pos_q = toks[shard]                                    # increasing
+    w = inp["dout"].astype(np.float64)[0] / (pos_q + 1.0)[:, None, None]   # [L, h, d]
+    wg = w.reshape(L, n_kv, h // n_kv, 128).sum(axis=2)   # [L, n_kv, d]
+    suffix = np.cumsum(wg[::-1], axis=0)[::-1]             # suffix[r] = sum over rows >= r
+    want = np.zeros((N, L, n_kv, 128))
+    for j in range(N):
+        first = np.searchsorted(pos_q, toks[j], side="left")   # first row with pos >= key pos
+        valid = first < L
+        want[j][valid] = suffix[first[valid]]
+    check_grad(dv0[:, 0], want, "config5 dV closed form (Q = 0)")

@@ -87,3 +87,27 @@ def test_zero_queries_value_gradient_is_prefix_weighted():
             pk = toks[j][u]
             want = sum(dout[0, r, 0] / (toks[1][r] + 1) for r in range(L) if pk <= toks[1][r])
             np.testing.assert_allclose(dv[j, 0, u, 0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_dq_rows_match_finite_differences():
+    """shard_dq_rows (a subset of rows) against central differences of the forward."""
+    from oracle import shard_dq_rows
+    N, b, L, h, n_kv, d = 2, 1, 4, 2, 1, 3
+    q = RNG.standard_normal((b, L, h, d))
+    k_all = RNG.standard_normal((N, b, L, n_kv, d))
+    v_all = RNG.standard_normal((N, b, L, n_kv, d))
+    dout = RNG.standard_normal((b, L, h, d))
+    kw = dict(N=N, shard=0, layout="striped", causal=True)
+    rows = [1, 3]
+    got = shard_dq_rows(q, k_all, v_all, dout, rows, **kw)
+    eps = 1e-6
+    for ri, r in enumerate(rows):
+        for hq in range(h):
+            for e in range(d):
+                orig = q[0, r, hq, e]
+                q[0, r, hq, e] = orig + eps
+                fp = _loss(q, k_all, v_all, dout, **kw)
+                q[0, r, hq, e] = orig - eps
+                fm = _loss(q, k_all, v_all, dout, **kw)
+                q[0, r, hq, e] = orig
+                assert got[0, ri, hq, e] == pytest.approx((fp - fm) / (2 * eps), rel=1e-6, abs=1e-8)
