@@ -44,12 +44,13 @@ __host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
 __host__ __device__ inline int kv_limit(int causal, int layout, int N, int L, int qs, int ks,
                                         int t) {
   if (!causal) return L;
-  const int64_t P = global_pos(layout, N, L, qs, t);
   if (layout == RA_LAYOUT_STRIPED) {
-    // keys of shard ks sit at uN + ks; count u >= 0 with uN + ks <= P
-    if (P < ks) return 0;
-    return (int)clamp64((P - ks) / N + 1, 0, L);
+    // keys of shard ks sit at uN + ks and query t at tN + qs; since |qs - ks| < N,
+    // uN + ks <= tN + qs holds exactly for u <= t when ks <= qs and for u < t otherwise
+    const int lim = t + (qs >= ks ? 1 : 0);
+    return lim < 0 ? 0 : (lim > L ? L : lim);
   }
+  const int64_t P = global_pos(layout, N, L, qs, t);
   if (layout == RA_LAYOUT_ZIGZAG) {
     const int C = L / 2;
     const int64_t a = clamp64(P - (int64_t)ks * C + 1, 0, C);

@@ -244,137 +244,319 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(StepArgs a, const __
 }
 
 // ------------------------------------------------------------------------------------------
-// dK/dV kernel: workgroup = 4 waves x 32 keys of one KV head; loops over the query tiles
-// (64 rows) of every head of the KV group.
+// dK/dV kernel: workgroup = 8 waves on 128 keys of one KV head, walking the 64-row query
+// tiles of every head of the KV group.
+//
+// Wave w owns keys 32 (w % 4) .. +31 of the workgroup and rows 32 (w / 4) .. +31 of each
+// query tile, so the two waves on a SIMD share their keys and split the rows.  Per tile a
+// wave runs a matrix phase (dV^T += dO^T P and dK^T += Q^T dS of the previous tile, then
+// S = Q K^T and dP = dO V^T of this tile: 32 products) and a vector phase (P, dS of this
+// tile).  The two groups (w / 4 = 0, 1) run half a tile apart, separated by workgroup
+// barriers, so that while one wave of a SIMD issues products the other does its vector
+// work.  The two row halves' dK and dV are summed through LDS at the end.
+// K rows stay in VGPRs; V rows of the 128 keys stay in LDS.  Q and dO tiles rotate
+// through three LDS stages (a tile is read during four consecutive half steps and loaded
+// during the two before).
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(StepArgs a, const __bf16* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ delta,
-                                                              float* __restrict__ dk, float* __restrict__ dv,
-                                                              int n_kb) {
-  __shared__ __attribute__((aligned(1024))) char q_lds[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char o_lds[2][TILE_BYTES];   // dO tiles
-  __shared__ float lse_lds[2][TILE_ROWS];
-  __shared__ float dlt_lds[2][TILE_ROWS];
-  __shared__ int lim_lds[2][TILE_ROWS];
+constexpr int KV_THREADS = 512;
+constexpr int KB = 128;                                // keys per workgroup
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;            // Q tile, then dO tile
+constexpr int N_STAGE = 3;
+constexpr int V_OFF = N_STAGE * STAGE_BYTES;           // 96 KB
+constexpr int SMEM_BYTES = V_OFF + KB * ROW_BYTES;     // + 32 KB of V rows
+
+// Workgroup barrier without a memory fence: memory operations may not move across it,
+// but no wait for outstanding loads is emitted (each wave waits for its own DMA).
+__device__ __forceinline__ void barrier_no_fence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, const __bf16* __restrict__ dout,
+                                                                 const float* __restrict__ lse,
+                                                                 const float* __restrict__ delta,
+                                                                 float* __restrict__ dk, float* __restrict__ dv) {
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float lse_lds[N_STAGE][TILE_ROWS];   // -LSE log2(e)
+  __shared__ __attribute__((aligned(16))) float dlt_lds[N_STAGE][TILE_ROWS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave & 3, grp = wave >> 2;
   const int lane = tid & 63, lk = lane & 31, lg = lane >> 5;
   const int L = a.L;
   const int G = a.h / a.n_kv;
   const int kb = (int)(blockIdx.x / (a.n_kv * a.b));   // keys early in the shard see more queries: first
   const int g = blockIdx.x % a.n_kv;
   const int bi = (blockIdx.x / a.n_kv) % a.b;
-  const int u0 = kb * 128;
-  const int uw = u0 + 32 * wave;            // this wave's first key
+  const int u0 = kb * KB;
+  const int uw = u0 + 32 * slot;            // this wave's first key
   const int u = uw + lk;                    // this lane's key
-  const int uc = min(u, L - 1);
+  auto limit = [&](int t) { return kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t); };
 
-  // resident K and V rows of this lane's key (B operands [k = d][n = key])
-  const int64_t krow = (((int64_t)bi * L + uc) * a.n_kv + g) * D + lg * 8;
-  bf16x8 kop[D / 16], vop[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kop[kk] = *(const bf16x8*)((const __bf16*)a.k + krow + kk * 16);
-    vop[kk] = *(const bf16x8*)((const __bf16*)a.v + krow + kk * 16);
-  }
   // first query row that may see key u0 (limits are nondecreasing in the query index)
   int t_lo = 0, t_hi = L;
   while (t_lo < t_hi) {
     const int mid = (t_lo + t_hi) >> 1;
-    if (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, mid) > u0) t_hi = mid;
+    if (limit(mid) > u0) t_hi = mid;
     else t_lo = mid + 1;
   }
+  if (t_lo >= L) return;                    // no query of this step sees these keys
   const int qt_first = t_lo / TILE_ROWS;
-  const int n_qt = (L + TILE_ROWS - 1) / TILE_ROWS - qt_first;   // query tiles per head
-  const int n_iter = n_qt > 0 ? n_qt * G : 0;
+  const int t_end = (L + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+  const int n_iter = (t_end / TILE_ROWS - qt_first) * G;   // (head, query tile) pairs
+
+  // resident K rows of this lane's key (B operand [k = d][n = key])
+  const int64_t krow = (((int64_t)bi * L + min(u, L - 1)) * a.n_kv + g) * D + lg * 8;
+  bf16x8 kop[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kop[kk] = *(const bf16x8*)((const __bf16*)a.k + krow + kk * 16);
+
   const float c2 = a.scale * LOG2E;
   const unsigned q_stride = (unsigned)a.h * D * 2;
-  const unsigned lane_off = dma_lane_offset(q_stride, lane, wave);
+  const unsigned kv_stride = (unsigned)a.n_kv * D * 2;
+  const int wq = wave & 3;                                    // DMA lane pattern of this wave
+  const unsigned q_lane_off = dma_lane_offset(q_stride, lane, wq);
 
-  f32x16 dka[D / 32], dva[D / 32];
+  // LDS read offsets.  Row reads (A operand [m = row][k = d], also the V rows as B
+  // operand): row lk of a 32-row block, chunk (2 kk + lg) ^ swz(lk), i.e. byte offset
+  // r_base ^ 32 kk.  Transposing reads (A operand [m = d][k = row]) of rows
+  // 16c + 8h + 4lg + {0..3} of a 32-row block, d = 32e + lane % 32 (see rows_transposed):
+  // byte offset t_base[h] ^ 64 e, plus 16c rows.  The bases stay in three VGPRs and the
+  // offsets are formed next to their reads.
+  const unsigned r_base = (unsigned)lk * ROW_BYTES + (unsigned)((lg ^ swz(lk)) * 16);
+  const int g16 = lane >> 4, j16 = lane & 15, jq = j16 >> 2;
+  const int low = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  unsigned t_base[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    t_base[h] = (unsigned)(8 * h + 4 * lg + jq) * ROW_BYTES +
+                (unsigned)((4 * jq + (low ^ ((2 * h + lg) & 3))) * 16) + (unsigned)((j16 & 1) * 8);
+
+  f32x16 dka[D / 32], dva[D / 32], sc, dp;
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) {
     dka[e] = f32x16{};
     dva[e] = f32x16{};
   }
+  bf16x8 pb[2] = {bf16x8{}, bf16x8{}}, ds[2] = {bf16x8{}, bf16x8{}};
 
-  // stage query tile `it` (head g*G + it / n_qt, tile qt_first + it % n_qt)
-  auto stage = [&](int it, int buf) {
-    const int hq = g * G + it / n_qt;
-    const int tq0 = (qt_first + it % n_qt) * TILE_ROWS;
-    const int64_t base = ((int64_t)bi * L * a.h + hq) * D;
-    const __amdgpu_buffer_rsrc_t qr = rows_rsrc((const __bf16*)a.q + base, L, q_stride);
-    const __amdgpu_buffer_rsrc_t orr = rows_rsrc(dout + base, L, q_stride);
-    dma_tile(qr, q_lds[buf], lane_off, (unsigned)tq0 * q_stride, q_stride, wave);
-    dma_tile(orr, o_lds[buf], lane_off, (unsigned)tq0 * q_stride, q_stride, wave);
-    if (tid < TILE_ROWS) {
-      const int tq = tq0 + tid;
-      const int64_t li = ((int64_t)bi * a.h + hq) * L + min(tq, L - 1);
-      const float l = lse[li];
-      lse_lds[buf][tid] = l > -INFINITY ? -l * LOG2E : -INFINITY;   // stored negated, base 2
-      dlt_lds[buf][tid] = delta[li];
-      lim_lds[buf][tid] = tq < L ? kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, tq) : 0;
+  // (head, first row) of a query tile index, advanced one tile at a time
+  struct Cursor {
+    int hq, tq0;
+  };
+  auto advance = [&](Cursor& c) {
+    c.tq0 += TILE_ROWS;
+    if (c.tq0 >= t_end) {
+      c.tq0 = qt_first * TILE_ROWS;
+      ++c.hq;
     }
   };
+  const Cursor first = {g * G, qt_first * TILE_ROWS};
+  auto stage_dma = [&](const Cursor& c, int buf) {   // group 1 only: Q and dO rows of a tile
+    const int64_t base = ((int64_t)bi * L * a.h + c.hq) * D;
+    char* dst = smem + buf * STAGE_BYTES;
+    dma_tile(rows_rsrc((const __bf16*)a.q + base, L, q_stride), dst, q_lane_off, (unsigned)c.tq0 * q_stride,
+             q_stride, wq);
+    dma_tile(rows_rsrc(dout + base, L, q_stride), dst + TILE_BYTES, q_lane_off, (unsigned)c.tq0 * q_stride,
+             q_stride, wq);
+  };
+  auto stats_index = [&](const Cursor& c) {
+    return ((int64_t)bi * a.h + c.hq) * L + min(c.tq0 + lane, L - 1);
+  };
+  auto stats_store = [&](const Cursor& c, int buf, float l, float dl) {
+    lse_lds[buf][lane] = (c.tq0 + lane < L && l > -INFINITY) ? -l * LOG2E : -INFINITY;
+    dlt_lds[buf][lane] = dl;
+  };
 
-  if (n_iter > 0) stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_iter) stage(it + 1, buf ^ 1);
-    const int tq0 = (qt_first + it % n_qt) * TILE_ROWS;
-    // skip when no query of the tile may see this wave's keys (limits grow with the
-    // query index; rows past the shard end have limit 0)
-    const int lim_last = lim_lds[buf][min(TILE_ROWS - 1, L - 1 - tq0)];
-    if (__builtin_amdgcn_readfirstlane(lim_last) > uw) {
-      const char* qt = q_lds[buf];
-      const char* ot = o_lds[buf];
-      f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  // ---- prologue: V rows, tile 0 (and its statistics and those of tile 1) in place ----------
+  {
+    const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc((const __bf16*)a.v + kv_base, L, kv_stride);
+    const unsigned v_lane_off = dma_lane_offset(kv_stride, lane, wave & 3);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          sc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk(qt, 32 * qs + lk, 2 * kk + lg),
-                                                           kop[kk], sc[qs], 0, 0, 0);
-          dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk(ot, 32 * qs + lk, 2 * kk + lg),
-                                                           vop[kk], dp[qs], 0, 0, 0);
-        }
-      // accumulator layout: lane = key u, register i of block qs = query
-      // tq0 + 32 qs + 8 (i/4) + 4 lg + (i%4)
-      bf16x8 pb[4], ds[4];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int r0 = 32 * qs + 8 * q4 + 4 * lg;
-          const f32x4 l4 = *(const f32x4*)&lse_lds[buf][r0];
-          const f32x4 d4 = *(const f32x4*)&dlt_lds[buf][r0];
-          const i32x4 m4 = *(const i32x4*)&lim_lds[buf][r0];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int i = 4 * q4 + x;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qs][i], c2, l4[x]));
-            if (u >= m4[x]) p = 0.f;
-            const float s = p * (dp[qs][i] - d4[x]);
-            pb[2 * qs + (i >> 3)][i & 7] = (__bf16)p;
-            ds[2 * qs + (i >> 3)][i & 7] = (__bf16)s;
-          }
-        }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e) {
-          dva[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_transposed(ot, lane, c, e), pb[c], dva[e], 0, 0, 0);
-          dka[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_transposed(qt, lane, c, e), ds[c], dka[e], 0, 0, 0);
-        }
+    for (int t = 0; t < 4; ++t) {
+      const int i = wave + 8 * t;            // i % 4 == wave % 4
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(smem + V_OFF + 1024 * i), 16, v_lane_off,
+                                               (unsigned)(u0 + 4 * i) * kv_stride, 0, 0);
     }
-    (void)tq0;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    u32x4* z = (u32x4*)(smem + 2 * STAGE_BYTES);   // stage 2 is read (with P = 0) before its first tile
+    for (int i = tid; i < STAGE_BYTES / 16; i += KV_THREADS) z[i] = u32x4{};
   }
-  if (u >= L) return;
+  Cursor cc = first;                          // tile of the current step
+  Cursor cs = first;                          // next tile to stage
+  if (grp == 1) stage_dma(cs, 0);
+  if (wave == 4) {
+    stats_store(cs, 0, lse[stats_index(cs)], delta[stats_index(cs)]);
+    Cursor c1 = cs;
+    advance(c1);
+    if (n_iter > 1) stats_store(c1, 1, lse[stats_index(c1)], delta[stats_index(c1)]);
+  }
+  advance(cs);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V rows and tile 0 are in place
+  __syncthreads();
+
+  // ---- main loop ---------------------------------------------------------------------------
+  // Every wave runs: matrix phase j, barrier, vector phase j, barrier.  Group 1 executes one
+  // extra barrier before the loop and group 0 one after it, so that between barriers 2j and
+  // 2j+1 group 0 runs matrix phase j and group 1 vector phase j-1, and between 2j+1 and
+  // 2j+2 group 0 runs vector phase j and group 1 matrix phase j.  Tile j (stage j % 3) is
+  // read from interval 2j+1 to 2j+4.  Group 1 starts the DMA of tile j as it enters its
+  // vector phase j-2 (interval 2j-1; the stage last held tile j-3, read up to interval 2j-2) and waits
+  // for it at the end of its matrix phase j-1 (interval 2j), one interval before tile j is
+  // first read.  Wave 4 loads the tile's statistics with it and stores them after the wait
+  // (first read in interval 2j+2).
+  auto matrix_phase = [&](int bcur, int bprev) {
+    unsigned rb = r_base, tb0 = t_base[0], tb1 = t_base[1];
+    __asm__ volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));   // keep the offsets next to their reads
+    auto row_op = [&](const char* blk, int kk) { return *(const bf16x8*)(blk + (rb ^ (32u * kk))); };
+    auto tr_op = [&](const char* blk, int c, int e) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(blk + c * 16 * ROW_BYTES + (tb0 ^ (64u * e))));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(blk + c * 16 * ROW_BYTES + (tb1 ^ (64u * e))));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    const char* qc = smem + bcur * STAGE_BYTES + grp * 32 * ROW_BYTES;    // this wave's rows
+    const char* oc = qc + TILE_BYTES;
+    const char* qp = smem + bprev * STAGE_BYTES + grp * 32 * ROW_BYTES;
+    const char* op = qp + TILE_BYTES;
+    const char* vt = smem + V_OFF + slot * 32 * ROW_BYTES;
+    // previous tile: dV^T += dO^T P, dK^T += Q^T dS (8 slots of two products)
+    bf16x8 xa[3], xb[3];
+    xa[0] = tr_op(op, 0, 0);
+    xb[0] = tr_op(qp, 0, 0);
+    xa[1] = tr_op(op, 0, 1);
+    xb[1] = tr_op(qp, 0, 1);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (x + 2 < 8) {
+        xa[(x + 2) % 3] = tr_op(op, (x + 2) >> 2, (x + 2) & 3);
+        xb[(x + 2) % 3] = tr_op(qp, (x + 2) >> 2, (x + 2) & 3);
+      }
+      dva[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[x % 3], pb[x >> 2], dva[x & 3], 0, 0, 0);
+      dka[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[x % 3], ds[x >> 2], dka[x & 3], 0, 0, 0);
+    }
+    // this tile: S = Q K^T, dP = dO V^T (8 slots of two products)
+    sc = f32x16{};
+    dp = f32x16{};
+    bf16x8 ya[3], yb[3], yv[3];
+    ya[0] = row_op(qc, 0);
+    yb[0] = row_op(oc, 0);
+    yv[0] = row_op(vt, 0);
+    ya[1] = row_op(qc, 1);
+    yb[1] = row_op(oc, 1);
+    yv[1] = row_op(vt, 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (kk + 2 < D / 16) {
+        ya[(kk + 2) % 3] = row_op(qc, kk + 2);
+        yb[(kk + 2) % 3] = row_op(oc, kk + 2);
+        yv[(kk + 2) % 3] = row_op(vt, kk + 2);
+      }
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya[kk % 3], kop[kk], sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[kk % 3], yv[kk % 3], dp, 0, 0, 0);
+    }
+  };
+  // accumulator layout: lane = key u, register i = row 8 (i / 4) + 4 lg + (i % 4) of the
+  // wave's 32-row half
+  auto vector_phase = [&](int j, int bcur) {
+    const int r0 = cc.tq0 + 32 * grp;
+    bool skip = j >= n_iter || r0 >= L;
+    if (!skip) skip = limit(min(r0 + 31, L - 1)) <= uw;
+    skip = __builtin_amdgcn_readfirstlane((int)skip) != 0;
+    if (skip) {
+      pb[0] = pb[1] = ds[0] = ds[1] = bf16x8{};
+      return;
+    }
+    const bool full = limit(r0) >= uw + 32;   // rows past the shard end have LSE = -inf
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int rr = 32 * grp + 8 * q4 + 4 * lg;
+      const f32x4 l4 = *(const f32x4*)&lse_lds[bcur][rr];
+      const f32x4 d4 = *(const f32x4*)&dlt_lds[bcur][rr];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = 4 * q4 + x;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, l4[x]));
+        sc[i] = p;
+        dp[i] = p * (dp[i] - d4[x]);
+      }
+    }
+    if (!full) {
+      // keep this a real (scalar) branch: only diagonal tiles pay for the mask
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = r0 + 8 * (i >> 2) + 4 * lg + (i & 3);
+        if (u >= limit(row)) {
+          sc[i] = 0.f;
+          dp[i] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        pb[c][x] = (__bf16)sc[8 * c + x];
+        ds[c][x] = (__bf16)dp[8 * c + x];
+      }
+  };
+
+  float st_l = 0.f, st_d = 0.f;             // statistics in flight (wave 4)
+  if (grp == 1) {
+    if (n_iter > 1) stage_dma(cs, 1);
+    barrier_no_fence();
+  }
+  int bcur = 0;
+  for (int j = 0; j <= n_iter; ++j) {
+    const int bprev = bcur == 0 ? 2 : bcur - 1;
+    const int bnext = bcur == 2 ? 0 : bcur + 1;
+    const int bnext2 = bprev;               // stage of tile j + 2
+    matrix_phase(bcur, bprev);
+    if (grp == 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads for tile j + 1 landed
+      if (wave == 4 && j >= 1 && j + 1 < n_iter) {
+        Cursor c1 = cc;
+        advance(c1);
+        stats_store(c1, bnext, st_l, st_d);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the barrier
+      }
+    }
+    barrier_no_fence();
+    if (grp == 1 && j + 2 < n_iter) {
+      advance(cs);                          // cs: tile j + 2
+      stage_dma(cs, bnext2);
+      if (wave == 4) {
+        const int64_t si = stats_index(cs);
+        st_l = lse[si];
+        st_d = delta[si];
+      }
+    }
+    vector_phase(j, bcur);
+    advance(cc);
+    bcur = bnext;
+    barrier_no_fence();
+  }
+  if (grp == 0) barrier_no_fence();
+
+  // ---- the two row halves' dK and dV meet in LDS; group 0 writes ---------------------------
+  __syncthreads();
+  f32x4* red = (f32x4*)(smem + slot * 32768);   // 2 x 16 x 64 x 16 B per key slot
+  if (grp == 1) {
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        red[((0 * 4 + e) * 4 + ib) * 64 + lane] =
+            f32x4{dka[e][4 * ib], dka[e][4 * ib + 1], dka[e][4 * ib + 2], dka[e][4 * ib + 3]};
+        red[((1 * 4 + e) * 4 + ib) * 64 + lane] =
+            f32x4{dva[e][4 * ib], dva[e][4 * ib + 1], dva[e][4 * ib + 2], dva[e][4 * ib + 3]};
+      }
+  }
+  __syncthreads();
+  if (grp == 1 || u >= L) return;
   // lane holds dK^T / dV^T [d = 32e + 8 (i/4) + 4 lg + i%4][key u]
   float* krow_out = dk + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
   float* vrow_out = dv + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
@@ -382,13 +564,15 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(StepArgs a, const 
   for (int e = 0; e < D / 32; ++e)
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
+      const f32x4 ok = red[((0 * 4 + e) * 4 + ib) * 64 + lane];
+      const f32x4 ov = red[((1 * 4 + e) * 4 + ib) * 64 + lane];
       f32x4* pk = (f32x4*)(krow_out + 32 * e + 8 * ib);
       f32x4* pv = (f32x4*)(vrow_out + 32 * e + 8 * ib);
       f32x4 vk = *pk, vv = *pv;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        vk[x] += a.scale * dka[e][4 * ib + x];
-        vv[x] += dva[e][4 * ib + x];
+        vk[x] += a.scale * (dka[e][4 * ib + x] + ok[x]);
+        vv[x] += dva[e][4 * ib + x] + ov[x];
       }
       *pk = vk;
       *pv = vv;
@@ -414,15 +598,15 @@ hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float
   const int n_qb = (a.L + 32 * PB - 1) / (32 * PB);
   const int inner = a.n_kv * a.b * (G / Hw);
   const int64_t grid_q = (int64_t)n_qb * inner;
-  const int n_kb = (a.L + 127) / 128;
+  const int n_kb = (a.L + KB - 1) / KB;
   const int64_t grid_k = (int64_t)n_kb * a.n_kv * a.b;
   if (grid_q > 0x7fffffff || grid_k > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid_q), dim3(THREADS), 0, s, a,
                      (const __bf16*)dout, lse, delta, dq, Hw, n_qb, inner);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_k), dim3(THREADS), 0, s, a,
-                     (const __bf16*)dout, lse, delta, dk, dv, n_kb);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_k), dim3(KV_THREADS), 0, s, a,
+                     (const __bf16*)dout, lse, delta, dk, dv);
   return hipGetLastError();
 }
 
