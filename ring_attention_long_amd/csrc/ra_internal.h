@@ -60,6 +60,37 @@ __host__ __device__ inline int kv_limit(int causal, int layout, int N, int L, in
   return (int)clamp64(P - (int64_t)ks * L + 1, 0, L);
 }
 
+// ---------------------------------------------------------------------------------------
+// Asynchronous global -> LDS copy (buffer_load_dwordx4 ... lds): every lane moves the 16
+// bytes at voffset + soffset of the buffer to LDS address lds_base + 16 * lane.  Reads at
+// or past the descriptor's num_records bytes return zeros.  The copy is issued through
+// inline assembly, so the compiler does not track it: it would otherwise wait for every
+// outstanding copy before each later LDS read, including reads of other buffers.  The
+// caller owns the wait: s_waitcnt vmcnt before any wave reads the destination, then a
+// barrier.  M0 carries the LDS base; no compiler-generated code in these kernels uses M0.
+// ---------------------------------------------------------------------------------------
+typedef int dma_rsrc __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ dma_rsrc make_dma_rsrc(const void* base, unsigned num_records) {
+  const uint64_t b = (uint64_t)base;
+  return dma_rsrc{(int)__builtin_amdgcn_readfirstlane((unsigned)b),
+                  (int)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xFFFFu),
+                  (int)__builtin_amdgcn_readfirstlane(num_records), 0x00020000};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_to_lds(dma_rsrc rsrc, const void* lds_dst, unsigned voffset,
+                                             unsigned soffset) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
+                   : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Epilogue of a forward step kernel.
 enum StepMode : int {
   MODE_PART = 0,   // write this step's normalised (O, LSE) partial

@@ -53,21 +53,19 @@ __device__ __forceinline__ unsigned dma_lane_offset(unsigned row_stride, int lan
   const int lrow = lane >> 4;
   return (unsigned)lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow + w)) * 16;
 }
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, char* dst, unsigned lane_off,
-                                         unsigned row0_off, unsigned row_stride, int w) {
+__device__ __forceinline__ void dma_tile(dma_rsrc rsrc, char* dst, unsigned lane_off, unsigned row0_off,
+                                         unsigned row_stride, int w) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int i = w + 4 * t;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * i), 16, lane_off,
-                                             row0_off + (unsigned)(4 * i) * row_stride, 0, 0);
+    dma16_to_lds(rsrc, dst + 1024 * i, lane_off, row0_off + (unsigned)(4 * i) * row_stride);
   }
 }
 // Buffer descriptor covering rows 0..rows-1 (row_stride bytes apart, 256 B each) from base;
 // reads beyond return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows,
-                                                            unsigned row_stride) {
-  const int n = rows > 0 ? (int)((unsigned)(rows - 1) * row_stride + ROW_BYTES) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, n, 0x00020000);
+__device__ __forceinline__ dma_rsrc rows_rsrc(const void* base, int rows, unsigned row_stride) {
+  const unsigned n = rows > 0 ? (unsigned)(rows - 1) * row_stride + ROW_BYTES : 0u;
+  return make_dma_rsrc(base, n);
 }
 // Row read: 16 B of row r, chunk c.
 __device__ __forceinline__ bf16x8 row_chunk(const char* tile, int r, int c) {
@@ -175,8 +173,8 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(StepArgs a, const __
 
   const unsigned row_stride = (unsigned)a.n_kv * D * 2;
   const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
-  const __amdgpu_buffer_rsrc_t k_rsrc = rows_rsrc((const __bf16*)a.k + kv_base, L, row_stride);
-  const __amdgpu_buffer_rsrc_t v_rsrc = rows_rsrc((const __bf16*)a.v + kv_base, L, row_stride);
+  const dma_rsrc k_rsrc = rows_rsrc((const __bf16*)a.k + kv_base, L, row_stride);
+  const dma_rsrc v_rsrc = rows_rsrc((const __bf16*)a.v + kv_base, L, row_stride);
   const unsigned lane_off = dma_lane_offset(row_stride, lane, wave);
 
   f32x16 acc[D / 32];
@@ -372,13 +370,12 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // ---- prologue: V rows, tile 0 (and its statistics and those of tile 1) in place ----------
   {
     const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
-    const __amdgpu_buffer_rsrc_t vr = rows_rsrc((const __bf16*)a.v + kv_base, L, kv_stride);
+    const dma_rsrc vr = rows_rsrc((const __bf16*)a.v + kv_base, L, kv_stride);
     const unsigned v_lane_off = dma_lane_offset(kv_stride, lane, wave & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = wave + 8 * t;            // i % 4 == wave % 4
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(smem + V_OFF + 1024 * i), 16, v_lane_off,
-                                               (unsigned)(u0 + 4 * i) * kv_stride, 0, 0);
+      dma16_to_lds(vr, smem + V_OFF + 1024 * i, v_lane_off, (unsigned)(u0 + 4 * i) * kv_stride);
     }
     u32x4* z = (u32x4*)(smem + 2 * STAGE_BYTES);   // stage 2 is read (with P = 0) before its first tile
     for (int i = tid; i < STAGE_BYTES / 16; i += KV_THREADS) z[i] = u32x4{};

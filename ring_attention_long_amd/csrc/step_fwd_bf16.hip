@@ -166,21 +166,17 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // past the shard end fail the hardware range check and arrive as zeros (always masked).
   const unsigned row_stride = (unsigned)a.n_kv * D * 2;   // bytes between keys in HBM
   const int num_records = (int)((unsigned)(L - 1) * row_stride + ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(kp + kv_base), 0, num_records, 0x00020000);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(vp + kv_base), 0, num_records, 0x00020000);
+  const dma_rsrc k_rsrc = make_dma_rsrc(kp + kv_base, (unsigned)num_records);
+  const dma_rsrc v_rsrc = make_dma_rsrc(vp + kv_base, (unsigned)num_records);
   const int ws = wave & 3;
   const unsigned lrow = lane >> 4;                       // row within a 1 KB load
   const unsigned k_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ ((4 * ws + lrow) & 15)) * 16;
   const unsigned v_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow)) * 16;
-  auto issue_tile_dma = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, unsigned off, int j) {
+  auto issue_tile_dma = [&](dma_rsrc rsrc, char* dst, unsigned off, int j) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = ws + 4 * t;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off,
-          (unsigned)(j * BN + 4 * i) * row_stride, 0, 0);
+      dma16_to_lds(rsrc, dst + 1024 * i, off, (unsigned)(j * BN + 4 * i) * row_stride);
     }
   };
 
