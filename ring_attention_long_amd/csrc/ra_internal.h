@@ -67,7 +67,8 @@ __host__ __device__ inline int kv_limit(int causal, int layout, int N, int L, in
 // inline assembly, so the compiler does not track it: it would otherwise wait for every
 // outstanding copy before each later LDS read, including reads of other buffers.  The
 // caller owns the wait: s_waitcnt vmcnt before any wave reads the destination, then a
-// barrier.  M0 carries the LDS base; no compiler-generated code in these kernels uses M0.
+// barrier, and the destination must not be read or written between the call and that
+// wait.  M0 carries the LDS base; no compiler-generated code in these kernels uses M0.
 // ---------------------------------------------------------------------------------------
 typedef int dma_rsrc __attribute__((ext_vector_type(4)));
 
@@ -84,10 +85,13 @@ __device__ __forceinline__ void dma16_to_lds(dma_rsrc rsrc, const void* lds_dst,
                                              unsigned soffset) {
   const unsigned m = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // s_nop: one wait state between writing M0 and an LDS-DMA load that reads it.  No memory
+  // clobber: the destination is never read before the caller's wait and barrier, and the
+  // compiler may keep scheduling LDS reads of other buffers around the load.
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    :
                    : "s"(m), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
-                   : "memory", "m0");
+                   : "m0");
 }
 #pragma clang diagnostic pop
 

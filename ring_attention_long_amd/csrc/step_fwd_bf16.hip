@@ -27,19 +27,25 @@
 //  * The probabilities never leave registers: the score accumulator, rounded to bf16, is
 //    exactly the B operand (P^T) of the second product O^T += V^T P^T, because the order
 //    in which the contraction visits keys is free as long as A and B agree.
-//  * Online softmax in base 2 with scale * log2(e) folded into one FMA per score, and a
-//    lazy rescale: the running maximum used for exponentiation moves only when a row's new
-//    maximum exceeds it by more than TAU (= 8, so P <= 2^8); the final O / l is unchanged
-//    in exact arithmetic, and most tiles skip the O *= alpha pass.
+//  * Online softmax in base 2 with scale * log2(e) folded into one FMA per score.  The
+//    running maximum m only has to keep the weights 2^(s - m) finite, not at most 1: the
+//    final O / l is the same in exact arithmetic for any m.  So most tiles exponentiate
+//    against m as it stands, without computing their own maximum, and check afterwards
+//    that the tile's weights stayed small (row-sum share <= 2^24); only a tile that fails
+//    the check, or a row without a maximum yet, takes the maximum and rescales, and then
+//    lazily: m moves only when the new maximum exceeds it by more than TAU = 8.  The
+//    softmax is the vector-unit bound of the kernel (the SIMD's vector issue is shared
+//    with the matrix instructions of the other wave), so every instruction saved counts.
 //  * Causal masking (page 1, "Causal Masking Dynamics"): with positions increasing inside
 //    every shard, the allowed keys of a row are a prefix [0, limit) of the KV shard, so a
 //    wave skips every key tile at or beyond its largest limit, runs maskless below its
 //    smallest limit, and masks only the diagonal tiles in between.
-//  * K/V tiles are double-buffered in LDS and staged by DMA (global_load_lds): no VGPRs
-//    and no vector instructions.  Group 1 starts the loads of the next K and V tiles at
-//    the end of its softmax phase (the shorter phase), into buffers both groups have
-//    finished reading, a full step before they are read.  V is stored row-major and read with the gfx950
-//    transposing LDS load, which yields the V^T operand directly.
+//  * K/V tiles rotate through three LDS stages each and are staged by DMA
+//    (buffer_load ... lds): no VGPRs and no vector instructions.  Each wave issues its
+//    four loads of a tile one at a time between the exponentials of its softmax phase
+//    (group 0 V tiles, group 1 K tiles), so the texture unit sees a steady trickle instead
+//    of one burst, and waits for them a whole step later.  V is stored row-major and read with
+//    the gfx950 transposing LDS load, which yields the V^T operand directly.
 //  * Workgroups are launched heaviest query block first (causal work grows with the query
 //    position), with the KV head as the fastest-varying index so that neighbouring
 //    workgroups, dispatched round-robin over the 8 XCDs, put each KV head's tiles into
@@ -63,6 +69,12 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int ROW_BYTES = D * 2;  // one key's K or V row: 256 B, sixteen 16-byte chunks
 constexpr int TILE_BYTES = BN * ROW_BYTES;   // 16 KB; written by 16 DMA loads of 1 KB
 constexpr float TAU = 8.0f;       // lazy-rescale threshold, log2 units
+constexpr int PREFETCH = 2;       // matrix-phase operand slots read ahead
+
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -89,8 +101,8 @@ __device__ __forceinline__ void barrier_no_fence() {
 template <int MODE>
 __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, int heads_per_wg,
                                                                   int n_qb, int inner_count) {
-  __shared__ __attribute__((aligned(1024))) char k_lds[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_lds[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds[3][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds[3][TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -116,7 +128,6 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const __bf16* qp = (const __bf16*)a.q;
   const __bf16* kp = (const __bf16*)a.k;
   const __bf16* vp = (const __bf16*)a.v;
-  const int64_t kv_row = (int64_t)a.n_kv * D;          // elements between keys
   const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
 
   // ---- key limits and tile ranges ---------------------------------------------------
@@ -179,6 +190,18 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
       dma16_to_lds(rsrc, dst + 1024 * i, off, (unsigned)(j * BN + 4 * i) * row_stride);
     }
   };
+  // In the main loop each wave issues its four loads of a tile spread over its softmax
+  // phase: group 0 stages V tiles, group 1 K tiles.  Loads of tiles past the wave's last
+  // one point beyond the buffer (zeros, no memory traffic) into a stage nobody reads
+  // again, so every softmax phase issues exactly four loads and the waits can count them.
+  const dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
+  const unsigned my_dma_off = group ? k_dma_off : v_dma_off;
+  char* const my_lds = group ? &k_lds[0][0] : &v_lds[0][0];
+  auto issue_one = [&](int tile, int stage, int t) {
+    const int i = ws + 4 * t;
+    const unsigned soff = tile < n_tiles ? (unsigned)(tile * BN + 4 * i) * row_stride : 0x80000000u;
+    dma16_to_lds(my_rsrc, my_lds + stage * TILE_BYTES + 1024 * i, my_dma_off, soff);
+  };
 
   // ---- the two phases of one wave ------------------------------------------------------
   // K operand of d-step kk, key sub-tile jj: row 32jj + lq, chunk 2kk + lg (16 B).  The
@@ -221,34 +244,62 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // keep one home: where the wave has no tile j-1, P is zero (the V buffer holds finite
   // data: a real tile, or zeros before the first); where it has no tile j, the scores
   // are computed from whatever K buffer is there and never used.
-  auto matrix_phase = [&](int j) {
-    const char* vt = v_lds[(j - 1) & 1];
-    const char* kt = k_lds[j & 1];
+  auto matrix_phase = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_c)::value;     // compile-time: LDS addresses fold
+    const char* vt = v_lds[(stage + 2) % 3];            // V(j-1)
+    const char* kt = k_lds[stage];                      // K(j)
     sc[0] = f32x16{};
     sc[1] = f32x16{};
-    bf16x8 va[3], ka[3];
-    va[0] = v_operand(vt, 0, 0);
-    ka[0] = k_operand(kt, 0, 0);
-    va[1] = v_operand(vt, 0, 1);
-    ka[1] = k_operand(kt, 0, 1);
+    bf16x8 va[PREFETCH + 1], ka[PREFETCH + 1];
+#pragma unroll
+    for (int x = 0; x < PREFETCH; ++x) {
+      va[x] = v_operand(vt, x >> 2, x & 3);
+      ka[x] = k_operand(kt, x >> 1, x & 1);
+    }
+    // Scheduling fences keep the program order: slot x first issues the reads of slot
+    // x + PREFETCH, then its two products, whose operands were read PREFETCH slots
+    // earlier, so the LDS latency hides behind 2 PREFETCH products.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      if (x + 2 < 16) {
-        va[(x + 2) % 3] = v_operand(vt, (x + 2) >> 2, (x + 2) & 3);
-        ka[(x + 2) % 3] = k_operand(kt, (x + 2) >> 1, (x + 2) & 1);
+      if (x + PREFETCH < 16) {
+        va[(x + PREFETCH) % (PREFETCH + 1)] = v_operand(vt, (x + PREFETCH) >> 2, (x + PREFETCH) & 3);
+        ka[(x + PREFETCH) % (PREFETCH + 1)] = k_operand(kt, (x + PREFETCH) >> 1, (x + PREFETCH) & 1);
       }
-      acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % 3], pb[x >> 2], acc[x & 3], 0, 0, 0);
-      sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % 3], qop[x >> 1], sc[x & 1], 0, 0, 0);
+      acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % (PREFETCH + 1)], pb[x >> 2], acc[x & 3], 0, 0, 0);
+      sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (PREFETCH + 1)], qop[x >> 1], sc[x & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int x = 0; x < 14; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next slot's LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // this slot's two MFMAs
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // Softmax phase of step j: mask, running max, lazy rescale, P = exp2(S c - m), row sum.
-  auto softmax_phase = [&](int j) {
+  // P = exp2(S c2 - m) into pb (rounded to bf16: the B operand of the next P V), and this
+  // lane's share of the row sum, taken in fp32 from the unrounded weights (the LSE keeps
+  // fp32 accuracy).  The scores in sc are left intact.
+  auto exponentiate = [&](float neg_m) __attribute__((always_inline)) {
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + x], c2, neg_m));
+        pb[c][x] = (__bf16)p;
+        r[c] += p;
+      }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+  };
+  // Softmax phase of step j: mask, P = exp2(S c2 - m), row sum.  Fast path: exponentiate
+  // against the running maximum as it stands, without computing this tile's maximum; it
+  // stands as long as no weight gets large (this lane's tile sum <= 2^24, which bounds
+  // every weight, keeps P and O finite and is checked together with inf and NaN).
+  // Otherwise, and while a row has no maximum yet, take the tile's maximum and rescale
+  // lazily: the maximum moves only when the new one exceeds it by more than TAU.
+  auto softmax_phase = [&](int j, int stage) __attribute__((always_inline)) {
+    // this wave's loads: group 0 V(j+1) into the stage of V(j-2), group 1 K(j+3) into the
+    // stage of K(j); both stages were last read in interval 2j
+    const int dma_tile_idx = group ? j + 3 : j + 1;
+    const int dma_stage = group ? stage : (stage == 2 ? 0 : stage + 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) issue_one(dma_tile_idx, dma_stage, t);
     if (j >= wave_tiles) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) pb[c] = bf16x8{};
@@ -264,43 +315,37 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
         for (int i = 0; i < 16; ++i)
           if (32 * jj + 8 * (i >> 2) + (i & 3) >= thr) sc[jj][i] = -INFINITY;
     }
-    float mx;
-    {
-      float x0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
-      float x1 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);
+    bool full_path = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    float rs = 0.f;
+    if (!full_path) {
+      rs = exponentiate(-m_run);
+      full_path = __builtin_amdgcn_ballot_w64(!(rs <= 0x1p24f)) != 0;
+    }
+    if (full_path) {
+      float mx;
+      {
+        float x0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+        float x1 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);
 #pragma unroll
-      for (int i = 3; i < 15; i += 2) {
-        x0 = fmaxf(fmaxf(x0, sc[0][i]), sc[0][i + 1]);
-        x1 = fmaxf(fmaxf(x1, sc[1][i]), sc[1][i + 1]);
+        for (int i = 3; i < 15; i += 2) {
+          x0 = fmaxf(fmaxf(x0, sc[0][i]), sc[0][i + 1]);
+          x1 = fmaxf(fmaxf(x1, sc[1][i]), sc[1][i + 1]);
+        }
+        x0 = fmaxf(fmaxf(x0, sc[0][15]), x1);
+        x0 = fmaxf(x0, sc[1][15]);
+        mx = lane_pair_max(x0) * c2;
       }
-      x0 = fmaxf(fmaxf(x0, sc[0][15]), x1);
-      x0 = fmaxf(x0, sc[1][15]);
-      mx = lane_pair_max(x0) * c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) acc[e] *= alpha;
+        m_run = m_new;
+      }
+      rs = exponentiate(m_run == -INFINITY ? 0.f : -m_run);
     }
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) acc[e] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][i], c2, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][i], c2, neg_m));
-      sc[0][i] = p0;
-      sc[1][i] = p1;
-      rs0 += p0;
-      rs1 += p1;
-    }
-    l_run += rs0 + rs1;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pb[c][x] = (__bf16)sc[c >> 1][8 * (c & 1) + x];
+    l_run += rs;
   };
   // ---- main loop -------------------------------------------------------------------------
   // Every wave runs the same sequence: matrix phase of step j, barrier, softmax phase of
@@ -309,39 +354,49 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // alternate between matrix and vector work.  Numbering the intervals between barriers,
   // interval 2j+1 holds group 0's matrix phase j and group 1's softmax phase j-1, interval
   // 2j+2 group 0's softmax phase j and group 1's matrix phase j.  K(j) is read in
-  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4.
-  // Group 1 stages: at the end of its softmax phase j (interval 2j+3) it starts the DMA of
-  // K(j+2) into the buffer of K(j) and of V(j+1) into the buffer of V(j-1), both last read
-  // in interval 2j+2, and waits for it at the end of its next matrix phase (interval
-  // 2j+4), one interval before the data is first read.  The first tiles come from the
-  // prologue: K(0) fully loaded, K(1) and V(0) in flight until group 1's first matrix
-  // phase ends.
-  if (group == 1 && n_tiles > 0) {
-    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);
-  }
+  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4; tile j lives in stage j % 3.
+  // Staging: in its softmax phase j (interval 2j+2) group 0 loads V(j+1), first read in
+  // interval 2j+5; in its softmax phase j (interval 2j+3) group 1 loads K(j+3), first read
+  // in interval 2j+7.  Each wave waits for its loads at the end of its next softmax phase
+  // (vmcnt(4): only the four just issued may still be in flight), before the barrier that
+  // opens the first interval reading them.  The prologue loads K(0), K(1), V(0) completely
+  // and starts K(2), which group 1's first wait covers.
   {
-    u32x4* z = (u32x4*)v_lds[1];        // read by the (zero-P) PV of step 0
+    u32x4* z = (u32x4*)v_lds[2];        // read by the (zero-P) PV of step 0
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q and K(0) are in place
+  if (group == 1) {
+    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);   // rows past L arrive as zeros
+    issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, 1);
+  } else {
+    issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, K(0), K(1), V(0) are in place
   __syncthreads();
   if (group == 1) {
-    if (n_tiles > 1) issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, 1);
-    if (n_tiles > 0) issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, 0);
+    issue_tile_dma(k_rsrc, k_lds[2], k_dma_off, 2);
     barrier_no_fence();
   }
-  for (int j = 0; j <= n_tiles; ++j) {
-    matrix_phase(j);
-    if (group == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+  auto step = [&](int j, auto stage_c) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);        // matrix phase first in the SIMD's issue arbitration
+    matrix_phase(stage_c);
+    __builtin_amdgcn_s_setprio(0);
     barrier_no_fence();
-    softmax_phase(j);
-    if (group == 1) {
-      if (j + 2 < n_tiles) issue_tile_dma(k_rsrc, k_lds[j & 1], k_dma_off, j + 2);
-      if (j + 1 < n_tiles) issue_tile_dma(v_rsrc, v_lds[(j + 1) & 1], v_dma_off, j + 1);
-    }
+    softmax_phase(j, decltype(stage_c)::value);
+    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): this wave's loads of its previous softmax phase landed
     barrier_no_fence();
+  };
+  // unrolled by the three stages so that every LDS address in the matrix phase is a
+  // per-lane base plus an immediate
+  for (int j = 0; j <= n_tiles; j += 3) {
+    step(j, Stage<0>{});
+    if (j + 1 > n_tiles) break;
+    step(j + 1, Stage<1>{});
+    if (j + 2 > n_tiles) break;
+    step(j + 2, Stage<2>{});
   }
   if (group == 0) barrier_no_fence();
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): no load into LDS outlives the loop
 
   // ---- epilogue ------------------------------------------------------------------------
   const float l_tot = lane_pair_sum(l_run);
