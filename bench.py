@@ -1,6 +1,8 @@
-"""Benchmark of one device's forward ring pass on one MI355X.
+"""Benchmark of one device's ring pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --workload bwd_striped_causal_8k      # the backward pass
+    python bench.py --sweep                                # L sweep, every shard, merge GB/s
 
 A "step" here is one whole ring pass of the hot path for one device: N ring steps, each a
 fused attention-step kernel (QK^T, mask, online softmax, PV, merge into the running
@@ -8,10 +10,11 @@ fused attention-step kernel (QK^T, mask, online softmax, PV, merge into the runn
 Inputs are seeded synthetic N(0, 1) bf16 tensors resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is useful attention TFLOP/s (4 h d FLOPs per allowed
-(query, key) pair; causal pairs above the diagonal do not count).  `roofline` reports the
-step kernel (the dominant kernel) against the bf16 dense MFMA peak, from per-launch HIP
-events on the compute stream; `cpu_baseline` times the fp64 oracle on a bounded sample of
-the same workload on the host cores.
+(query, key) pair; causal pairs above the diagonal do not count; the backward counts
+10 h d, five products, the FlashAttention convention of 2.5 x the forward).  `roofline`
+reports the dominant kernel against the bf16 dense MFMA peak, from per-launch HIP events
+on the compute stream; `cpu_baseline` times the fp64 oracle on a bounded sample of the
+same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -45,8 +48,16 @@ WORKLOADS = {
                          "shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
                          "contiguous", False, 0, 1002),
 }
+BWD_WORKLOADS = {
+    "bwd_striped_causal_8k": ("ring_bwd striped causal, S=65536 N=8 L=8192 h=32 n_kv=8 d=128 "
+                              "bf16, shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
+                              "striped", True, 0, 1005),
+}
 DEFAULT_WORKLOAD = "striped_causal_32k"
 METRIC = "ring-step attention TFLOP/s (bf16, causal) and % of MI355X MFMA peak"
+BWD_METRIC = ("ring-step attention backward TFLOP/s (bf16, causal, 2.5x forward FLOPs) and % of "
+              "MI355X MFMA peak")
+XGMI_LINK_GBPS = 153.0     # one xGMI link, one direction (for the modelled ring transfer)
 
 
 def log(*a):
@@ -122,12 +133,264 @@ def copy_calibration(mib, steps):
                                            "dispatches": steps, "kernel": "copy_f32_kernel"}}))
 
 
+def cpu_baseline_bwd(inp, cfg, layout, causal, shard, budget_s=20.0):
+    """Time the fp64 oracle's dQ of whole query rows (all heads, every key) until about
+    budget_s seconds; report TFLOP/s counting the three products a dQ row needs (S, dP,
+    dQ: 6 h d FLOPs per allowed pair)."""
+    from oracle import shard_dq_rows, shard_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    x = {k: inp[k].astype(np.float64) for k in ("q", "k_all", "v_all", "dout")}
+    N, L, h, d = cfg["N"], cfg["L"], cfg["h"], cfg["d"]
+    toks = shard_tokens(layout, N, L)
+    all_pos = np.sort(np.concatenate(toks))
+    rng = np.random.default_rng(98)
+    rows_done, pairs, elapsed = [], 0, 0.0
+    chunk = 8
+    while elapsed < budget_s and len(rows_done) < L:
+        rows = rng.choice(L, size=chunk, replace=False)
+        t0 = time.perf_counter()
+        shard_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard,
+                      layout=layout, causal=causal)
+        elapsed += time.perf_counter() - t0
+        rows_done.extend(rows.tolist())
+        pairs += int(np.searchsorted(all_pos, toks[shard][rows], side="right").sum()) if causal \
+            else chunk * N * L
+    flops = 6.0 * h * d * pairs * cfg["b"]
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"dQ of {len(rows_done)} random query rows of shard {shard} x all {h} heads "
+                      f"against all {N * L} keys (fp64 numpy, {elapsed:.1f} s; 6 h d FLOPs per pair)"}
+
+
+def run_backward(args):
+    import torch
+
+    import ring_attention_long_amd as ra
+    import synth
+    from ring_attention_long_amd import accounting
+
+    desc, cfg, layout, causal, shard, seed = BWD_WORKLOADS[args.workload]
+    b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
+    log(f"[bench] workload {args.workload}: {desc}")
+    inp = synth.shard_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16", with_dout=True)
+    dev = torch.device("cuda:0")
+    g = lambda name: torch.from_numpy(inp[name]).to(dev, torch.bfloat16)  # noqa: E731
+    q, k_all, v_all, dout = g("q"), g("k_all"), g("v_all"), g("dout")
+    o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+    p = ra.make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                        dtype=torch.bfloat16)
+    ws = torch.empty(int(ra._lib.lib().ra_ring_bwd_workspace(__import__("ctypes").byref(p))),
+                     device=dev, dtype=torch.uint8)
+    out = (torch.empty((b, L, h, d), device=dev, dtype=torch.float32),
+           torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32),
+           torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32))
+    pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+    flops = 10.0 * h * d * pairs
+    compute = torch.cuda.current_stream()
+
+    def one_pass():
+        ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal, layout=layout,
+                    workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        one_pass()
+        log(f"[bench] warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(compute)
+    for _ in range(args.steps):
+        one_pass()
+    t1.record(compute)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+
+    # Per-step launches of ra_step_bwd (dQ kernel + dK/dV kernel) on the compute stream,
+    # K/V read in place, timed with HIP events.
+    delta = ra.bwd_preprocess(o, dout)
+    dq, dk, dv = out
+    step_ms, step_flops = [], 0
+    for k in range(N):
+        src = (shard - k) % N
+        pk = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal,
+                              layout=layout)
+        if pk == 0:
+            continue
+        ts = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(compute)
+            ra.step_bwd(q, k_all[src], v_all[src], dout, lse, delta, N=N, q_shard=shard,
+                        kv_shard=src, causal=causal, layout=layout, dq_acc=dq, dk_acc=dk[src],
+                        dv_acc=dv[src])
+            e1.record(compute)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        step_ms.append(float(np.median(ts)))
+        step_flops += 10.0 * h * d * pk
+    kern_ms = sum(step_ms)
+    achieved = step_flops / (kern_ms * 1e-3) / 1e12
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) bf16 Q/K/V/dO from seeded numpy PCG64",
+        "config": {"workload": desc, "S": N * L, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv,
+                   "d": d, "layout": layout, "causal": causal, "q_shard": shard,
+                   "useful_tflop_per_pass": round(flops / 1e12, 4),
+                   "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "ra_step_bwd: bwd_dq_kernel + bwd_dkdv_kernel (10 h d FLOPs per "
+                               "allowed pair; the kernels execute 14 h d)",
+                     "launches": len(step_ms),
+                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline_bwd(inp, cfg, layout, causal, shard, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def run_sweep(args):
+    """Where the time goes across sizes and shards (timing only: inputs are seeded
+    torch.randn bf16 on the GPU; attention time does not depend on the values)."""
+    import torch
+
+    import ring_attention_long_amd as ra
+    from ring_attention_long_amd import accounting
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1004)
+    h, n_kv, d, N, b = 32, 8, 128, 8, 1
+
+    def inputs(L):
+        q = torch.randn((b, L, h, d), device=dev, generator=gen).to(torch.bfloat16)
+        k = torch.randn((N, b, L, n_kv, d), device=dev, generator=gen).to(torch.bfloat16)
+        v = torch.randn((N, b, L, n_kv, d), device=dev, generator=gen).to(torch.bfloat16)
+        return q, k, v
+
+    def timed(q, k, v, shard, layout, causal, copy_stream="auto", reps=3):
+        ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=causal, layout=layout), device=dev,
+                         dtype=torch.uint8)
+        for _ in range(2):
+            ra.ring_fwd(q, k, v, q_shard=shard, causal=causal, layout=layout, workspace=ws,
+                        copy_stream=copy_stream)
+        runs = [ra.ring_fwd_timed(q, k, v, q_shard=shard, causal=causal, layout=layout,
+                                  workspace=ws, copy_stream=copy_stream)[2] for _ in range(reps)]
+        return sorted(runs, key=lambda t: t["total_ms"])[reps // 2]
+
+    def summarise(tm, L, shard, layout, causal):
+        steps, copies, overlap, exposed = [], [], [], []
+        for k in range(N):
+            if tm["step_begin_ms"][k] >= 0:
+                steps.append(tm["step_end_ms"][k] - tm["step_begin_ms"][k])
+            if k >= 1 and tm["copy_begin_ms"][k] >= 0:
+                cb, ce = tm["copy_begin_ms"][k], tm["copy_end_ms"][k]
+                copies.append(ce - cb)
+                sb, se = tm["step_begin_ms"][k - 1], tm["step_end_ms"][k - 1]
+                if sb >= 0 and ce > cb:
+                    overlap.append(max(0.0, min(ce, se) - max(cb, sb)) / (ce - cb))
+                    exposed.append(max(0.0, ce - se))
+        pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+        fl = accounting.flops_from_pairs(pairs, h, d)
+        return {"pass_ms": round(tm["total_ms"], 4), "tflops": round(fl / tm["total_ms"] / 1e9, 1),
+                "live_steps": len(steps), "step_ms_mean": round(float(np.mean(steps)), 4) if steps else 0,
+                "copy_ms_mean": round(float(np.mean(copies)), 4) if copies else 0,
+                "overlap_min": round(min(overlap), 4) if overlap else None,
+                "exposed_ms_max": round(max(exposed), 4) if exposed else None}
+
+    out = {"sweep": {"h": h, "n_kv": n_kv, "d": d, "N": N, "b": b, "data": "torch.randn bf16, seed 1004"}}
+    # (1) L sweep, striped causal shard 0 and non-causal shard 0
+    rows = []
+    for L in (1024, 2048, 4096, 8192, 16384, 32768):
+        q, k, v = inputs(L)
+        kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
+        row = {"L": L, "S": N * L, "kv_bytes_per_step": kv_bytes,
+               "xgmi_ms_per_step_model": round(kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3, 4)}
+        for layout, causal, key in (("striped", True, "striped_causal"),
+                                    ("contiguous", False, "noncausal")):
+            row[key] = summarise(timed(q, k, v, 0, layout, causal), L, 0, layout, causal)
+        rows.append(row)
+        log(f"[sweep] L={L}: {row}")
+        del q, k, v
+    out["sweep"]["L_sweep"] = rows
+    for key in ("striped_causal", "noncausal"):
+        cross = [r["L"] for r in rows if r[key]["step_ms_mean"] >= r["xgmi_ms_per_step_model"]]
+        out["sweep"][f"L_star_xgmi_model_{key}"] = min(cross) if cross else None
+        hidden = [r["L"] for r in rows if r[key]["exposed_ms_max"] is not None
+                  and r[key]["exposed_ms_max"] <= 0.01 * r[key]["step_ms_mean"]]
+        out["sweep"][f"L_min_copy_hidden_on_gpu_{key}"] = min(hidden) if hidden else None
+    # (2) every shard of each causal layout at L = 32768 (load balance across devices)
+    L = 32768
+    q, k, v = inputs(L)
+    shards = {}
+    for layout in ("contiguous", "striped", "zigzag"):
+        shards[layout] = [summarise(timed(q, k, v, s, layout, True, reps=1), L, s, layout, True)
+                          for s in range(N)]
+        log(f"[sweep] shards {layout}: {[x['pass_ms'] for x in shards[layout]]}")
+    out["sweep"]["shards_L32768"] = shards
+    # (3) interference: step kernels with the copy on a side stream vs copies serialised
+    side = summarise(timed(q, k, v, 0, "striped", True), L, 0, "striped", True)
+    serial = summarise(timed(q, k, v, 0, "striped", True, copy_stream=None), L, 0, "striped", True)
+    out["sweep"]["interference_L32768_striped"] = {
+        "step_ms_mean_with_concurrent_copy": side["step_ms_mean"],
+        "step_ms_mean_copies_serialised": serial["step_ms_mean"],
+        "slowdown": round(side["step_ms_mean"] / serial["step_ms_mean"], 4)}
+    # (4) HBM-bound kernels: merge and finalize at the L = 32768 shapes, against a torch copy
+    oa = torch.randn((b, L, h, d), device=dev, generator=gen)
+    op = torch.randn((b, L, h, d), device=dev, generator=gen)
+    la = torch.randn((b, h, L), device=dev, generator=gen)
+    lp = torch.randn((b, h, L), device=dev, generator=gen)
+
+    def gbps(fn, nbytes, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+    merge_bytes = accounting.merge_bytes(b, L, h, d)
+    dst = torch.empty_like(oa)
+    out["sweep"]["hbm_GBps"] = {
+        "merge_lse": gbps(lambda: ra.merge_lse(oa, la, op, lp), merge_bytes),
+        "finalize_bf16": gbps(lambda: ra.finalize(oa), 6 * b * L * h * d),
+        "torch_copy_fp32": gbps(lambda: dst.copy_(oa), 8 * b * L * h * d),
+        "spec": 8000.0, "merge_bytes_per_call": merge_bytes}
+    out["sweep"]["peak_bf16_tflops"] = accounting.MI355X_BF16_DENSE_TFLOPS
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS))
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of one workload: L sweep of the striped causal ring pass, every "
+                         "shard of each causal layout at L=32768, copy interference, merge GB/s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -141,6 +404,10 @@ def main():
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
               "(the ring's other devices are emulated on the one GPU)", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return run_sweep(args)
+    if args.workload in BWD_WORKLOADS:
+        return run_backward(args)
 
     import torch
 

@@ -234,10 +234,10 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
 
 
 def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",
-             scale=None, stream=None, copy_stream="auto", workspace=None):
+             scale=None, stream=None, copy_stream="auto", workspace=None, out=None):
     """Backward ring pass of device q_shard.  q, o, dout [b, L, h, d] (bf16), lse [b, h, L]
     from the forward, k_all, v_all [N, b, L, n_kv, d].  Returns fp32 (dq [b, L, h, d],
-    dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d])."""
+    dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d]), written into `out` when given."""
     N, b, L, n_kv, d = k_all.shape
     h = q.shape[2]
     _need(q, "q", (b, L, h, d), q.dtype)
@@ -253,9 +253,18 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
         raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ring_bwd_workspace")
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    dq = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
-    dk = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
-    dv = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
+    if out is None:
+        dq = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
+        dk = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
+        dv = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)
+    else:
+        dq, dk, dv = out
+        _need(dq, "dq", (b, L, h, d), torch.float32)
+        _need(dk, "dk_all", (N, b, L, n_kv, d), torch.float32)
+        _need(dv, "dv_all", (N, b, L, n_kv, d), torch.float32)
+    _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    if workspace.numel() < need:
+        raise RaError(int(_lib.RA_ERR_WORKSPACE), "ra_ring_bwd")
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
     check(_lib.lib().ra_ring_bwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                  _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
