@@ -257,6 +257,7 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(StepArgs a, const __
 // during the two before).
 // ------------------------------------------------------------------------------------------
 constexpr int KV_THREADS = 512;
+
 constexpr int KB = 128;                                // keys per workgroup
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;            // Q tile, then dO tile
 constexpr int N_STAGE = 3;
@@ -403,7 +404,14 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // for it at the end of its matrix phase j-1 (interval 2j), one interval before tile j is
   // first read.  Wave 4 loads the tile's statistics with it and stores them after the wait
   // (first read in interval 2j+2).
-  auto matrix_phase = [&](int bcur, int bprev) {
+  // Matrix phase of tile j (stage BCUR; the previous tile is in stage (BCUR + 2) % 3): 16
+  // slots of two products, first dV^T += dO^T P and dK^T += Q^T dS of tile j - 1, then
+  // S = Q K^T and dP = dO V^T of tile j.  Slot x issues the LDS reads of slot x + 2, then
+  // its products; scheduling fences keep that order so the LDS latency hides behind four
+  // products.  The LDS offsets are rebuilt from three base registers each phase (keeping
+  // all of them live would not fit the 256 VGPRs of two waves per SIMD).
+  auto matrix_phase = [&](int bcur) __attribute__((always_inline)) {
+    const int bprev = bcur == 0 ? 2 : bcur - 1;
     unsigned rb = r_base, tb0 = t_base[0], tb1 = t_base[1];
     __asm__ volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));   // keep the offsets next to their reads
     auto row_op = [&](const char* blk, int kk) { return *(const bf16x8*)(blk + (rb ^ (32u * kk))); };
@@ -419,45 +427,39 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     const char* qp = smem + bprev * STAGE_BYTES + grp * 32 * ROW_BYTES;
     const char* op = qp + TILE_BYTES;
     const char* vt = smem + V_OFF + slot * 32 * ROW_BYTES;
-    // previous tile: dV^T += dO^T P, dK^T += Q^T dS (8 slots of two products)
-    bf16x8 xa[3], xb[3];
-    xa[0] = tr_op(op, 0, 0);
-    xb[0] = tr_op(qp, 0, 0);
-    xa[1] = tr_op(op, 0, 1);
-    xb[1] = tr_op(qp, 0, 1);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      if (x + 2 < 8) {
-        xa[(x + 2) % 3] = tr_op(op, (x + 2) >> 2, (x + 2) & 3);
-        xb[(x + 2) % 3] = tr_op(qp, (x + 2) >> 2, (x + 2) & 3);
+    bf16x8 ra[3], rbv[3], rv[3];
+    auto load = [&](int y) {
+      if (y < 8) {
+        ra[y % 3] = tr_op(op, y >> 2, y & 3);
+        rbv[y % 3] = tr_op(qp, y >> 2, y & 3);
+      } else {
+        ra[y % 3] = row_op(qc, y - 8);
+        rbv[y % 3] = row_op(oc, y - 8);
+        rv[y % 3] = row_op(vt, y - 8);
       }
-      dva[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[x % 3], pb[x >> 2], dva[x & 3], 0, 0, 0);
-      dka[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[x % 3], ds[x >> 2], dka[x & 3], 0, 0, 0);
-    }
-    // this tile: S = Q K^T, dP = dO V^T (8 slots of two products)
-    sc = f32x16{};
-    dp = f32x16{};
-    bf16x8 ya[3], yb[3], yv[3];
-    ya[0] = row_op(qc, 0);
-    yb[0] = row_op(oc, 0);
-    yv[0] = row_op(vt, 0);
-    ya[1] = row_op(qc, 1);
-    yb[1] = row_op(oc, 1);
-    yv[1] = row_op(vt, 1);
+    };
+    load(0);
+    load(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      if (kk + 2 < D / 16) {
-        ya[(kk + 2) % 3] = row_op(qc, kk + 2);
-        yb[(kk + 2) % 3] = row_op(oc, kk + 2);
-        yv[(kk + 2) % 3] = row_op(vt, kk + 2);
+    for (int x = 0; x < 16; ++x) {
+      if (x + 2 < 16) load(x + 2);
+      if (x < 8) {
+        dva[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], pb[x >> 2], dva[x & 3], 0, 0, 0);
+        dka[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], ds[x >> 2], dka[x & 3], 0, 0, 0);
+      } else if (x == 8) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], kop[0], f32x16{}, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], rv[x % 3], f32x16{}, 0, 0, 0);
+      } else {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], kop[x - 8], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], rv[x % 3], dp, 0, 0, 0);
       }
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya[kk % 3], kop[kk], sc, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[kk % 3], yv[kk % 3], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // accumulator layout: lane = key u, register i = row 8 (i / 4) + 4 lg + (i % 4) of the
   // wave's 32-row half
-  auto vector_phase = [&](int j, int bcur) {
+  auto vector_phase = [&](int j, int bcur) __attribute__((always_inline)) {
     const int r0 = cc.tq0 + 32 * grp;
     bool skip = j >= n_iter || r0 >= L;
     if (!skip) skip = limit(min(r0 + 31, L - 1)) <= uw;
@@ -508,10 +510,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   }
   int bcur = 0;
   for (int j = 0; j <= n_iter; ++j) {
-    const int bprev = bcur == 0 ? 2 : bcur - 1;
     const int bnext = bcur == 2 ? 0 : bcur + 1;
-    const int bnext2 = bprev;               // stage of tile j + 2
-    matrix_phase(bcur, bprev);
+    const int bnext2 = bcur == 0 ? 2 : bcur - 1;   // stage of tile j + 2 (held tile j - 1)
+    __builtin_amdgcn_s_setprio(1);          // matrix phase first in the SIMD's issue arbitration
+    matrix_phase(bcur);
+    __builtin_amdgcn_s_setprio(0);
     if (grp == 1) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads for tile j + 1 landed
       if (wave == 4 && j >= 1 && j + 1 < n_iter) {
