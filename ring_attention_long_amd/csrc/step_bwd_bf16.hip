@@ -11,7 +11,8 @@
 // Two kernels per step, each keeping one lane layout end to end:
 //  * dQ kernel (query-major, like the forward): S^T = K Q^T and dP^T = V dO^T with Q^T and
 //    dO^T resident in VGPRs; lane l holds one query's scores, so LSE and D are one value
-//    per lane; dQ^T += K^T dS^T with K^T read by the transposing LDS load.
+//    per lane; dQ^T += K^T dS^T with K^T read by the transposing LDS load.  Eight waves in
+//    the forward's ping-pong.
 //  * dK/dV kernel (key-major): each wave keeps K and V rows of 32 keys in VGPRs and walks
 //    the query tiles of every head of its KV group; S = Q K^T and dP = dO V^T put one key
 //    per lane, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and Q^T from transposing LDS
@@ -39,7 +40,6 @@ constexpr int D = 128;
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_ROWS = 64;
 constexpr int TILE_BYTES = TILE_ROWS * ROW_BYTES;   // 16 KB, 16 DMA loads of 1 KB
-constexpr int THREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -117,128 +117,6 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
     const int64_t bi = bt / L;
     delta[(bi * h + hq) * L + t] = s;
   }
-}
-
-// ------------------------------------------------------------------------------------------
-// dQ kernel: workgroup = 4 waves x 32 query rows (heads of one KV group first), 64-key tiles.
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(StepArgs a, const __bf16* __restrict__ dout,
-                                                            const float* __restrict__ lse,
-                                                            const float* __restrict__ delta,
-                                                            float* __restrict__ dq, int heads_per_wg,
-                                                            int n_qb, int inner_count) {
-  __shared__ __attribute__((aligned(1024))) char k_lds[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_lds[2][TILE_BYTES];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lq = lane & 31, lg = lane >> 5;
-  const int L = a.L;
-  const int G = a.h / a.n_kv;
-  const int Hw = heads_per_wg, PB = 4 / Hw;
-  const int inner = blockIdx.x % inner_count;
-  const int qb = n_qb - 1 - blockIdx.x / inner_count;
-  const int g = inner % a.n_kv;
-  const int bi = (inner / a.n_kv) % a.b;
-  const int hs = inner / (a.n_kv * a.b);
-  const int hq = g * G + hs * Hw + (wave % Hw);
-  const int t0_wg = qb * 32 * PB;
-  const int t0 = t0_wg + (wave / Hw) * 32;
-  const int t = t0 + lq;
-  const int tc = min(t, L - 1);
-
-  const int lim = t < L ? kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t) : 0;
-  int wave_tiles = 0, wave_full = 0, n_tiles = 0;
-  if (t0 < L) {
-    wave_tiles = (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, min(t0 + 31, L - 1)) + 63) / 64;
-    wave_full = kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t0) / 64;
-  }
-  if (t0_wg < L)
-    n_tiles = (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, min(t0_wg + 32 * PB - 1, L - 1)) + 63) / 64;
-  wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
-  wave_full = __builtin_amdgcn_readfirstlane(wave_full);
-  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-
-  // resident operands: Q^T and dO^T of this lane's query, one row per lane
-  const int64_t qrow = (((int64_t)bi * L + tc) * a.h + hq) * D + lg * 8;
-  bf16x8 qop[D / 16], dop[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    qop[kk] = *(const bf16x8*)((const __bf16*)a.q + qrow + kk * 16);
-    dop[kk] = *(const bf16x8*)(dout + qrow + kk * 16);
-  }
-  const float lse_t = lse[((int64_t)bi * a.h + hq) * L + tc];
-  const float neg_lse2 = lse_t > -INFINITY ? -lse_t * LOG2E : -INFINITY;   // empty row: P = 0
-  const float dlt = delta[((int64_t)bi * a.h + hq) * L + tc];
-  const float c2 = a.scale * LOG2E;
-
-  const unsigned row_stride = (unsigned)a.n_kv * D * 2;
-  const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
-  const dma_rsrc k_rsrc = rows_rsrc((const __bf16*)a.k + kv_base, L, row_stride);
-  const dma_rsrc v_rsrc = rows_rsrc((const __bf16*)a.v + kv_base, L, row_stride);
-  const unsigned lane_off = dma_lane_offset(row_stride, lane, wave);
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e) acc[e] = f32x16{};
-
-  if (n_tiles > 0) {
-    dma_tile(k_rsrc, k_lds[0], lane_off, 0, row_stride, wave);
-    dma_tile(v_rsrc, v_lds[0], lane_off, 0, row_stride, wave);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) {
-      dma_tile(k_rsrc, k_lds[buf ^ 1], lane_off, (unsigned)((j + 1) * 64) * row_stride, row_stride, wave);
-      dma_tile(v_rsrc, v_lds[buf ^ 1], lane_off, (unsigned)((j + 1) * 64) * row_stride, row_stride, wave);
-    }
-    if (j < wave_tiles) {
-      const char* kt = k_lds[buf];
-      const char* vt = v_lds[buf];
-      f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk(kt, 32 * jj + lq, 2 * kk + lg),
-                                                           qop[kk], sc[jj], 0, 0, 0);
-          dp[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk(vt, 32 * jj + lq, 2 * kk + lg),
-                                                           dop[kk], dp[jj], 0, 0, 0);
-        }
-      const bool masked = j >= wave_full;
-      bf16x8 ds[4];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * 64 + 32 * jj + 8 * (i >> 2) + 4 * lg + (i & 3);
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][i], c2, neg_lse2));
-          if (masked && key >= lim) p = 0.f;
-          const float v = p * (dp[jj][i] - dlt);
-          ds[2 * jj + (i >> 3)][i & 7] = (__bf16)v;
-        }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e)
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_transposed(kt, lane, c, e), ds[c], acc[e], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-  if (t >= L) return;
-  float* row = dq + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      f32x4* p = (f32x4*)(row + 32 * e + 8 * ib);
-      f32x4 v = *p;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) v[x] += a.scale * acc[e][4 * ib + x];
-      *p = v;
-    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -579,6 +457,233 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// dQ kernel: workgroup = 8 waves x 32 query rows (query heads of one KV group first, as in the
+// forward), walking the 64-key tiles of the KV shard.
+//
+// Wave w holds Q^T and dO^T of its 32 rows in VGPRs; per key tile it computes
+// S^T = K Q^T and dP^T = V dO^T (lane = query, so LSE and D are one value per lane),
+// dS = P * (dP - D) with P = exp2(S c2 - LSE log2 e), and dQ^T += K^T dS^T (K^T from the
+// transposing LDS read).  Ping-pong as in the forward: matrix phase j = dQ of tile j-1
+// (16 products) and S, dP of tile j (32 products); vector phase j = dS of tile j.  K tiles
+// rotate through four LDS stages (read in matrix phases j and j+1), V tiles through three.
+// In its vector phase j group 0 loads V(j+2) and group 1 loads K(j+3), four loads per
+// wave, and each wave waits for them at the end of its next vector phase.
+// ------------------------------------------------------------------------------------------
+constexpr int DQ_THREADS = 512;
+constexpr int K_STAGES = 4;
+constexpr int V_STAGES = 3;
+
+__global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const __bf16* __restrict__ dout,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ delta,
+                                                               float* __restrict__ dq, int heads_per_wg,
+                                                               int n_qb, int inner_count) {
+  __shared__ __attribute__((aligned(1024))) char k_lds[K_STAGES][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds[V_STAGES][TILE_BYTES];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63, lq = lane & 31, lg = lane >> 5;
+  const int L = a.L;
+  const int G = a.h / a.n_kv;
+  const int Hw = heads_per_wg, PB = 8 / Hw;
+  const int inner = blockIdx.x % inner_count;
+  const int qb = n_qb - 1 - blockIdx.x / inner_count;   // heaviest query block first
+  const int g = inner % a.n_kv;
+  const int bi = (inner / a.n_kv) % a.b;
+  const int hs = inner / (a.n_kv * a.b);
+  const int hq = g * G + hs * Hw + (wave % Hw);
+  const int t0_wg = qb * 32 * PB;
+  const int t0 = t0_wg + (wave / Hw) * 32;
+  const int t = t0 + lq;
+  const int tc = min(t, L - 1);
+  auto limit = [&](int row) { return kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row); };
+
+  const int lim = t < L ? limit(t) : 0;
+  int wave_tiles = 0, wave_full = 0, n_tiles = 0;
+  if (t0 < L) {
+    wave_tiles = (limit(min(t0 + 31, L - 1)) + 63) / 64;
+    wave_full = limit(t0) / 64;
+  }
+  if (t0_wg < L) n_tiles = (limit(min(t0_wg + 32 * PB - 1, L - 1)) + 63) / 64;
+  wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
+  wave_full = __builtin_amdgcn_readfirstlane(wave_full);
+  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  if (n_tiles == 0) return;   // uniform over the workgroup: no key of this step is allowed
+
+  // resident operands: Q^T and dO^T of this lane's query, one row per lane
+  const int64_t qrow = (((int64_t)bi * L + tc) * a.h + hq) * D + lg * 8;
+  bf16x8 qop[D / 16], dop[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qop[kk] = *(const bf16x8*)((const __bf16*)a.q + qrow + kk * 16);
+    dop[kk] = *(const bf16x8*)(dout + qrow + kk * 16);
+  }
+  const float lse_t = lse[((int64_t)bi * a.h + hq) * L + tc];
+  const float neg_lse2 = lse_t > -INFINITY ? -lse_t * LOG2E : -INFINITY;   // empty row: P = 0
+  const float dlt = delta[((int64_t)bi * a.h + hq) * L + tc];
+  const float c2 = a.scale * LOG2E;
+
+  const unsigned row_stride = (unsigned)a.n_kv * D * 2;
+  const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
+  const dma_rsrc k_rsrc = rows_rsrc((const __bf16*)a.k + kv_base, L, row_stride);
+  const dma_rsrc v_rsrc = rows_rsrc((const __bf16*)a.v + kv_base, L, row_stride);
+  const unsigned lane_off = dma_lane_offset(row_stride, lane, wave & 3);
+  // tile `tile` of K or V into an LDS stage (this wave's four loads); tiles past the last
+  // point beyond the buffer: zeros, no memory traffic, into a stage nobody reads again
+  auto tile_dma = [&](const dma_rsrc& r, char* dst, int tile) {
+    dma_tile(r, dst, lane_off, tile < n_tiles ? (unsigned)(tile * 64) * row_stride : 0x80000000u,
+             row_stride, wave & 3);
+  };
+
+  // LDS read offsets (see the dK/dV kernel): row reads at r_base ^ 32 kk (+ 32 rows per
+  // jj), transposing reads at t_base[h] ^ 64 e (+ 16 rows per c)
+  const unsigned r_base = (unsigned)lq * ROW_BYTES + (unsigned)((lg ^ swz(lq)) * 16);
+  const int g16 = lane >> 4, j16 = lane & 15, jq = j16 >> 2;
+  const int low = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  unsigned t_base[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    t_base[h] = (unsigned)(8 * h + 4 * lg + jq) * ROW_BYTES +
+                (unsigned)((4 * jq + (low ^ ((2 * h + lg) & 3))) * 16) + (unsigned)((j16 & 1) * 8);
+
+  f32x16 acc[D / 32], sc[2], dp[2];
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) acc[e] = f32x16{};
+  bf16x8 ds[4] = {bf16x8{}, bf16x8{}, bf16x8{}, bf16x8{}};
+
+  // Matrix phase j: dQ^T += K(j-1)^T dS(j-1)^T (8 slots), then S^T(j) and dP^T(j) (16 slots);
+  // slot x issues the reads of slot x + 2, then its two products (scheduling fences).
+  auto matrix_phase = [&](int ks, int kp, int vs) __attribute__((always_inline)) {
+    unsigned rb = r_base, tb0 = t_base[0], tb1 = t_base[1];
+    __asm__ volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));   // keep the offsets next to their reads
+    const char* kc = k_lds[ks];
+    const char* kprev = k_lds[kp];
+    const char* vc = v_lds[vs];
+    auto row_op = [&](const char* blk, int jj, int kk) {
+      return *(const bf16x8*)(blk + jj * 32 * ROW_BYTES + (rb ^ (32u * kk)));
+    };
+    auto tr_op = [&](const char* blk, int c, int e) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(blk + c * 16 * ROW_BYTES + (tb0 ^ (64u * e))));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(blk + c * 16 * ROW_BYTES + (tb1 ^ (64u * e))));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 r0[3], r1[3];
+    auto load = [&](int y) {
+      if (y < 8) {                      // dQ slot: c = y / 2, d-tiles e = 2 (y % 2) + {0, 1}
+        r0[y % 3] = tr_op(kprev, y >> 1, 2 * (y & 1));
+        r1[y % 3] = tr_op(kprev, y >> 1, 2 * (y & 1) + 1);
+      } else {                          // S/dP slot: kk = (y - 8) / 2, jj = (y - 8) % 2
+        r0[y % 3] = row_op(kc, (y - 8) & 1, (y - 8) >> 1);
+        r1[y % 3] = row_op(vc, (y - 8) & 1, (y - 8) >> 1);
+      }
+    };
+    load(0);
+    load(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < 24; ++x) {
+      if (x + 2 < 24) load(x + 2);
+      if (x < 8) {
+        const int c = x >> 1, e = 2 * (x & 1);
+        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[x % 3], ds[c], acc[e], 0, 0, 0);
+        acc[e + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[x % 3], ds[c], acc[e + 1], 0, 0, 0);
+      } else {
+        const int kk = (x - 8) >> 1, jj = (x - 8) & 1;
+        sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[x % 3], qop[kk], kk == 0 ? f32x16{} : sc[jj], 0, 0, 0);
+        dp[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[x % 3], dop[kk], kk == 0 ? f32x16{} : dp[jj], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Vector phase j: this wave's loads, then dS of tile j (zero where the wave has no tile).
+  // Accumulator layout: lane = query, register i of block jj = key
+  // 64 j + 32 jj + 8 (i / 4) + 4 lg + (i % 4).
+  auto vector_phase = [&](int j, int vs2, int ks3) __attribute__((always_inline)) {
+    if (grp == 0) tile_dma(v_rsrc, v_lds[vs2], j + 2);
+    else tile_dma(k_rsrc, k_lds[ks3], j + 3);
+    if (j >= wave_tiles) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ds[c] = bf16x8{};
+      return;
+    }
+    if (j >= wave_full) {
+      // keep this a real (scalar) branch: only diagonal and ragged tiles pay for the mask
+      __asm__ volatile("" ::: "memory");
+      const int thr = lim - (j * 64 + 4 * lg);       // first masked key offset of this row
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * jj + 8 * (i >> 2) + (i & 3) >= thr) sc[jj][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][i], c2, neg_lse2));
+        ds[2 * jj + (i >> 3)][i & 7] = (__bf16)(p * (dp[jj][i] - dlt));
+      }
+  };
+
+  // ---- prologue: K(0), K(1), V(0), V(1) in place, K(2) in flight ----------------------------
+  {
+    u32x4* z = (u32x4*)k_lds[K_STAGES - 1];   // K(-1): read (with dS = 0) by matrix phase 0
+    for (int i = tid; i < TILE_BYTES / 16; i += DQ_THREADS) z[i] = u32x4{};
+  }
+  if (grp == 1) {
+    tile_dma(k_rsrc, k_lds[0], 0);
+    tile_dma(k_rsrc, k_lds[1], 1);
+  } else {
+    tile_dma(v_rsrc, v_lds[0], 0);
+    tile_dma(v_rsrc, v_lds[1], 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  // Intervals between barriers: 2j+1 holds group 0's matrix phase j and group 1's vector
+  // phase j-1; 2j+2 group 0's vector phase j and group 1's matrix phase j.  K(j) is read in
+  // intervals 2j+1 .. 2j+4, V(j) in 2j+1, 2j+2.  Group 0 loads V(j+2) in interval 2j+2 into
+  // the stage of V(j-1) and has it by the end of 2j+4; group 1 loads K(j+3) in 2j+3 into the
+  // stage of K(j-1) and has it by the end of 2j+5.
+  if (grp == 1) {
+    tile_dma(k_rsrc, k_lds[2], 2);
+    barrier_no_fence();
+  }
+  int ks = 0, vs = 0;
+  for (int j = 0; j <= n_tiles; ++j) {
+    const int kp = ks == 0 ? K_STAGES - 1 : ks - 1;
+    const int ks3 = kp;                               // stage of K(j+3) (held K(j-1))
+    const int vs2 = vs == 0 ? V_STAGES - 1 : vs - 1;  // stage of V(j+2) (held V(j-1))
+    __builtin_amdgcn_s_setprio(1);        // matrix phase first in the SIMD's issue arbitration
+    matrix_phase(ks, kp, vs);
+    __builtin_amdgcn_s_setprio(0);
+    barrier_no_fence();
+    vector_phase(j, vs2, ks3);
+    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): this wave's loads of its previous vector phase landed
+    ks = ks == K_STAGES - 1 ? 0 : ks + 1;
+    vs = vs == V_STAGES - 1 ? 0 : vs + 1;
+    barrier_no_fence();
+  }
+  if (grp == 0) barrier_no_fence();
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): no load into LDS outlives the loop
+
+  if (t >= L) return;
+  float* row = dq + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4* p = (f32x4*)(row + 32 * e + 8 * ib);
+      f32x4 v = *p;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) v[x] += a.scale * acc[e][4 * ib + x];
+      *p = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
@@ -594,14 +699,14 @@ hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float
                                 const float* delta, float* dq, float* dk, float* dv, hipStream_t s) {
   const int G = a.h / a.n_kv;
   const int Hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
-  const int PB = 4 / Hw;
+  const int PB = 8 / Hw;
   const int n_qb = (a.L + 32 * PB - 1) / (32 * PB);
   const int inner = a.n_kv * a.b * (G / Hw);
   const int64_t grid_q = (int64_t)n_qb * inner;
   const int n_kb = (a.L + KB - 1) / KB;
   const int64_t grid_k = (int64_t)n_kb * a.n_kv * a.b;
   if (grid_q > 0x7fffffff || grid_k > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid_q), dim3(THREADS), 0, s, a,
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid_q), dim3(DQ_THREADS), 0, s, a,
                      (const __bf16*)dout, lse, delta, dq, Hw, n_qb, inner);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
