@@ -4,8 +4,8 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import 
 package.  The product path never does.
 """
 from .ring_oracle import (  # noqa: F401
-    LAYOUTS, allowed_pairs, attend, attention_over_shards, brute_force_row, merge,
-    online_blocks, positions, ring_order, shard_attention, shard_dq_rows, shard_grads,
+    LAYOUTS, allowed_mask, allowed_pairs, attend, attention_over_shards, brute_force_row, merge,
+    document_of, online_blocks, positions, ring_order, shard_attention, shard_dq_rows, shard_grads,
     shard_tokens,
     step_attention,
 )

@@ -26,6 +26,8 @@ Readings taken where the pages are silent or garbled (each also listed in DESIGN
   * a query row with no allowed key gives O = 0 and LSE = -inf (no NaN); merging such a
     partial is the identity.
   * zigzag: 2N chunks of L/2 tokens; shard p holds chunk p followed by chunk 2N-1-p.
+  * packed documents: a key is allowed only in the query's own document, on top of the
+    causal rule; documents are given by their global start positions.
 
 Pins (tests/test_oracle_pins.py, tests/test_layout_pins.py, tests/test_grads_pins.py):
 every public function below has at least one pin that does not retype its own formula:
@@ -111,18 +113,39 @@ def _default_scale(d: int, scale: float | None) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def attend(q_rows, pos_q, keys, vals, pos_k, *, causal: bool, scale: float):
+# --------------------------------------------------------------------------------------
+# Packed documents (page 3, section 5: several documents packed end to end into one window,
+# with a block-diagonal mask that stops attention across documents).  `docs` lists the
+# documents' global start positions followed by the window length: [0, b_1, ..., S].
+# --------------------------------------------------------------------------------------
+def document_of(pos, docs) -> np.ndarray:
+    """Index of the document holding each global position."""
+    return np.searchsorted(np.asarray(docs), np.asarray(pos), side="right") - 1
+
+
+def allowed_mask(pos_q, pos_k, *, causal: bool, docs=None) -> np.ndarray:
+    """[R, C] boolean: may query at pos_q[r] attend key at pos_k[c]?  Causal keeps keys at
+    or before the query (inclusive); packed documents keep keys of the query's document."""
+    pos_q = np.asarray(pos_q)
+    pos_k = np.asarray(pos_k)
+    if causal:
+        m = pos_k[None, :] <= pos_q[:, None]
+    else:
+        m = np.ones((pos_q.size, pos_k.size), dtype=bool)
+    if docs is not None:
+        m &= document_of(pos_q, docs)[:, None] == document_of(pos_k, docs)[None, :]
+    return m
+
+
+def attend(q_rows, pos_q, keys, vals, pos_k, *, causal: bool, scale: float, docs=None):
     """softmax(q K^T * scale) V over an explicit key set, for one head.
 
     q_rows [R, d], keys [C, d], vals [C, dv], pos_q [R], pos_k [C]  ->  (O [R, dv], LSE [R]).
-    A key is allowed for a query iff not causal or pos_k <= pos_q (inclusive).
-    Rows with no allowed key return O = 0, LSE = -inf.
+    A key is allowed for a query iff allowed_mask says so (causal: pos_k <= pos_q,
+    inclusive; packed: same document).  Rows with no allowed key return O = 0, LSE = -inf.
     """
     s = (q_rows @ keys.T) * scale                                   # [R, C]
-    if causal:
-        allowed = pos_k[None, :] <= pos_q[:, None]
-    else:
-        allowed = np.ones(s.shape, dtype=bool)
+    allowed = allowed_mask(pos_q, pos_k, causal=causal, docs=docs)
     s = np.where(allowed, s, -np.inf)
     any_allowed = allowed.any(axis=1)
     m = np.where(any_allowed, s.max(axis=1, initial=-np.inf), 0.0)
@@ -139,7 +162,8 @@ def _gqa_group(h: int, n_kv: int) -> int:
     return h // n_kv
 
 
-def attention_over_shards(q, k_sel, v_sel, pos_q, pos_k, *, causal, scale=None, rows=None):
+def attention_over_shards(q, k_sel, v_sel, pos_q, pos_k, *, causal, scale=None, rows=None,
+                          docs=None):
     """Attention of q [b, L, h, d] against an explicit concatenated key set.
 
     k_sel, v_sel [b, C, n_kv, d] with global positions pos_k [C]; pos_q [L].
@@ -157,12 +181,12 @@ def attention_over_shards(q, k_sel, v_sel, pos_q, pos_k, *, causal, scale=None, 
             g = hq // group
             O[bi, :, hq, :], LSE[bi, hq, :] = attend(
                 q[bi, rows, hq, :], pos_q[rows], k_sel[bi, :, g, :], v_sel[bi, :, g, :],
-                pos_k, causal=causal, scale=sc)
+                pos_k, causal=causal, scale=sc, docs=docs)
     return O, LSE
 
 
 def shard_attention(q, k_all, v_all, *, N, shard, layout="contiguous", causal=False,
-                    scale=None, rows=None):
+                    scale=None, rows=None, docs=None):
     """What device `shard` must output after the whole ring pass: its queries attended to
     every key of the sequence (all N shards at once), with the causal mask by global
     position.  This is the quantity Ring Attention computes exactly."""
@@ -174,17 +198,17 @@ def shard_attention(q, k_all, v_all, *, N, shard, layout="contiguous", causal=Fa
     v_cat = np.concatenate([v_all[j] for j in range(N)], axis=1)
     pos_k = np.concatenate(toks)
     return attention_over_shards(q, k_cat, v_cat, toks[shard], pos_k, causal=causal,
-                                 scale=scale, rows=rows)
+                                 scale=scale, rows=rows, docs=docs)
 
 
 def step_attention(q, k, v, *, N, q_shard, kv_shard, layout="contiguous", causal=False,
-                   scale=None, rows=None):
+                   scale=None, rows=None, docs=None):
     """One ring step: device q_shard's queries against the single KV shard kv_shard
     (k, v [b, L, n_kv, d]).  Rows with no allowed key in this shard give (0, -inf)."""
     L = q.shape[1]
     toks = shard_tokens(layout, N, L)
     return attention_over_shards(q, k, v, toks[q_shard], toks[kv_shard], causal=causal,
-                                 scale=scale, rows=rows)
+                                 scale=scale, rows=rows, docs=docs)
 
 
 # --------------------------------------------------------------------------------------
@@ -257,7 +281,7 @@ def online_blocks(q_rows, pos_q, blocks, *, causal, scale):
 # the gradients themselves are the textbook softmax-attention gradients, no autograd.
 # --------------------------------------------------------------------------------------
 def shard_grads(q, k_all, v_all, dout, *, N, shard, layout="contiguous", causal=False,
-                scale=None):
+                scale=None, docs=None):
     """Gradients of sum(dout * O_shard) with respect to the shard's Q and every shard's
     K, V, where O_shard is shard_attention(...) of device `shard`.
 
@@ -288,7 +312,7 @@ def shard_grads(q, k_all, v_all, dout, *, N, shard, layout="contiguous", causal=
             g = hq // group
             Qh, Kh, Vh, dOh = q[bi, :, hq], k_cat[bi, :, g], v_cat[bi, :, g], dout[bi, :, hq]
             s = (Qh @ Kh.T) * sc
-            allowed = (pos_k[None, :] <= pos_q[:, None]) if causal else np.ones(s.shape, bool)
+            allowed = allowed_mask(pos_q, pos_k, causal=causal, docs=docs)
             s = np.where(allowed, s, -np.inf)
             m = s.max(axis=1, initial=-np.inf)
             m = np.where(np.isfinite(m), m, 0.0)
@@ -309,7 +333,7 @@ def shard_grads(q, k_all, v_all, dout, *, N, shard, layout="contiguous", causal=
 
 
 def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous", causal=False,
-                  scale=None):
+                  scale=None, docs=None):
     """dQ of selected query rows only (same definition as shard_grads, evaluated for the
     given rows; a row's dQ needs only its own P, O and D).  Returns dq [b, R, h, d]."""
     Nk, b, L, n_kv, d = k_all.shape
@@ -328,7 +352,7 @@ def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous",
             g = hq // group
             Qh, Kh, Vh, dOh = q[bi, rows, hq], k_cat[bi, :, g], v_cat[bi, :, g], dout[bi, rows, hq]
             s = (Qh @ Kh.T) * sc
-            allowed = (pos_k[None, :] <= pos_q[:, None]) if causal else np.ones(s.shape, bool)
+            allowed = allowed_mask(pos_q, pos_k, causal=causal, docs=docs)
             s = np.where(allowed, s, -np.inf)
             m = s.max(axis=1, initial=-np.inf)
             m = np.where(np.isfinite(m), m, 0.0)
@@ -348,12 +372,14 @@ def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous",
 # query-key pairs; page 3, section 2: total FLOPs 4 b S^2 h d non-causal)
 # --------------------------------------------------------------------------------------
 def allowed_pairs(layout: str, N: int, L: int, q_shard: int, kv_shard: int | None = None,
-                  causal: bool = True) -> int:
+                  causal: bool = True, docs=None) -> int:
     """Number of (query, key) pairs device q_shard may attend to, against one KV shard or
     (kv_shard=None) the whole sequence.  Counted from the explicit positions."""
     toks = shard_tokens(layout, N, L)
     pos_q = toks[q_shard]
     pos_k = np.sort(np.concatenate(toks) if kv_shard is None else toks[kv_shard])
+    if docs is not None:
+        return int(allowed_mask(pos_q, pos_k, causal=causal, docs=docs).sum())
     if not causal:
         return int(pos_q.size * pos_k.size)
     return int(np.searchsorted(pos_k, pos_q, side="right").sum())

@@ -56,3 +56,19 @@ def shard_inputs(*, b, L, h, n_kv, d, N, q_shard, seed, dtype="bf16", with_dout=
     if with_dout:
         out["dout"] = normal((b, L, h, d), seed=seed, name="do", shard=q_shard, dtype=dtype)
     return out
+
+
+def document_bounds(S: int, *, seed: int, mean_len: float, min_len: int = 1,
+                    max_len: int | None = None) -> np.ndarray:
+    """Packed-window document boundaries [0, b_1, ..., S] (int64): lengths drawn from a
+    seeded lognormal with the given mean (sigma 1, a heavy-tailed mix of short and long
+    documents), clipped to [min_len, max_len], the last document cut at the window end."""
+    rng = np.random.default_rng([seed, 7])
+    hi = S if max_len is None else max_len
+    sigma = 1.0
+    mu = np.log(max(mean_len, 1.0)) - sigma * sigma / 2
+    bounds = [0]
+    while bounds[-1] < S:
+        n = int(np.clip(round(rng.lognormal(mu, sigma)), min_len, hi))
+        bounds.append(min(S, bounds[-1] + n))
+    return np.asarray(bounds, dtype=np.int64)
