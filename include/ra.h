@@ -70,6 +70,17 @@ typedef struct ra_problem {
   int32_t layout; /* RA_LAYOUT_*; only matters when causal = 1                      */
   int32_t dtype;  /* RA_F32 or RA_BF16                                             */
   float scale;    /* softmax scale on q.k; <= 0 selects 1/sqrt(d)                   */
+  /* Packed documents (page 3, section 5: documents packed end to end into one window, a
+   * block-diagonal mask stopping attention across them).  Both NULL: one sequence.
+   * Otherwise DEVICE arrays [b][L] of int32 giving, for every query row of the shard the
+   * call computes, the global position of its document's first token (doc_begin) and one
+   * past its last (doc_end); the row attends only to keys at positions in
+   * [doc_begin, doc_end), and only to those at or before its own position when causal.
+   * Both must be nondecreasing along the shard's rows, as they are for packed documents
+   * (ra_document_ranges builds them).  They are read on the device and not validated: bad
+   * values give wrong masks, never out-of-bounds accesses.  Both or neither. */
+  const int32_t* doc_begin;
+  const int32_t* doc_end;
 } ra_problem;
 
 typedef void* ra_stream; /* a hipStream_t */
@@ -189,6 +200,20 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t q_shard, const void* q, const
  * FLOPs of the forward are 4 * d * h * pairs (page 3, section 2: two GEMMs, 2 FLOPs per
  * multiply-add).  Returns -1 on invalid arguments. */
 int64_t ra_allowed_pairs(const ra_problem* p, int32_t q_shard, int32_t kv_shard);
+
+/* Host-only: allowed pairs as ra_allowed_pairs, with the packed-document bounds given as
+ * HOST arrays [b][L] (same meaning as p->doc_begin / p->doc_end, which are ignored).
+ * Returns -1 on invalid arguments. */
+int64_t ra_allowed_pairs_packed(const ra_problem* p, int32_t q_shard, int32_t kv_shard,
+                                const int32_t* doc_begin_host, const int32_t* doc_end_host);
+
+/* Host-only: the per-row document bounds of shard `shard` for one batch row, from the
+ * documents' global start positions bounds[0..n_docs] (bounds[0] = 0, strictly
+ * increasing, bounds[n_docs] = S = N * L; all host memory).  Writes begin_out[t] and
+ * end_out[t] (host arrays of L int32) for every local row t of the shard under p->layout.
+ * RA_ERR_INVALID_ARG if the bounds are not of that form. */
+ra_status ra_document_ranges(const ra_problem* p, int32_t shard, const int32_t* bounds,
+                             int32_t n_docs, int32_t* begin_out, int32_t* end_out);
 
 /* Static text for a status code, and the detail of the calling thread's last error. */
 const char* ra_status_string(ra_status s);

@@ -41,13 +41,50 @@ def library_path() -> str:
 
 
 def make_problem(*, b, L, h, n_kv, d, N, causal=False, layout="contiguous",
-                 dtype=torch.bfloat16, scale=None) -> RaProblem:
+                 dtype=torch.bfloat16, scale=None, docs=None) -> RaProblem:
+    """The C-ABI problem descriptor.  docs: None, or (doc_begin, doc_end), int32 GPU tensors
+    [b, L] holding each query row's packed-document bounds (see document_ranges)."""
     if layout not in RA_LAYOUT:
         raise ValueError(f"layout must be one of {sorted(RA_LAYOUT)}")
     if dtype not in _DTYPES:
         raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
+    db = de = None
+    if docs is not None:
+        begin, end = docs
+        _need(begin, "doc_begin", (b, L), torch.int32)
+        _need(end, "doc_end", (b, L), torch.int32)
+        db, de = begin.data_ptr(), end.data_ptr()
     return RaProblem(b, L, h, n_kv, d, N, int(bool(causal)), RA_LAYOUT[layout], _DTYPES[dtype],
-                     0.0 if scale is None else float(scale))
+                     0.0 if scale is None else float(scale), db, de)
+
+
+def document_ranges(bounds, *, N, L, shard, layout="contiguous"):
+    """Host-side: per-row packed-document bounds of shard `shard` (numpy int32 arrays [L],
+    begin and end), from the documents' global start positions bounds = [0, ..., N * L]."""
+    import numpy as np
+    bounds = np.ascontiguousarray(bounds, dtype=np.int32)
+    begin = np.empty(L, dtype=np.int32)
+    end = np.empty(L, dtype=np.int32)
+    p = make_problem(b=1, L=L, h=1, n_kv=1, d=128, N=N, layout=layout)
+    check(_lib.lib().ra_document_ranges(ctypes.byref(p), shard, bounds.ctypes.data,
+                                        bounds.size - 1, begin.ctypes.data, end.ctypes.data),
+          "ra_document_ranges")
+    return begin, end
+
+
+def allowed_pairs_packed(doc_begin, doc_end, *, N, q_shard, kv_shard=-1, causal=True,
+                         layout="contiguous") -> int:
+    """Host-only pair count with packed documents; doc_begin, doc_end numpy int32 [b, L]."""
+    import numpy as np
+    db = np.ascontiguousarray(doc_begin, dtype=np.int32)
+    de = np.ascontiguousarray(doc_end, dtype=np.int32)
+    b, L = db.shape
+    p = make_problem(b=b, L=L, h=1, n_kv=1, d=128, N=N, causal=causal, layout=layout)
+    n = int(_lib.lib().ra_allowed_pairs_packed(ctypes.byref(p), q_shard, kv_shard, db.ctypes.data,
+                                               de.ctypes.data))
+    if n < 0:
+        raise ValueError("invalid arguments to allowed_pairs_packed")
+    return n
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
@@ -80,7 +117,7 @@ def _shapes_from_q(q, kv):
 
 
 def step_fwd(q, k, v, *, N, q_shard, kv_shard, causal=False, layout="contiguous", scale=None,
-             stream=None):
+             stream=None, docs=None):
     """One ring step: shard q_shard's queries q [b, L, h, d] against the keys/values of shard
     kv_shard (k, v [b, L, n_kv, d]).  Returns the normalised partial (o_part [b, L, h, d]
     fp32, lse_part [b, h, L] fp32); rows with no allowed key get (0, -inf)."""
@@ -89,7 +126,7 @@ def step_fwd(q, k, v, *, N, q_shard, kv_shard, causal=False, layout="contiguous"
     _need(k, "k", (b, L, n_kv, d), q.dtype)
     _need(v, "v", (b, L, n_kv, d), q.dtype)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale)
+                     dtype=q.dtype, scale=scale, docs=docs)
     o = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
     lse = torch.empty((b, h, L), device=q.device, dtype=torch.float32)
     check(_lib.lib().ra_step_fwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
@@ -138,14 +175,14 @@ def ring_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=N
     return int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
 
 
-def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out):
+def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, docs=None):
     N, b, L, n_kv, d = k_all.shape
     h = q.shape[2]
     _need(q, "q", (b, L, h, d), q.dtype)
     _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
     _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale)
+                     dtype=q.dtype, scale=scale, docs=docs)
     need = int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
     if need == 0:
         raise RaError(int(_lib.RA_ERR_INVALID_ARG), "ra_ring_fwd_workspace")
@@ -160,12 +197,13 @@ def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out):
 
 
 def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
-             stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None):
+             stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, docs=None):
     """Forward ring pass of device q_shard: q [b, L, h, d] against all N KV shards
     k_all, v_all [N, b, L, n_kv, d] in ring order.  Returns (o [b, L, h, d] in q's dtype,
     lse [b, h, L] fp32).  copy_stream="auto" stages KV on a side stream; None stages on
     the compute stream."""
-    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
+                                docs)
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
     check(_lib.lib().ra_ring_fwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream),
@@ -175,9 +213,11 @@ def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", sca
 
 
 def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
-                   stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None):
+                   stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None,
+                   docs=None):
     """ring_fwd plus timings (ms from entry): returns (o, lse, dict).  Synchronises."""
-    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
+                                docs)
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
     tm = RaRingTiming()
     check(_lib.lib().ra_ring_fwd_timed(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all),
@@ -208,7 +248,7 @@ def bwd_preprocess(o, dout, *, stream=None):
 
 def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
              layout="contiguous", scale=None, dq_acc=None, dk_acc=None, dv_acc=None,
-             stream=None):
+             stream=None, docs=None):
     """One backward ring step: adds this (query shard, KV shard) pair's contributions to
     dq_acc [b, L, h, d] and dk_acc, dv_acc [b, L, n_kv, d] (fp32; zeros when not given).
     Returns (dq_acc, dk_acc, dv_acc)."""
@@ -226,7 +266,7 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
     _need(dk_acc, "dk_acc", (b, L, n_kv, d), torch.float32)
     _need(dv_acc, "dv_acc", (b, L, n_kv, d), torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale)
+                     dtype=q.dtype, scale=scale, docs=docs)
     check(_lib.lib().ra_step_bwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
                                  _ptr(dv_acc), _stream(stream)), "ra_step_bwd")
@@ -234,7 +274,7 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
 
 
 def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",
-             scale=None, stream=None, copy_stream="auto", workspace=None, out=None):
+             scale=None, stream=None, copy_stream="auto", workspace=None, out=None, docs=None):
     """Backward ring pass of device q_shard.  q, o, dout [b, L, h, d] (bf16), lse [b, h, L]
     from the forward, k_all, v_all [N, b, L, n_kv, d].  Returns fp32 (dq [b, L, h, d],
     dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d]), written into `out` when given."""
@@ -247,7 +287,7 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
     _need(dout, "dout", (b, L, h, d), q.dtype)
     _need(lse, "lse", (b, h, L), torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale)
+                     dtype=q.dtype, scale=scale, docs=docs)
     need = int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p)))
     if need == 0:
         raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ring_bwd_workspace")

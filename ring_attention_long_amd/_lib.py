@@ -26,6 +26,7 @@ class RaProblem(ctypes.Structure):
         ("n_kv", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("layout", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("doc_begin", ctypes.c_void_p), ("doc_end", ctypes.c_void_p),
     ]
 
 
@@ -58,6 +59,8 @@ SIGNATURES = [
     ("ra_ring_bwd_workspace", _S, [_P]),
     ("ra_ring_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_allowed_pairs", ctypes.c_int64, [_P, _I, _I]),
+    ("ra_allowed_pairs_packed", ctypes.c_int64, [_P, _I, _I, _V, _V]),
+    ("ra_document_ranges", _I, [_P, _I, _V, _I, _V, _V]),
     ("ra_status_string", ctypes.c_char_p, [_I]),
     ("ra_last_error", ctypes.c_char_p, []),
 ]

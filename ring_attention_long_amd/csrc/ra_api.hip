@@ -71,6 +71,10 @@ ra_status check_shape(const ra_problem* p) {
 ra_status check_problem(const ra_problem* p) {
   const ra_status s = check_shape(p);
   if (s != RA_OK) return s;
+  if ((p->doc_begin == nullptr) != (p->doc_end == nullptr))
+    return fail(RA_ERR_INVALID_ARG, "doc_begin and doc_end must both be set or both be NULL");
+  if (p->doc_begin && (!aligned(p->doc_begin, 4) || !aligned(p->doc_end, 4)))
+    return fail(RA_ERR_INVALID_ARG, "doc_begin / doc_end are not 4-byte aligned");
   if (p->dtype == RA_BF16 && p->d != 128)
     return fail(RA_ERR_UNSUPPORTED, "bf16 kernels support d = 128 only (got %d)", p->d);
   if (p->dtype == RA_F32 && p->d != 64 && p->d != 128)
@@ -116,6 +120,8 @@ ra::StepArgs step_args(const ra_problem* p, int32_t qs, int32_t ks, const void* 
   a.q_shard = qs;
   a.kv_shard = ks;
   a.scale = effective_scale(p);
+  a.doc_begin = p->doc_begin;
+  a.doc_end = p->doc_end;
   return a;
 }
 
@@ -489,6 +495,50 @@ int64_t ra_allowed_pairs(const ra_problem* p, int32_t q_shard, int32_t kv_shard)
     for (int t = 0; t < p->L; ++t) total += ra::kv_limit(p->causal, p->layout, p->N, p->L, q_shard, ks, t);
   }
   return total * p->b;
+}
+
+int64_t ra_allowed_pairs_packed(const ra_problem* p, int32_t q_shard, int32_t kv_shard,
+                                const int32_t* doc_begin_host, const int32_t* doc_end_host) {
+  if (check_shape(p) != RA_OK) return -1;
+  if (q_shard < 0 || q_shard >= p->N || kv_shard < -1 || kv_shard >= p->N) return -1;
+  if (!doc_begin_host || !doc_end_host) return -1;
+  int64_t total = 0;
+  for (int bi = 0; bi < p->b; ++bi)
+    for (int ks = 0; ks < p->N; ++ks) {
+      if (kv_shard >= 0 && ks != kv_shard) continue;
+      for (int t = 0; t < p->L; ++t) {
+        const int64_t i = (int64_t)bi * p->L + t;
+        const ra::KeyRange r = ra::key_range(p->causal, p->layout, p->N, p->L, q_shard, ks, t, true,
+                                             doc_begin_host[i], doc_end_host[i]);
+        total += r.hi - r.lo;
+      }
+    }
+  return total;
+}
+
+ra_status ra_document_ranges(const ra_problem* p, int32_t shard, const int32_t* bounds,
+                             int32_t n_docs, int32_t* begin_out, int32_t* end_out) {
+  RA_TRY(check_shape(p));
+  RA_TRY(check_shard(p, shard, "shard"));
+  if (!bounds || !begin_out || !end_out) return fail(RA_ERR_INVALID_ARG, "NULL array");
+  const int64_t S = (int64_t)p->N * p->L;
+  if (n_docs < 1 || bounds[0] != 0 || bounds[n_docs] != S)
+    return fail(RA_ERR_INVALID_ARG, "bounds must run from 0 to S=%lld over n_docs >= 1 documents",
+                (long long)S);
+  for (int i = 0; i < n_docs; ++i)
+    if (bounds[i + 1] <= bounds[i]) return fail(RA_ERR_INVALID_ARG, "bounds not strictly increasing at %d", i);
+  for (int t = 0; t < p->L; ++t) {
+    const int64_t P = ra::global_pos(p->layout, p->N, p->L, shard, t);
+    int lo = 0, hi = n_docs;                   // largest i with bounds[i] <= P
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (bounds[mid] <= P) lo = mid;
+      else hi = mid;
+    }
+    begin_out[t] = bounds[lo];
+    end_out[t] = bounds[lo + 1];
+  }
+  return RA_OK;
 }
 
 }  // extern "C"

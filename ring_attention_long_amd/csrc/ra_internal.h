@@ -95,6 +95,49 @@ __device__ __forceinline__ void dma16_to_lds(dma_rsrc rsrc, const void* lds_dst,
 }
 #pragma clang diagnostic pop
 
+// ---------------------------------------------------------------------------------------
+// Number of keys of shard ks whose global position is < X (X may lie anywhere; the count is
+// clamped to [0, L]).  Positions increase with the local index, so these keys are a prefix.
+// ---------------------------------------------------------------------------------------
+__host__ __device__ inline int count_below(int layout, int N, int L, int ks, int64_t X) {
+  if (layout == RA_LAYOUT_STRIPED) {
+    // keys at uN + ks < X  <=>  u < (X - ks) / N, rounded up
+    if (X <= ks) return 0;
+    return (int)clamp64((X - ks + N - 1) / N, 0, L);
+  }
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int C = L / 2;
+    const int64_t a = clamp64(X - (int64_t)ks * C, 0, C);
+    const int64_t b = clamp64(X - (int64_t)(2 * N - 1 - ks) * C, 0, C);
+    return (int)(a + b);
+  }
+  return (int)clamp64(X - (int64_t)ks * L, 0, L);
+}
+
+// ---------------------------------------------------------------------------------------
+// Allowed keys of query row t (shard qs) in KV shard ks: the local index range [lo, hi).
+// Without packed documents lo = 0 and hi = kv_limit.  With them (page 3, section 5:
+// documents packed into one window, no attention across documents) the row may only see
+// positions in [doc_begin, doc_end) of its own document, intersected with the causal rule;
+// since positions increase with the local index this is again one index range.
+// doc_begin / doc_end hold the row's document bounds (global positions) for this batch row.
+// ---------------------------------------------------------------------------------------
+struct KeyRange {
+  int lo, hi;
+};
+__host__ __device__ inline KeyRange key_range(int causal, int layout, int N, int L, int qs, int ks,
+                                              int t, bool packed, int64_t doc_begin, int64_t doc_end) {
+  if (!packed) return KeyRange{0, kv_limit(causal, layout, N, L, qs, ks, t)};
+  int64_t end = doc_end;
+  if (causal) {
+    const int64_t P = global_pos(layout, N, L, qs, t);
+    end = end < P + 1 ? end : P + 1;
+  }
+  const int lo = count_below(layout, N, L, ks, doc_begin);
+  const int hi = count_below(layout, N, L, ks, end);
+  return KeyRange{lo, hi > lo ? hi : lo};
+}
+
 // Epilogue of a forward step kernel.
 enum StepMode : int {
   MODE_PART = 0,   // write this step's normalised (O, LSE) partial
@@ -111,6 +154,8 @@ struct StepArgs {
   int causal, layout;
   int q_shard, kv_shard;
   float scale;         // softmax scale on q.k
+  const int32_t* doc_begin;   // [b][L] packed-document bounds of each query row, or null
+  const int32_t* doc_end;
 };
 
 hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t s);

@@ -157,6 +157,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float lse_lds[N_STAGE][TILE_ROWS];   // -LSE log2(e)
   __shared__ __attribute__((aligned(16))) float dlt_lds[N_STAGE][TILE_ROWS];
+  __shared__ __attribute__((aligned(16))) int lo_lds[N_STAGE][TILE_ROWS];   // allowed keys [lo, hi)
+  __shared__ __attribute__((aligned(16))) int hi_lds[N_STAGE][TILE_ROWS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = wave & 3, grp = wave >> 2;
@@ -169,18 +171,37 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   const int u0 = kb * KB;
   const int uw = u0 + 32 * slot;            // this wave's first key
   const int u = uw + lk;                    // this lane's key
-  auto limit = [&](int t) { return kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t); };
+  // allowed keys of query row t: [lo, hi), both nondecreasing in t (see key_range)
+  const bool packed = a.doc_begin != nullptr;
+  auto range_of = [&](int row, int64_t db, int64_t de) {
+    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+  };
+  auto range = [&](int row) {
+    int64_t db = 0, de = 0;
+    if (packed) {
+      db = a.doc_begin[(int64_t)bi * L + row];
+      de = a.doc_end[(int64_t)bi * L + row];
+    }
+    return range_of(row, db, de);
+  };
 
-  // first query row that may see key u0 (limits are nondecreasing in the query index)
+  // the query rows that may see keys [u0, u0 + KB): from the first with hi > u0 to the last
+  // with lo < u0 + KB
   int t_lo = 0, t_hi = L;
   while (t_lo < t_hi) {
     const int mid = (t_lo + t_hi) >> 1;
-    if (limit(mid) > u0) t_hi = mid;
+    if (range(mid).hi > u0) t_hi = mid;
     else t_lo = mid + 1;
   }
-  if (t_lo >= L) return;                    // no query of this step sees these keys
+  int t_stop = t_lo, t_top = L;
+  while (t_stop < t_top) {
+    const int mid = (t_stop + t_top) >> 1;
+    if (range(mid).lo >= u0 + KB) t_top = mid;
+    else t_stop = mid + 1;
+  }
+  if (t_lo >= t_stop) return;               // no query of this step sees these keys
   const int qt_first = t_lo / TILE_ROWS;
-  const int t_end = (L + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+  const int t_end = (t_stop + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
   const int n_iter = (t_end / TILE_ROWS - qt_first) * G;   // (head, query tile) pairs
 
   // resident K rows of this lane's key (B operand [k = d][n = key])
@@ -241,10 +262,17 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   auto stats_index = [&](const Cursor& c) {
     return ((int64_t)bi * a.h + c.hq) * L + min(c.tq0 + lane, L - 1);
   };
-  auto stats_store = [&](const Cursor& c, int buf, float l, float dl) {
-    lse_lds[buf][lane] = (c.tq0 + lane < L && l > -INFINITY) ? -l * LOG2E : -INFINITY;
+  auto doc_index = [&](const Cursor& c) { return (int64_t)bi * L + min(c.tq0 + lane, L - 1); };
+  auto stats_store = [&](const Cursor& c, int buf, float l, float dl, int db, int de) {
+    const int row = c.tq0 + lane;
+    lse_lds[buf][lane] = (row < L && l > -INFINITY) ? -l * LOG2E : -INFINITY;
     dlt_lds[buf][lane] = dl;
+    const KeyRange r = row < L ? range_of(row, db, de) : KeyRange{0, 0};
+    lo_lds[buf][lane] = r.lo;
+    hi_lds[buf][lane] = r.hi;
   };
+  auto doc_b = [&](const Cursor& c) { return packed ? a.doc_begin[doc_index(c)] : 0; };
+  auto doc_e = [&](const Cursor& c) { return packed ? a.doc_end[doc_index(c)] : 0; };
 
   // ---- prologue: V rows, tile 0 (and its statistics and those of tile 1) in place ----------
   {
@@ -263,10 +291,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   Cursor cs = first;                          // next tile to stage
   if (grp == 1) stage_dma(cs, 0);
   if (wave == 4) {
-    stats_store(cs, 0, lse[stats_index(cs)], delta[stats_index(cs)]);
+    stats_store(cs, 0, lse[stats_index(cs)], delta[stats_index(cs)], doc_b(cs), doc_e(cs));
     Cursor c1 = cs;
     advance(c1);
-    if (n_iter > 1) stats_store(c1, 1, lse[stats_index(c1)], delta[stats_index(c1)]);
+    if (n_iter > 1)
+      stats_store(c1, 1, lse[stats_index(c1)], delta[stats_index(c1)], doc_b(c1), doc_e(c1));
   }
   advance(cs);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V rows and tile 0 are in place
@@ -340,13 +369,22 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   auto vector_phase = [&](int j, int bcur) __attribute__((always_inline)) {
     const int r0 = cc.tq0 + 32 * grp;
     bool skip = j >= n_iter || r0 >= L;
-    if (!skip) skip = limit(min(r0 + 31, L - 1)) <= uw;
+    bool full = false;
+    if (!skip) {
+      // the half's first row and last row inside the shard bound its key ranges
+      const int i0 = 32 * grp, i1 = min(32 * grp + 31, L - 1 - cc.tq0);
+      const int lo_first = __builtin_amdgcn_readfirstlane(lo_lds[bcur][i0]);
+      const int hi_first = __builtin_amdgcn_readfirstlane(hi_lds[bcur][i0]);
+      const int lo_last = __builtin_amdgcn_readfirstlane(lo_lds[bcur][i1]);
+      const int hi_last = __builtin_amdgcn_readfirstlane(hi_lds[bcur][i1]);
+      skip = hi_last <= uw || lo_first >= uw + 32;
+      full = hi_first >= uw + 32 && lo_last <= uw;   // rows past the shard end have LSE = -inf
+    }
     skip = __builtin_amdgcn_readfirstlane((int)skip) != 0;
     if (skip) {
       pb[0] = pb[1] = ds[0] = ds[1] = bf16x8{};
       return;
     }
-    const bool full = limit(r0) >= uw + 32;   // rows past the shard end have LSE = -inf
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int rr = 32 * grp + 8 * q4 + 4 * lg;
@@ -361,14 +399,20 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
       }
     }
     if (!full) {
-      // keep this a real (scalar) branch: only diagonal tiles pay for the mask
+      // keep this a real (scalar) branch: only diagonal and boundary tiles pay for the mask
       __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = r0 + 8 * (i >> 2) + 4 * lg + (i & 3);
-        if (u >= limit(row)) {
-          sc[i] = 0.f;
-          dp[i] = 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 32 * grp + 8 * q4 + 4 * lg;
+        const i32x4 lo4 = *(const i32x4*)&lo_lds[bcur][rr];
+        const i32x4 hi4 = *(const i32x4*)&hi_lds[bcur][rr];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 4 * q4 + x;
+          if (u >= hi4[x] || u < lo4[x]) {
+            sc[i] = 0.f;
+            dp[i] = 0.f;
+          }
         }
       }
     }
@@ -382,6 +426,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   };
 
   float st_l = 0.f, st_d = 0.f;             // statistics in flight (wave 4)
+  int st_b = 0, st_e = 0;
   if (grp == 1) {
     if (n_iter > 1) stage_dma(cs, 1);
     barrier_no_fence();
@@ -398,7 +443,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
       if (wave == 4 && j >= 1 && j + 1 < n_iter) {
         Cursor c1 = cc;
         advance(c1);
-        stats_store(c1, bnext, st_l, st_d);
+        stats_store(c1, bnext, st_l, st_d, st_b, st_e);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the barrier
       }
     }
@@ -410,6 +455,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
         const int64_t si = stats_index(cs);
         st_l = lse[si];
         st_d = delta[si];
+        if (packed) {
+          st_b = a.doc_begin[doc_index(cs)];
+          st_e = a.doc_end[doc_index(cs)];
+        }
       }
     }
     vector_phase(j, bcur);
@@ -498,19 +547,38 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   const int t0 = t0_wg + (wave / Hw) * 32;
   const int t = t0 + lq;
   const int tc = min(t, L - 1);
-  auto limit = [&](int row) { return kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row); };
-
-  const int lim = t < L ? limit(t) : 0;
-  int wave_tiles = 0, wave_full = 0, n_tiles = 0;
+  // allowed keys of row t: [lo, hi), both nondecreasing in t (see key_range); tile classes
+  // as in the forward step kernel
+  const bool packed = a.doc_begin != nullptr;
+  auto range = [&](int row) {
+    int64_t db = 0, de = 0;
+    if (packed) {
+      db = a.doc_begin[(int64_t)bi * L + row];
+      de = a.doc_end[(int64_t)bi * L + row];
+    }
+    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+  };
+  const KeyRange rr = t < L ? range(t) : KeyRange{0, 0};
+  const int lim = rr.hi, lo = rr.lo;
+  int wave_first = 0, wave_tiles = 0, full_begin = 0, full_end = 0, j_begin = 0, n_tiles = 0;
   if (t0 < L) {
-    wave_tiles = (limit(min(t0 + 31, L - 1)) + 63) / 64;
-    wave_full = limit(t0) / 64;
+    const KeyRange r0 = range(t0), r1 = range(min(t0 + 31, L - 1));
+    wave_first = r0.lo / 64;
+    wave_tiles = (r1.hi + 63) / 64;
+    full_begin = (r1.lo + 63) / 64;
+    full_end = r0.hi / 64;
   }
-  if (t0_wg < L) n_tiles = (limit(min(t0_wg + 32 * PB - 1, L - 1)) + 63) / 64;
+  if (t0_wg < L) {
+    j_begin = range(t0_wg).lo / 64;
+    n_tiles = (range(min(t0_wg + 32 * PB - 1, L - 1)).hi + 63) / 64;
+  }
+  wave_first = __builtin_amdgcn_readfirstlane(wave_first);
   wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
-  wave_full = __builtin_amdgcn_readfirstlane(wave_full);
+  full_begin = __builtin_amdgcn_readfirstlane(full_begin);
+  full_end = __builtin_amdgcn_readfirstlane(full_end);
+  j_begin = __builtin_amdgcn_readfirstlane(j_begin);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  if (n_tiles == 0) return;   // uniform over the workgroup: no key of this step is allowed
+  if (n_tiles <= j_begin) return;   // uniform over the workgroup: no key of this step is allowed
 
   // resident operands: Q^T and dO^T of this lane's query, one row per lane
   const int64_t qrow = (((int64_t)bi * L + tc) * a.h + hq) * D + lg * 8;
@@ -605,20 +673,24 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   auto vector_phase = [&](int j, int vs2, int ks3) __attribute__((always_inline)) {
     if (grp == 0) tile_dma(v_rsrc, v_lds[vs2], j + 2);
     else tile_dma(k_rsrc, k_lds[ks3], j + 3);
-    if (j >= wave_tiles) {
+    if (j >= wave_tiles || j < wave_first) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) ds[c] = bf16x8{};
       return;
     }
-    if (j >= wave_full) {
-      // keep this a real (scalar) branch: only diagonal and ragged tiles pay for the mask
+    if (j < full_begin || j >= full_end) {
+      // keep this a real (scalar) branch: only diagonal, boundary and ragged tiles pay for
+      // the mask
       __asm__ volatile("" ::: "memory");
       const int thr = lim - (j * 64 + 4 * lg);       // first masked key offset of this row
+      const int thr_lo = lo - (j * 64 + 4 * lg);     // first allowed key offset of this row
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * jj + 8 * (i >> 2) + (i & 3) >= thr) sc[jj][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int x = 32 * jj + 8 * (i >> 2) + (i & 3);
+          if (x >= thr || x < thr_lo) sc[jj][i] = -INFINITY;
+        }
     }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -635,11 +707,11 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
     for (int i = tid; i < TILE_BYTES / 16; i += DQ_THREADS) z[i] = u32x4{};
   }
   if (grp == 1) {
-    tile_dma(k_rsrc, k_lds[0], 0);
-    tile_dma(k_rsrc, k_lds[1], 1);
+    tile_dma(k_rsrc, k_lds[0], j_begin);
+    tile_dma(k_rsrc, k_lds[1], j_begin + 1);
   } else {
-    tile_dma(v_rsrc, v_lds[0], 0);
-    tile_dma(v_rsrc, v_lds[1], 1);
+    tile_dma(v_rsrc, v_lds[0], j_begin);
+    tile_dma(v_rsrc, v_lds[1], j_begin + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
@@ -649,11 +721,11 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   // the stage of V(j-1) and has it by the end of 2j+4; group 1 loads K(j+3) in 2j+3 into the
   // stage of K(j-1) and has it by the end of 2j+5.
   if (grp == 1) {
-    tile_dma(k_rsrc, k_lds[2], 2);
+    tile_dma(k_rsrc, k_lds[2], j_begin + 2);
     barrier_no_fence();
   }
-  int ks = 0, vs = 0;
-  for (int j = 0; j <= n_tiles; ++j) {
+  int ks = 0, vs = 0;                     // stages of tile j: counted from j_begin
+  for (int j = j_begin; j <= n_tiles; ++j) {
     const int kp = ks == 0 ? K_STAGES - 1 : ks - 1;
     const int ks3 = kp;                               // stage of K(j+3) (held K(j-1))
     const int vs2 = vs == 0 ? V_STAGES - 1 : vs - 1;  // stage of V(j+2) (held V(j-1))

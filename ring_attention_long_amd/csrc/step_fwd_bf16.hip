@@ -130,21 +130,40 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const __bf16* vp = (const __bf16*)a.v;
   const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
 
-  // ---- key limits and tile ranges ---------------------------------------------------
-  const int lim = t < L ? kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t) : 0;
-  int wave_tiles = 0, wave_full = 0;
+  // ---- key ranges and tile ranges ----------------------------------------------------
+  // Row t may attend to the keys [lo, hi) of this KV shard (a prefix when documents are
+  // not packed).  Both bounds are nondecreasing in t, so a wave's tile range comes from its
+  // first and last valid rows: tiles before wave_first or from wave_tiles on are skipped,
+  // tiles in [full_begin, full_end) need no mask, the rest are masked.
+  const bool packed = a.doc_begin != nullptr;
+  auto range = [&](int row) {
+    int64_t db = 0, de = 0;
+    if (packed) {
+      db = a.doc_begin[(int64_t)bi * L + row];
+      de = a.doc_end[(int64_t)bi * L + row];
+    }
+    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+  };
+  const KeyRange rr = t < L ? range(t) : KeyRange{0, 0};
+  const int lim = rr.hi, lo = rr.lo;
+  int wave_first = 0, wave_tiles = 0, full_begin = 0, full_end = 0;
   if (t0 < L) {
-    const int t_last = min(t0 + QW - 1, L - 1);
-    wave_tiles = (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t_last) + BN - 1) / BN;
-    wave_full = kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t0) / BN;
+    const KeyRange r0 = range(t0), r1 = range(min(t0 + QW - 1, L - 1));
+    wave_first = r0.lo / BN;
+    wave_tiles = (r1.hi + BN - 1) / BN;
+    full_begin = (r1.lo + BN - 1) / BN;
+    full_end = r0.hi / BN;
   }
+  wave_first = __builtin_amdgcn_readfirstlane(wave_first);
   wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
-  wave_full = __builtin_amdgcn_readfirstlane(wave_full);
-  int n_tiles = 0;
+  full_begin = __builtin_amdgcn_readfirstlane(full_begin);
+  full_end = __builtin_amdgcn_readfirstlane(full_end);
+  int j_begin = 0, n_tiles = 0;     // the workgroup's key tiles: [j_begin, n_tiles)
   if (t0_wg < L) {
-    const int t_last = min(t0_wg + QW * PB - 1, L - 1);
-    n_tiles = (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t_last) + BN - 1) / BN;
+    j_begin = range(t0_wg).lo / BN;
+    n_tiles = (range(min(t0_wg + QW * PB - 1, L - 1)).hi + BN - 1) / BN;
   }
+  j_begin = __builtin_amdgcn_readfirstlane(j_begin);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
 
   // ---- Q^T operand, resident for the whole kernel -------------------------------------
@@ -300,20 +319,24 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     const int dma_stage = group ? stage : (stage == 2 ? 0 : stage + 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) issue_one(dma_tile_idx, dma_stage, t);
-    if (j >= wave_tiles) {
+    if (j >= wave_tiles || j < wave_first) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) pb[c] = bf16x8{};
       return;
     }
-    if (j >= wave_full) {
-      // keep this a real (scalar) branch: only diagonal and ragged tiles pay for the mask
+    if (j < full_begin || j >= full_end) {
+      // keep this a real (scalar) branch: only diagonal, boundary and ragged tiles pay for
+      // the mask
       __asm__ volatile("" ::: "memory");
       const int thr = lim - (j * BN + 4 * lg);       // first masked key offset of this row
+      const int thr_lo = lo - (j * BN + 4 * lg);     // first allowed key offset of this row
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * jj + 8 * (i >> 2) + (i & 3) >= thr) sc[jj][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int x = 32 * jj + 8 * (i >> 2) + (i & 3);
+          if (x >= thr || x < thr_lo) sc[jj][i] = -INFINITY;
+        }
     }
     bool full_path = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     float rs = 0.f;
@@ -354,27 +377,29 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // alternate between matrix and vector work.  Numbering the intervals between barriers,
   // interval 2j+1 holds group 0's matrix phase j and group 1's softmax phase j-1, interval
   // 2j+2 group 0's softmax phase j and group 1's matrix phase j.  K(j) is read in
-  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4; tile j lives in stage j % 3.
+  // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4; tile j lives in stage (j - j_begin) % 3
+  // (j_begin: the workgroup's first key tile; the steps below count from it).
   // Staging: in its softmax phase j (interval 2j+2) group 0 loads V(j+1), first read in
   // interval 2j+5; in its softmax phase j (interval 2j+3) group 1 loads K(j+3), first read
   // in interval 2j+7.  Each wave waits for its loads at the end of its next softmax phase
   // (vmcnt(4): only the four just issued may still be in flight), before the barrier that
-  // opens the first interval reading them.  The prologue loads K(0), K(1), V(0) completely
-  // and starts K(2), which group 1's first wait covers.
+  // opens the first interval reading them.  The prologue loads the first two K tiles and
+  // the first V tile completely and starts the third K tile, which group 1's first wait
+  // covers.
   {
     u32x4* z = (u32x4*)v_lds[2];        // read by the (zero-P) PV of step 0
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
   }
   if (group == 1) {
-    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, 0);   // rows past L arrive as zeros
-    issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, 1);
+    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, j_begin);   // rows past L arrive as zeros
+    issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, j_begin + 1);
   } else {
-    issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, 0);
+    issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, j_begin);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, K(0), K(1), V(0) are in place
   __syncthreads();
   if (group == 1) {
-    issue_tile_dma(k_rsrc, k_lds[2], k_dma_off, 2);
+    issue_tile_dma(k_rsrc, k_lds[2], k_dma_off, j_begin + 2);
     barrier_no_fence();
   }
   auto step = [&](int j, auto stage_c) __attribute__((always_inline)) {
@@ -387,8 +412,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     barrier_no_fence();
   };
   // unrolled by the three stages so that every LDS address in the matrix phase is a
-  // per-lane base plus an immediate
-  for (int j = 0; j <= n_tiles; j += 3) {
+  // per-lane base plus an immediate; tile j lives in stage (j - j_begin) % 3
+  for (int j = j_begin; j <= n_tiles; j += 3) {
     step(j, Stage<0>{});
     if (j + 1 > n_tiles) break;
     step(j + 1, Stage<1>{});

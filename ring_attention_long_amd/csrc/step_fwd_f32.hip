@@ -4,7 +4,7 @@
 // Formulations"), kept plain for full fp32 accuracy: one thread owns one query row, the
 // workgroup's 64 rows share K/V tiles of 32 keys staged in LDS (every lane reads the same
 // key, an LDS broadcast), and the running maximum is refreshed exactly on every tile.
-// Causal masking uses the same per-row key limit as the bf16 kernel.
+// Causal and packed-document masking use the same per-row key range as the bf16 kernel.
 #include "ra_internal.h"
 
 namespace ra {
@@ -25,9 +25,20 @@ __global__ __launch_bounds__(ROWS) void step_fwd_f32_kernel(StepArgs a, int n_qb
   const int g = hq / G;
   const int t = qb * ROWS + threadIdx.x;
   const int t_last = min(qb * ROWS + ROWS - 1, L - 1);
-  const int n_tiles =
-      (kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t_last) + KT - 1) / KT;
-  const int lim = t < L ? kv_limit(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, t) : 0;
+  // allowed keys of a row: [lo, hi), nondecreasing in the row (see key_range)
+  const bool packed = a.doc_begin != nullptr;
+  auto range = [&](int row) {
+    int64_t db = 0, de = 0;
+    if (packed) {
+      db = a.doc_begin[(int64_t)bi * L + row];
+      de = a.doc_end[(int64_t)bi * L + row];
+    }
+    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+  };
+  const int j_begin = range(qb * ROWS).lo / KT;
+  const int n_tiles = (range(t_last).hi + KT - 1) / KT;
+  const KeyRange rr = t < L ? range(t) : KeyRange{0, 0};
+  const int lim = rr.hi, lo = rr.lo;
 
   const float* qp = (const float*)a.q + (((int64_t)bi * L + min(t, L - 1)) * a.h + hq) * D;
   const float* kp = (const float*)a.k + ((int64_t)bi * L * a.n_kv + g) * D;
@@ -40,7 +51,7 @@ __global__ __launch_bounds__(ROWS) void step_fwd_f32_kernel(StepArgs a, int n_qb
   }
   float m = -INFINITY, l = 0.f;
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = j_begin; j < n_tiles; ++j) {
     const int kv0 = j * KT;
     __syncthreads();
     for (int idx = threadIdx.x; idx < KT * D; idx += ROWS) {
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(ROWS) void step_fwd_f32_kernel(StepArgs a, int n_qb
       float x = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) x = fmaf(q[e], k_lds[r][e], x);
-      s[r] = (kv0 + r < lim) ? x : -INFINITY;
+      s[r] = (kv0 + r < lim && kv0 + r >= lo) ? x : -INFINITY;
       mt = fmaxf(mt, s[r]);
     }
     const float m_new = fmaxf(m, mt);

@@ -198,3 +198,46 @@ def test_backward_workspace_is_two_kv_buffers_plus_delta():
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
     want = 4 * pad(2 * 1000 * 2 * 128 * 2) + pad(2 * 4 * 1000 * 4)
     assert lib.ra_ring_bwd_workspace(ctypes.byref(p)) == want
+
+
+# ------------------------------------------------------------------ packed documents (host side)
+DOC_BOUNDS = np.array([0, 7, 8, 19, 33, 40], dtype=np.int32)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_document_ranges_match_oracle(layout):
+    from oracle import document_of, shard_tokens
+    N, L = 4, 10
+    for shard in range(N):
+        begin, end = ra.document_ranges(DOC_BOUNDS, N=N, L=L, shard=shard, layout=layout)
+        doc = document_of(shard_tokens(layout, N, L)[shard], DOC_BOUNDS)
+        np.testing.assert_array_equal(begin, DOC_BOUNDS[doc])
+        np.testing.assert_array_equal(end, DOC_BOUNDS[doc + 1])
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_allowed_pairs_packed_match_oracle(layout, causal):
+    N, L = 4, 10
+    for shard in range(N):
+        begin, end = ra.document_ranges(DOC_BOUNDS, N=N, L=L, shard=shard, layout=layout)
+        for kv in [-1] + list(range(N)):
+            got = ra.allowed_pairs_packed(begin[None], end[None], N=N, q_shard=shard, kv_shard=kv,
+                                          causal=causal, layout=layout)
+            want = oracle_pairs(layout, N, L, shard, None if kv < 0 else kv, causal,
+                                docs=DOC_BOUNDS)
+            assert got == want, (shard, kv)
+
+
+def test_document_inputs_are_validated():
+    lib = _lib.lib()
+    p = _prob()
+    p.doc_begin = FAKE.value            # doc_end missing
+    assert lib.ra_step_fwd(ctypes.byref(p), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.RA_ERR_INVALID_ARG
+    p.doc_end = 0x10002                 # misaligned
+    assert lib.ra_step_fwd(ctypes.byref(p), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_step_bwd(ctypes.byref(p), 0, 0, *([FAKE] * 9), None) == _lib.RA_ERR_INVALID_ARG
+    with pytest.raises(ra.RaError):     # bounds must run from 0 to S, strictly increasing
+        ra.document_ranges(np.array([0, 5, 5, 40], dtype=np.int32), N=4, L=10, shard=0)
+    with pytest.raises(ra.RaError):
+        ra.document_ranges(np.array([0, 39], dtype=np.int32), N=4, L=10, shard=0)
