@@ -53,6 +53,13 @@ BWD_WORKLOADS = {
                               "bf16, shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
                               "striped", True, 0, 1005),
 }
+# packed-document workloads (page 3, section 5): the same shapes with documents of lognormal
+# length packed into the window; value counts only pairs inside a document
+WORKLOADS["packed_striped_causal_32k"] = (
+    "ring_fwd striped causal, packed documents (lognormal lengths, mean 4096), S=262144 N=8 "
+    "L=32768 h=32 n_kv=8 d=128 bf16, shard 0", dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8),
+    "striped", True, 0, 1006)
+PACKED_MEAN_LEN = {"packed_striped_causal_32k": 4096}
 DEFAULT_WORKLOAD = "striped_causal_32k"
 METRIC = "ring-step attention TFLOP/s (bf16, causal) and % of MI355X MFMA peak"
 BWD_METRIC = ("ring-step attention backward TFLOP/s (bf16, causal, 2.5x forward FLOPs) and % of "
@@ -64,10 +71,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0):
+def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0, docs=None):
     """Time the fp64 oracle on whole query rows (all heads, every key of the sequence)
     until about budget_s seconds of CPU work; report useful TFLOP/s of that sample."""
-    from oracle import allowed_pairs, shard_attention, shard_tokens  # noqa: F401
+    from oracle import allowed_mask, shard_attention, shard_tokens
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -85,10 +92,13 @@ def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0):
     while elapsed < budget_s and len(rows_done) < L:
         rows = rng.choice(L, size=chunk, replace=False)
         t0 = time.perf_counter()
-        shard_attention(q, k_all, v_all, N=N, shard=shard, layout=layout, causal=causal, rows=rows)
+        shard_attention(q, k_all, v_all, N=N, shard=shard, layout=layout, causal=causal, rows=rows,
+                        docs=docs)
         elapsed += time.perf_counter() - t0
         rows_done.extend(rows.tolist())
-        if causal:
+        if docs is not None:
+            pairs += int(allowed_mask(toks[shard][rows], all_pos, causal=causal, docs=docs).sum())
+        elif causal:
             pairs += int(np.searchsorted(all_pos, toks[shard][rows], side="right").sum())
         else:
             pairs += chunk * N * L
@@ -427,13 +437,25 @@ def main():
                      device=dev, dtype=torch.uint8)
     o = torch.empty_like(q)
     lse = torch.empty((b, h, L), device=dev, dtype=torch.float32)
-    pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+    docs = bounds = None
+    if args.workload in PACKED_MEAN_LEN:
+        bounds = synth.document_bounds(N * L, seed=seed, mean_len=PACKED_MEAN_LEN[args.workload])
+        begin, end = ra.document_ranges(bounds, N=N, L=L, shard=shard, layout=layout)
+        docs = (torch.from_numpy(begin[None]).to(dev), torch.from_numpy(end[None]).to(dev))
+
+    def pairs_of(kv_shard=-1):
+        if docs is None:
+            return ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=kv_shard, causal=causal,
+                                    layout=layout)
+        return ra.allowed_pairs_packed(begin[None], end[None], N=N, q_shard=shard,
+                                       kv_shard=kv_shard, causal=causal, layout=layout)
+    pairs = pairs_of()
     flops = accounting.flops_from_pairs(pairs, h, d)
     compute = torch.cuda.current_stream()
 
     def one_pass():
         ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws,
-                    out=o, lse_out=lse)
+                    out=o, lse_out=lse, docs=docs)
 
     for i in range(args.warmup):
         one_pass()
@@ -454,16 +476,14 @@ def main():
     step_ms, live_flops, timings = [], 0, []
     for _ in range(3):
         _, _, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
-                                     workspace=ws, out=o, lse_out=lse)
+                                     workspace=ws, out=o, lse_out=lse, docs=docs)
         timings.append(tm)
     tm = timings[-1]
     for k in range(N):
         src = (shard - k) % N
         if tm["step_begin_ms"][k] >= 0:
             step_ms.append(tm["step_end_ms"][k] - tm["step_begin_ms"][k])
-            live_flops += accounting.flops_from_pairs(
-                ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal,
-                                 layout=layout), h, d)
+            live_flops += accounting.flops_from_pairs(pairs_of(src), h, d)
     kern_ms = sum(step_ms)
     achieved = live_flops / (kern_ms * 1e-3) / 1e12
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
@@ -495,6 +515,7 @@ def main():
         "data": "synthetic: iid N(0,1) bf16 Q/K/V from seeded numpy PCG64",
         "config": {"workload": desc, "S": N * L, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv,
                    "d": d, "layout": layout, "causal": causal, "q_shard": shard,
+                   "documents": None if bounds is None else int(bounds.size - 1),
                    "useful_tflop_per_pass": round(flops / 1e12, 4),
                    "pct_of_bf16_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -511,7 +532,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(inp, cfg, layout, causal, shard, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, layout, causal, shard, args.cpu_budget,
+                                              docs=bounds)
     print(json.dumps(result), flush=True)
 
 
