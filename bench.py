@@ -388,6 +388,34 @@ def run_sweep(args):
         "finalize_bf16": gbps(lambda: ra.finalize(oa), 6 * b * L * h * d),
         "torch_copy_fp32": gbps(lambda: dst.copy_(oa), 8 * b * L * h * d),
         "spec": 8000.0, "merge_bytes_per_call": merge_bytes}
+    # (5) packed documents (page 3, section 5): mean document length against the work left
+    #     and the step time, with the staged KV bytes per step unchanged
+    import synth
+    packed = []
+    for mean_len in (1024, 4096, 16384, 65536):
+        bounds = synth.document_bounds(N * L, seed=1006, mean_len=mean_len)
+        row = {"mean_doc_len": mean_len, "documents": int(bounds.size - 1)}
+        for layout in ("striped", "contiguous"):
+            begin, end = ra.document_ranges(bounds, N=N, L=L, shard=0, layout=layout)
+            docs = (torch.from_numpy(begin[None]).to(dev), torch.from_numpy(end[None]).to(dev))
+            ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=True, layout=layout), device=dev,
+                             dtype=torch.uint8)
+            for _ in range(2):
+                ra.ring_fwd(q, k, v, q_shard=0, causal=True, layout=layout, workspace=ws, docs=docs)
+            tm = sorted((ra.ring_fwd_timed(q, k, v, q_shard=0, causal=True, layout=layout,
+                                           workspace=ws, docs=docs)[2] for _ in range(3)),
+                        key=lambda t: t["total_ms"])[1]
+            pairs = ra.allowed_pairs_packed(begin[None], end[None], N=N, q_shard=0, causal=True,
+                                            layout=layout)
+            fl = accounting.flops_from_pairs(pairs, h, d)
+            steps = [tm["step_end_ms"][kk] - tm["step_begin_ms"][kk] for kk in range(N)
+                     if tm["step_begin_ms"][kk] >= 0]
+            row[layout] = {"useful_tflop": round(fl / 1e12, 4), "pass_ms": round(tm["total_ms"], 4),
+                           "tflops": round(fl / tm["total_ms"] / 1e9, 1),
+                           "step_ms_mean": round(float(np.mean(steps)), 4)}
+        packed.append(row)
+        log(f"[sweep] packed {row}")
+    out["sweep"]["packed_L32768_shard0"] = packed
     out["sweep"]["peak_bf16_tflops"] = accounting.MI355X_BF16_DENSE_TFLOPS
     print(json.dumps(out), flush=True)
 

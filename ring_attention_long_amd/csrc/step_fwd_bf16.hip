@@ -165,6 +165,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   }
   j_begin = __builtin_amdgcn_readfirstlane(j_begin);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  // no row of the workgroup sees a key of this shard: merging would leave (O, LSE) as it is
+  if (MODE == MODE_MERGE && n_tiles <= j_begin) return;
 
   // ---- Q^T operand, resident for the whole kernel -------------------------------------
   // Rows past the shard end read row L-1 instead: they are never stored, and their key
