@@ -143,6 +143,37 @@ def copy_calibration(mib, steps):
                                            "dispatches": steps, "kernel": "copy_f32_kernel"}}))
 
 
+def overlap_fraction(copy_begin, copy_end, steps):
+    """Share of a staging copy that ran while some step kernel ran ([begin, end) intervals,
+    pairwise disjoint since the steps share one stream).  The driver starts a copy as soon
+    as the buffer it fills is free, which can be during an earlier step than the one just
+    before the step it stages, so every step interval counts."""
+    inside = sum(max(0.0, min(copy_end, e) - max(copy_begin, b)) for b, e in steps)
+    return inside / (copy_end - copy_begin)
+
+
+def exposure_band(exposed_ms, compute_ms):
+    """The pages' three bands for exposed communication over compute time."""
+    r = exposed_ms / compute_ms if compute_ms > 0 else 0.0
+    return "< 5 %" if r < 0.05 else ("5-15 %" if r <= 0.15 else "> 15 %")
+
+
+def timed_passes(one_pass, steps, stream):
+    """Run `steps` passes between HIP events on `stream`: mean ms per pass, and the median,
+    min and max of the individual passes (an event between passes)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        one_pass()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    return mean, {"median": round(float(np.median(per)), 4), "min": round(min(per), 4),
+                  "max": round(max(per), 4)}
+
+
 def cpu_baseline_bwd(inp, cfg, layout, causal, shard, budget_s=20.0):
     """Time the fp64 oracle's dQ of whole query rows (all heads, every key) until about
     budget_s seconds; report TFLOP/s counting the three products a dQ row needs (S, dP,
@@ -174,6 +205,83 @@ def cpu_baseline_bwd(inp, cfg, layout, causal, shard, budget_s=20.0):
             "kind": "oracle",
             "sample": f"dQ of {len(rows_done)} random query rows of shard {shard} x all {h} heads "
                       f"against all {N * L} keys (fp64 numpy, {elapsed:.1f} s; 6 h d FLOPs per pair)"}
+
+
+def oracle_timing():
+    """The fp64 oracle on the host cores, per configuration, in useful TFLOP/s (a baseline,
+    not a target).  c1 runs in full (median of 5); the large ones on a fixed sample of query
+    rows (all heads, every key), extrapolated by allowed pairs."""
+    import platform
+    import statistics
+
+    import synth
+    from oracle import allowed_mask, shard_attention, shard_dq_rows, shard_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{k: p.get(k) for k in ("internal_api", "num_threads", "version")}
+                for p in threadpool_info()]
+    except Exception:  # pragma: no cover
+        blas = []
+    model = ""
+    try:
+        model = next(line.split(":", 1)[1].strip() for line in open("/proc/cpuinfo")
+                     if line.startswith("model name"))
+    except (OSError, StopIteration):
+        model = platform.processor()
+    out = {"host": {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+                    "sched_affinity": len(os.sched_getaffinity(0)), "blas": blas}, "configs": {}}
+
+    def rows_sample(L, n, seed):
+        rng = np.random.default_rng(seed)
+        return np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=n, replace=False)]))
+
+    def fwd_case(name, cfg, layout, causal, shard, seed, dtype, n_rows=None, reps=1):
+        b, L, h, d, N = cfg["b"], cfg["L"], cfg["h"], cfg["d"], cfg["N"]
+        inp = synth.shard_inputs(**cfg, q_shard=shard, seed=seed, dtype=dtype)
+        x = {k: inp[k].astype(np.float64) for k in ("q", "k_all", "v_all")}
+        toks = shard_tokens(layout, N, L)
+        all_pos = np.sort(np.concatenate(toks))
+        rows = None if n_rows is None else rows_sample(L, n_rows, 7)
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            shard_attention(x["q"], x["k_all"], x["v_all"], N=N, shard=shard, layout=layout,
+                            causal=causal, rows=rows)
+            ts.append(time.perf_counter() - t0)
+        sel = toks[shard] if rows is None else toks[shard][rows]
+        pairs = int(allowed_mask(sel, all_pos, causal=causal).sum()) * b
+        full_pairs = int(allowed_mask(toks[shard], all_pos, causal=causal).sum()) * b
+        t = statistics.median(ts)
+        tf = 4.0 * h * d * pairs / t / 1e12
+        out["configs"][name] = {
+            "useful_tflops": tf, "seconds": round(t, 3),
+            "sample": "full shard" if rows is None else f"{rows.size} rows, all heads, every key",
+            "full_shard_seconds_extrapolated": round(t * full_pairs / pairs, 1)}
+        log(f"[oracle] {name}: {out['configs'][name]}")
+
+    fwd_case("c1 fp32 S=1024 N=4 d=64 non-causal", dict(b=1, L=256, h=1, n_kv=1, d=64, N=4),
+             "contiguous", False, 0, 1001, "f32", None, reps=5)
+    fwd_case("c2 bf16 S=65536 N=8 non-causal GQA", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
+             "contiguous", False, 0, 1002, "bf16", 256)
+    fwd_case("c3 bf16 S=262144 N=8 contiguous causal shard 7",
+             dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "contiguous", True, 7, 1003, "bf16", 256)
+    fwd_case("c4 bf16 S=262144 N=8 striped causal shard 0",
+             dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "striped", True, 0, 1004, "bf16", 256)
+    # c5: the backward's dQ rows (three products per pair)
+    cfg = dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8)
+    inp = synth.shard_inputs(**cfg, q_shard=0, seed=1005, dtype="bf16", with_dout=True)
+    x = {k: inp[k].astype(np.float64) for k in ("q", "k_all", "v_all", "dout")}
+    rows = rows_sample(8192, 128, 8)
+    t0 = time.perf_counter()
+    shard_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=8, shard=0,
+                  layout="striped", causal=True)
+    t = time.perf_counter() - t0
+    toks = shard_tokens("striped", 8, 8192)
+    pairs = int(allowed_mask(toks[0][rows], np.sort(np.concatenate(toks)), causal=True).sum())
+    out["configs"]["c5 bf16 backward S=65536 striped causal shard 0 (dQ rows)"] = {
+        "useful_tflops": 6.0 * 32 * 128 * pairs / t / 1e12, "seconds": round(t, 3),
+        "sample": f"dQ of {rows.size} rows, all heads, every key (6 h d FLOPs per pair)"}
+    print(json.dumps({"oracle_timing": out}), flush=True)
 
 
 def run_backward(args):
@@ -210,14 +318,7 @@ def run_backward(args):
         one_pass()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(compute)
-    for _ in range(args.steps):
-        one_pass()
-    t1.record(compute)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
 
@@ -256,6 +357,7 @@ def run_backward(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "pass_ms": pass_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -308,7 +410,9 @@ def run_sweep(args):
         return sorted(runs, key=lambda t: t["total_ms"])[reps // 2]
 
     def summarise(tm, L, shard, layout, causal):
-        steps, copies, overlap, exposed = [], [], [], []
+        steps, copies, overlapped, exposed = [], [], [], []
+        intervals = [(tm["step_begin_ms"][k], tm["step_end_ms"][k]) for k in range(N)
+                     if tm["step_begin_ms"][k] >= 0]
         for k in range(N):
             if tm["step_begin_ms"][k] >= 0:
                 steps.append(tm["step_end_ms"][k] - tm["step_begin_ms"][k])
@@ -317,14 +421,14 @@ def run_sweep(args):
                 copies.append(ce - cb)
                 sb, se = tm["step_begin_ms"][k - 1], tm["step_end_ms"][k - 1]
                 if sb >= 0 and ce > cb:
-                    overlap.append(max(0.0, min(ce, se) - max(cb, sb)) / (ce - cb))
+                    overlapped.append(overlap_fraction(cb, ce, intervals))
                     exposed.append(max(0.0, ce - se))
         pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
         fl = accounting.flops_from_pairs(pairs, h, d)
         return {"pass_ms": round(tm["total_ms"], 4), "tflops": round(fl / tm["total_ms"] / 1e9, 1),
                 "live_steps": len(steps), "step_ms_mean": round(float(np.mean(steps)), 4) if steps else 0,
                 "copy_ms_mean": round(float(np.mean(copies)), 4) if copies else 0,
-                "overlap_min": round(min(overlap), 4) if overlap else None,
+                "overlap_min": round(min(overlapped), 4) if overlapped else None,
                 "exposed_ms_max": round(max(exposed), 4) if exposed else None}
 
     out = {"sweep": {"h": h, "n_kv": n_kv, "d": d, "N": N, "b": b, "data": "torch.randn bf16, seed 1004"}}
@@ -426,6 +530,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS))
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="CPU only: time the fp64 oracle on each configuration (full or a bounded "
+                         "sample, extrapolated) and describe the host")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of one workload: L sweep of the striped causal ring pass, every "
                          "shard of each causal layout at L=32768, copy interference, merge GB/s")
@@ -438,6 +545,8 @@ def main():
     args = ap.parse_args()
     if args.copy_calibration_mb:
         return copy_calibration(args.copy_calibration_mb, args.steps)
+    if args.oracle_timing:
+        return oracle_timing()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
               "(the ring's other devices are emulated on the one GPU)", file=sys.stderr)
@@ -489,14 +598,7 @@ def main():
         one_pass()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(compute)
-    for _ in range(args.steps):
-        one_pass()
-    t1.record(compute)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
 
@@ -515,15 +617,18 @@ def main():
     kern_ms = sum(step_ms)
     achieved = live_flops / (kern_ms * 1e-3) / 1e12
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
-    # copy / compute overlap per ring step: fraction of the copy staging step k+1 that ran
-    # while step k's kernel ran
-    overlap = []
+    # per staged step k: share of its copy that ran under step kernels, and the time (if
+    # any) the copy ran on past the end of step k-1's kernel
+    intervals = [(tm["step_begin_ms"][k], tm["step_end_ms"][k]) for k in range(N)
+                 if tm["step_begin_ms"][k] >= 0]
+    overlapped, exposed = [], []
     for k in range(1, N):
         cb, ce = tm["copy_begin_ms"][k], tm["copy_end_ms"][k]
-        sb, se = tm["step_begin_ms"][k - 1], tm["step_end_ms"][k - 1]
-        if cb < 0 or sb < 0 or ce <= cb:
+        se = tm["step_end_ms"][k - 1]
+        if cb < 0 or tm["step_begin_ms"][k - 1] < 0 or ce <= cb:
             continue
-        overlap.append(max(0.0, min(ce, se) - max(cb, sb)) / (ce - cb))
+        overlapped.append(overlap_fraction(cb, ce, intervals))
+        exposed.append(max(0.0, ce - se))
     kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
     copy_ms = [tm["copy_end_ms"][k] - tm["copy_begin_ms"][k] for k in range(1, N)
                if tm["copy_begin_ms"][k] >= 0]
@@ -536,6 +641,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "pass_ms": pass_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -555,7 +661,9 @@ def main():
         "staging": {"kv_bytes_per_step": kv_bytes,
                     "copy_ms": [round(x, 4) for x in copy_ms],
                     "copy_GBps": [round(2 * kv_bytes / (x * 1e-3) / 1e9, 1) for x in copy_ms if x > 0],
-                    "overlap_fraction_per_step": [round(x, 4) for x in overlap],
+                    "overlap_fraction_per_step": [round(x, 4) for x in overlapped],
+                    "exposed_ms_per_step": [round(x, 4) for x in exposed],
+                    "exposed_over_compute_band": exposure_band(sum(exposed), kern_ms),
                     "step_kernel_ms": [round(x, 4) for x in step_ms]},
     }
     if not args.no_cpu_baseline:

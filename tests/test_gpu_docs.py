@@ -182,3 +182,34 @@ def test_packed_bwd_full_size():
     announce(f"sum dK max abs {np.abs(dk_sum).max():.3e}; sum dV err {np.abs(dv_sum - do_sum).max():.3e}")
     assert np.abs(dk_sum).max() <= 2e-2 * np.sqrt(L)
     assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.sqrt(L)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_every_token_its_own_document(causal):
+    """One token per document: each row sees only itself, so O = its own V row (exactly) and
+    LSE = scale q.k of its own key (closed form, no oracle call)."""
+    N, L, h, n_kv, d, shard = 4, 256, 8, 2, 128, 1
+    bounds = np.arange(N * L + 1, dtype=np.int32)
+    for layout in LAYOUTS:
+        announce("one token per document", layout, "causal", causal)
+        inp = make_inputs(b=1, L=L, h=h, n_kv=n_kv, d=d, N=N, q_shard=shard, seed=111, dtype="bf16")
+        docs = gpu_docs([bounds], N=N, L=L, shard=shard, layout=layout)
+        o, lse = ra.ring_fwd(to_gpu(inp["q"], "bf16"), to_gpu(inp["k_all"], "bf16"),
+                             to_gpu(inp["v_all"], "bf16"), q_shard=shard, causal=causal,
+                             layout=layout, docs=docs)
+        torch.cuda.synchronize()
+        toks = shard_tokens(layout, N, L)
+        owner = np.empty(N * L, dtype=np.int64)
+        local = np.empty(N * L, dtype=np.int64)
+        for j in range(N):
+            owner[toks[j]] = j
+            local[toks[j]] = np.arange(L)
+        P = toks[shard]
+        grp = h // n_kv
+        v_self = np.stack([inp["v_all"][owner[p], 0, local[p]] for p in P])      # [L, n_kv, d]
+        k_self = np.stack([inp["k_all"][owner[p], 0, local[p]] for p in P])
+        want_o = np.repeat(v_self, grp, axis=1).astype(np.float64)               # [L, h, d]
+        s_self = np.einsum("thd,thd->ht", inp["q"][0].astype(np.float64),
+                           np.repeat(k_self, grp, axis=1).astype(np.float64)) / np.sqrt(d)
+        assert np.array_equal(f64(o)[0], want_o)
+        assert np.abs(f64(lse)[0] - s_self).max() <= 1e-3
