@@ -9,13 +9,15 @@
 // the running (O, LSE) of earlier ring steps (page 2, "FlashAttention Integration").
 //
 // Mapping onto CDNA4:
-//  * On gfx950 a wave's vector instructions do not run underneath its own matrix
-//    instructions, but the vector unit of a SIMD does run one wave's softmax while the
-//    matrix unit runs another wave's products.  So a workgroup is 8 wave64s, two per SIMD,
-//    in two groups that swap roles every half step (a "ping-pong"): while group 0 issues
-//    its matrix phase (P V of the previous key tile and Q K^T of the current one), group 1
-//    runs the softmax of its current tile, and the other way round in the next half step.
-//    A workgroup barrier separates the half steps.
+//  * On gfx950 the vector unit of a SIMD runs one wave's softmax while the matrix unit runs
+//    another wave's products.  A wave's own independent vector instructions also run under
+//    its matrix instructions, but its softmax is a chain of dependent instructions whose
+//    stalls only another wave can fill; measured, whole alternating phases take fewer
+//    cycles per tile than each wave interleaving its own softmax with its products.  So a
+//    workgroup is 8 wave64s, two per SIMD, in two groups that swap roles every half step (a
+//    "ping-pong"): while group 0 issues its matrix phase (P V of the previous key tile and
+//    Q K^T of the current one), group 1 runs the softmax of its current tile, and the other
+//    way round in the next half step.  A workgroup barrier separates the half steps.
 //  * Each wave owns 32 query rows of one head; the workgroup's waves share one KV head.
 //    With grouped-query attention the query heads of a KV group go to different waves
 //    (page 3, section 2: several query heads share one KV group), so every K/V tile staged
