@@ -91,6 +91,43 @@ def test_ring_fwd_rejects_small_workspace():
                                  None, None, None) == _lib.RA_ERR_INVALID_ARG
 
 
+def _no_hip_device():
+    """True when the HIP runtime sees no device at all (this container), so a call with
+    valid arguments fails at its first HIP call and never touches memory."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return False
+    n = ctypes.c_int(-1)
+    err = hip.hipGetDeviceCount(ctypes.byref(n))
+    return err != 0 or n.value == 0
+
+
+@pytest.mark.skipif(not _no_hip_device(), reason="needs a host without a GPU: the arguments are dummies")
+def test_hip_failure_is_reported_as_ra_err_hip():
+    """A HIP failure after validation comes back as RA_ERR_HIP with HIP's own text, from every
+    entry point that launches work (here forced by the absence of a device)."""
+    lib = _lib.lib()
+    p = _prob()
+    ws = lib.ra_ring_fwd_workspace(ctypes.byref(p))
+    calls = {
+        "ra_step_fwd": lambda: lib.ra_step_fwd(ctypes.byref(p), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None),
+        "ra_merge_lse": lambda: lib.ra_merge_lse(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None),
+        "ra_ring_fwd": lambda: lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                               None, None),
+        "ra_step_bwd": lambda: lib.ra_step_bwd(ctypes.byref(p), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, FAKE, FAKE, FAKE, None),
+        "ra_ring_bwd": lambda: lib.ra_ring_bwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, FAKE, FAKE, lib.ra_ring_bwd_workspace(ctypes.byref(p)),
+                                               None, None),
+    }
+    for name, call in calls.items():
+        assert call() == _lib.RA_ERR_HIP, name
+        detail = lib.ra_last_error()
+        assert detail and b"device" in detail.lower(), (name, detail)
+    assert b"HIP" in lib.ra_status_string(_lib.RA_ERR_HIP).upper()
+
+
 def test_workspace_size_is_two_kv_buffers_plus_fp32_accumulator():
     """Page 4, memory analysis: a device holds its own and one incoming KV block; here the
     two staging buffers (K and V each) plus the fp32 output accumulator of bf16 problems."""
