@@ -44,7 +44,8 @@ extern "C" {
 typedef int32_t ra_status;
 #define RA_OK 0
 #define RA_ERR_INVALID_ARG (-1) /* bad shape, index, enum, null or misaligned pointer   */
-#define RA_ERR_UNSUPPORTED (-2) /* valid problem with no kernel (e.g. bf16 with d != 128) */
+#define RA_ERR_UNSUPPORTED (-2) /* valid problem with no kernel (e.g. bf16 with d != 128, or a
+                                 bf16 K/V slice L*n_kv*d*2 of 2 GiB or more)               */
 #define RA_ERR_WORKSPACE (-3)   /* workspace smaller than ra_ring_{fwd,bwd}_workspace()  */
 #define RA_ERR_HIP (-4)         /* a HIP call or launch failed                            */
 

@@ -77,6 +77,11 @@ ra_status check_problem(const ra_problem* p) {
     return fail(RA_ERR_INVALID_ARG, "doc_begin / doc_end are not 4-byte aligned");
   if (p->dtype == RA_BF16 && p->d != 128)
     return fail(RA_ERR_UNSUPPORTED, "bf16 kernels support d = 128 only (got %d)", p->d);
+  // the bf16 kernels stage K/V rows by DMA through a buffer range of 32-bit byte offsets
+  // that must stay below 2^31 (larger offsets mark loads past the shard end)
+  if (p->dtype == RA_BF16 && (int64_t)p->L * p->n_kv * p->d * 2 >= ((int64_t)1 << 31))
+    return fail(RA_ERR_UNSUPPORTED, "one (batch, KV head) slice of K or V (L*n_kv*d*2 = %lld bytes) must stay below 2 GiB",
+                (long long)p->L * p->n_kv * p->d * 2);
   if (p->dtype == RA_F32 && p->d != 64 && p->d != 128)
     return fail(RA_ERR_UNSUPPORTED, "fp32 kernels support d = 64 or 128 (got %d)", p->d);
   return RA_OK;

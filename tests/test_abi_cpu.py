@@ -77,6 +77,18 @@ def test_step_fwd_rejects_bad_shards_and_pointers():
     assert lib.ra_step_fwd(None, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.RA_ERR_INVALID_ARG
 
 
+def test_bf16_kv_slice_limit():
+    """K/V rows are staged through 32-bit buffer offsets below 2^31: a (batch, KV head) slice of
+    2 GiB or more is refused before anything is enqueued, and the largest that fits is not."""
+    lib = _lib.lib()
+    big = _prob(L=1 << 20, n_kv=8, h=8, N=1)          # 2^20 * 8 * 128 * 2 = 2 GiB
+    assert lib.ra_step_fwd(ctypes.byref(big), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.RA_ERR_UNSUPPORTED
+    assert b"2 GiB" in lib.ra_last_error()
+    if _no_hip_device():                                # valid arguments reach the launch
+        fits = _prob(L=(1 << 20) - 64, n_kv=8, h=8, N=1)
+        assert lib.ra_step_fwd(ctypes.byref(fits), 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.RA_ERR_HIP
+
+
 def test_ring_fwd_rejects_small_workspace():
     lib = _lib.lib()
     p = _prob()
