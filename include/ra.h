@@ -196,6 +196,42 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t q_shard, const void* q, const
                       float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
                       ra_stream compute, ra_stream copy);
 
+/* ---- All-to-all sequence parallelism, one device's share (page 3, sections 4.2 and 7) ----
+ * The other way of spreading attention over N devices: each device starts with one shard
+ * of the sequence for every head, trades it in an all-to-all exchange for the whole
+ * sequence of h/N query heads and n_kv/N KV heads, runs one attention over the whole
+ * sequence, and sends each shard's rows of its heads back in a second exchange.  Needs h
+ * and n_kv to be multiples of N (the pages' divisibility constraint).
+ *
+ * ra_ulysses_fwd computes device head_group's share on one GPU, where the N devices'
+ * shards are resident: q_all [N][b][L][h][d], k_all and v_all [N][b][L][n_kv][d], shard j
+ * in its own local order under p->layout (as for ra_ring_fwd).  It writes query heads
+ * [head_group h/N, (head_group+1) h/N) of every shard: o_all [N][b][L][h][d] (dtype) and
+ * lse_all [N][b][h][L] (fp32); other heads are left untouched, so calling it for every head
+ * group fills the whole outputs, which equal ra_ring_fwd's for every shard.  The
+ * exchanges are copy kernels on `stream` (gather, then attention, then scatter).
+ * Workspace: ra_ulysses_fwd_workspace(p) bytes (the gathered Q, K, V of the head group, an
+ * fp32 output and the LSE of the whole sequence), 16-byte aligned; 0 if p is invalid for
+ * this path.  RA_ERR_INVALID_ARG if h or n_kv is not a multiple of N; RA_ERR_UNSUPPORTED
+ * with packed documents or where the whole-sequence problem (b, N L, h/N, n_kv/N, d) has
+ * no kernel. */
+size_t ra_ulysses_fwd_workspace(const ra_problem* p);
+ra_status ra_ulysses_fwd(const ra_problem* p, int32_t head_group, const void* q_all, const void* k_all,
+                         const void* v_all, void* o_all, float* lse_all, void* ws, size_t ws_bytes,
+                         ra_stream stream);
+
+/* ra_ulysses_fwd plus the time of its three parts (HIP events on `stream`, ms); waits for
+ * the call to finish before returning. */
+typedef struct ra_ulysses_timing {
+  float gather_ms;  /* first exchange: Q, K, V of the head group gathered                */
+  float attend_ms;  /* the attention over the whole sequence                             */
+  float scatter_ms; /* second exchange: O (converted to dtype) and LSE sent back          */
+  float total_ms;
+} ra_ulysses_timing;
+ra_status ra_ulysses_fwd_timed(const ra_problem* p, int32_t head_group, const void* q_all,
+                               const void* k_all, const void* v_all, void* o_all, float* lse_all,
+                               void* ws, size_t ws_bytes, ra_stream stream, ra_ulysses_timing* t);
+
 /* Host-only (no GPU work): number of (query, key) pairs shard q_shard may attend to in KV
  * shard kv_shard (or the whole sequence when kv_shard = -1), summed over the batch.  Useful
  * FLOPs of the forward are 4 * d * h * pairs (page 3, section 2: two GEMMs, 2 FLOPs per

@@ -15,6 +15,9 @@ Entry points (same names as the C-ABI, without the ``ra_`` prefix):
     step_bwd      one backward ring step (accumulates dQ, dK, dV)
     ring_bwd      the whole backward ring pass of one device
     allowed_pairs   host-side count of allowed (query, key) pairs (useful-FLOP accounting)
+    ulysses_fwd   one device's share of all-to-all sequence parallelism: whole-sequence
+                  attention for a group of h/N heads, exchanged in and out by copy kernels
+    ulysses_fwd_timed  ulysses_fwd plus the time of its gather, attention and scatter
 
 Tensor layouts (page 1, "Practical Implementation Patterns": batch, sequence, heads, dim):
     q, o [b, L, h, d];  k, v [b, L, n_kv, d];  k_all, v_all [N, b, L, n_kv, d];
@@ -27,10 +30,11 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, check
+from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, RaUlyssesTiming, check
 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
-           "bwd_preprocess", "step_bwd", "ring_bwd", "make_problem", "RaError", "library_path"]
+           "bwd_preprocess", "step_bwd", "ring_bwd", "ulysses_fwd", "ulysses_fwd_timed",
+           "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 _copy_streams: dict[int, torch.cuda.Stream] = {}
@@ -232,6 +236,54 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
         "total_ms": tm.total_ms,
     }
     return o, lse, timing
+
+
+def _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out):
+    N, b, L, h, d = q_all.shape
+    n_kv = k_all.shape[3]
+    _need(q_all, "q_all", (N, b, L, h, d), q_all.dtype)
+    _need(k_all, "k_all", (N, b, L, n_kv, d), q_all.dtype)
+    _need(v_all, "v_all", (N, b, L, n_kv, d), q_all.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q_all.dtype, scale=scale)
+    need = int(_lib.lib().ra_ulysses_fwd_workspace(ctypes.byref(p)))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_INVALID_ARG), "ra_ulysses_fwd_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q_all.device, dtype=torch.uint8)
+    o = out if out is not None else torch.zeros((N, b, L, h, d), device=q_all.device, dtype=q_all.dtype)
+    lse = lse_out if lse_out is not None else torch.full((N, b, h, L), float("-inf"),
+                                                         device=q_all.device, dtype=torch.float32)
+    _need(o, "o_all", (N, b, L, h, d), q_all.dtype)
+    _need(lse, "lse_all", (N, b, h, L), torch.float32)
+    return p, workspace, o, lse
+
+
+def ulysses_fwd(q_all, k_all, v_all, *, head_group, causal=False, layout="contiguous", scale=None,
+                stream=None, workspace=None, out=None, lse_out=None):
+    """Device head_group's share of all-to-all sequence parallelism: q_all [N, b, L, h, d],
+    k_all, v_all [N, b, L, n_kv, d] (every shard, each in its own layout order).  Writes query
+    heads [head_group h/N, (head_group+1) h/N) of every shard into out [N, b, L, h, d]
+    (q's dtype) and lse_out [N, b, h, L] fp32 (allocated if None: zeros and -inf elsewhere)
+    and returns them; call it for every head group to fill them."""
+    p, ws, o, lse = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    check(_lib.lib().ra_ulysses_fwd(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all),
+                                    _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
+          "ra_ulysses_fwd")
+    return o, lse
+
+
+def ulysses_fwd_timed(q_all, k_all, v_all, *, head_group, causal=False, layout="contiguous",
+                      scale=None, stream=None, workspace=None, out=None, lse_out=None):
+    """ulysses_fwd plus the time of its parts: returns (o, lse, dict with gather_ms,
+    attend_ms, scatter_ms, total_ms).  Synchronises."""
+    p, ws, o, lse = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    tm = RaUlyssesTiming()
+    check(_lib.lib().ra_ulysses_fwd_timed(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all),
+                                          _ptr(v_all), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                          _stream(stream), ctypes.byref(tm)), "ra_ulysses_fwd_timed")
+    return o, lse, {"gather_ms": tm.gather_ms, "attend_ms": tm.attend_ms,
+                    "scatter_ms": tm.scatter_ms, "total_ms": tm.total_ms}
 
 
 def bwd_preprocess(o, dout, *, stream=None):

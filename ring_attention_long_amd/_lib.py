@@ -41,6 +41,11 @@ class RaRingTiming(ctypes.Structure):
     ]
 
 
+class RaUlyssesTiming(ctypes.Structure):
+    _fields_ = [("gather_ms", ctypes.c_float), ("attend_ms", ctypes.c_float),
+                ("scatter_ms", ctypes.c_float), ("total_ms", ctypes.c_float)]
+
+
 # (name, restype, argtypes) of every exported entry point, in include/ra.h order.
 _P = ctypes.POINTER(RaProblem)
 _V = ctypes.c_void_p
@@ -58,6 +63,10 @@ SIGNATURES = [
     ("ra_step_bwd", _I, [_P, _I, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     ("ra_ring_bwd_workspace", _S, [_P]),
     ("ra_ring_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
+    ("ra_ulysses_fwd_workspace", _S, [_P]),
+    ("ra_ulysses_fwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V]),
+    ("ra_ulysses_fwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V,
+                                  ctypes.POINTER(RaUlyssesTiming)]),
     ("ra_allowed_pairs", ctypes.c_int64, [_P, _I, _I]),
     ("ra_allowed_pairs_packed", ctypes.c_int64, [_P, _I, _I, _V, _V]),
     ("ra_document_ranges", _I, [_P, _I, _V, _I, _V, _V]),

@@ -7,7 +7,10 @@ the per-step example) and page 1 ("Overlapping Arithmetic and Communication Rati
   * with a causal mask only allowed pairs count: 4 h d FLOPs per allowed (query, key) pair;
   * KV bytes received per step: 2 b L n_kv d p (K and V, p bytes per element);
   * step intensity I_step = (h / n_kv) * L and whole-layer intensity
-    I = (h / n_kv) * S / (N - 1) FLOPs per received byte.
+    I = (h / n_kv) * S / (N - 1) FLOPs per received byte;
+  * all-to-all sequence parallelism (page 3, sections 4.2 and 7): per device and layer the
+    two exchanges move (N-1)/N of its S/N slice of Q and O (h heads) and K and V (n_kv
+    heads), and the attention work is 4 b S^2 (h/N) d, the same as a ring device's.
 """
 from __future__ import annotations
 
@@ -41,3 +44,19 @@ def merge_bytes(b: int, L: int, h: int, d: int) -> int:
     """HBM bytes of one standalone merge: read O_acc, O_part, write O_acc (fp32) plus the
     same three passes over the LSE rows."""
     return 3 * 4 * b * L * h * d + 3 * 4 * b * h * L
+
+
+def ring_kv_bytes_per_pass(b: int, S: int, N: int, n_kv: int, d: int, elem_bytes: int) -> int:
+    """KV bytes one device receives over a forward ring pass: N-1 shards (its own is local)."""
+    return (N - 1) * kv_bytes_per_step(b, S // N, n_kv, d, elem_bytes)
+
+
+def ulysses_bytes_per_device(b: int, S: int, N: int, h: int, n_kv: int, d: int, elem_bytes: int) -> float:
+    """Bytes one device receives in the two all-to-all exchanges of one layer: (N-1)/N of an
+    S/N slice of Q and O (h heads each) and of K and V (n_kv heads each)."""
+    return (N - 1) / N * b * (S / N) * (2 * h + 2 * n_kv) * d * elem_bytes
+
+
+def ulysses_flops_noncausal(b: int, S: int, N: int, h: int, d: int) -> int:
+    """Attention work of one device after the exchange: whole sequence, h/N heads."""
+    return 4 * b * S * S * (h // N) * d

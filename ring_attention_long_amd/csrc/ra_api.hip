@@ -281,6 +281,109 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   return RA_OK;
 }
 
+// ---- all-to-all sequence parallelism (page 3, sections 4.2 and 7) -----------------------
+// Device g of N holds, after the first exchange, the whole sequence (S = N L tokens) of
+// query heads [g h/N, (g+1) h/N) and KV heads [g n_kv/N, (g+1) n_kv/N): the same query
+// head to KV head map as the full problem, since h/N over n_kv/N is h / n_kv.  It runs one
+// attention over the whole sequence in global position order, then sends each shard's rows
+// of its heads back.
+ra_status check_ulysses(const ra_problem* p) {
+  RA_TRY(check_problem(p));
+  if (p->doc_begin) return fail(RA_ERR_UNSUPPORTED, "packed documents are not supported by the all-to-all path");
+  if (p->h % p->N || p->n_kv % p->N)
+    return fail(RA_ERR_INVALID_ARG, "the all-to-all path splits heads over the N devices: h=%d and n_kv=%d must be "
+                "multiples of N=%d", p->h, p->n_kv, p->N);
+  if (p->b > 65535) return fail(RA_ERR_UNSUPPORTED, "batch %d above 65535", p->b);
+  return RA_OK;
+}
+
+// The attention problem one device solves after the first exchange.
+ra_problem ulysses_local(const ra_problem* p) {
+  ra_problem q = *p;
+  q.L = p->N * p->L;
+  q.h = p->h / p->N;
+  q.n_kv = p->n_kv / p->N;
+  q.N = 1;
+  q.layout = RA_LAYOUT_CONTIGUOUS;
+  q.scale = effective_scale(p);
+  q.doc_begin = q.doc_end = nullptr;
+  return q;
+}
+
+struct UlyssesWs {
+  size_t q, kv, o, lse, total;
+};
+UlyssesWs ulysses_ws(const ra_problem* p) {
+  const size_t S = (size_t)p->N * p->L, es = elem_size(p);
+  UlyssesWs w;
+  w.q = align_up((size_t)p->b * S * (p->h / p->N) * p->d * es, 256);
+  w.kv = align_up((size_t)p->b * S * (p->n_kv / p->N) * p->d * es, 256);
+  w.o = align_up((size_t)p->b * S * (p->h / p->N) * p->d * 4, 256);
+  w.lse = align_up((size_t)p->b * (p->h / p->N) * S * 4, 256);
+  w.total = w.q + 2 * w.kv + w.o + w.lse;
+  return w;
+}
+
+ra_status ulysses_fwd_impl(const ra_problem* p, int32_t group, const void* q_all, const void* k_all,
+                           const void* v_all, void* o_all, float* lse_all, void* ws, size_t ws_bytes,
+                           ra_stream stream, ra_ulysses_timing* tm) {
+  RA_TRY(check_ulysses(p));
+  RA_TRY(check_shard(p, group, "head_group"));
+  const ra_problem lp = ulysses_local(p);
+  RA_TRY(check_problem(&lp));
+  RA_TRY(check_ptr(q_all, "q_all", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o_all, "o_all", 16));
+  RA_TRY(check_ptr(lse_all, "lse_all", 4));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const UlyssesWs w = ulysses_ws(p);
+  if (ws_bytes < w.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+
+  char* base = (char*)ws;
+  void* q_g = base;
+  void* k_g = base + w.q;
+  void* v_g = base + w.q + w.kv;
+  float* o_g = (float*)(base + w.q + 2 * w.kv);
+  float* lse_g = (float*)(base + w.q + 2 * w.kv + w.o);
+  const hipStream_t s = (hipStream_t)stream;
+  const int Hg = p->h / p->N, Kg = p->n_kv / p->N, es = (int)elem_size(p);
+
+  Events ev;
+  hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr;
+  hipError_t e;
+  if (tm) {
+    if ((e = ev.make(&t0, true)) != hipSuccess || (e = ev.make(&t1, true)) != hipSuccess ||
+        (e = ev.make(&t2, true)) != hipSuccess || (e = ev.make(&t3, true)) != hipSuccess)
+      return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventRecord(t0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if ((e = ra::launch_ulysses_gather(q_g, q_all, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather(k_g, k_all, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather(v_g, v_all, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d, es, s)) !=
+          hipSuccess)
+    return hip_fail(e, "gather kernel launch");
+  if (tm && (e = hipEventRecord(t1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const ra::StepArgs a = step_args(&lp, 0, 0, q_g, k_g, v_g, o_g, lse_g);
+  if ((e = launch_step(&lp, a, ra::MODE_PART, s)) != hipSuccess) return hip_fail(e, "step kernel launch");
+  if (tm && (e = hipEventRecord(t2, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = ra::launch_ulysses_scatter(o_all, lse_all, o_g, lse_g, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg,
+                                      p->d, p->dtype, s)) != hipSuccess)
+    return hip_fail(e, "scatter kernel launch");
+  if (tm) {
+    if ((e = hipEventRecord(t3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipEventSynchronize(t3)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    (void)hipEventElapsedTime(&tm->gather_ms, t0, t1);
+    (void)hipEventElapsedTime(&tm->attend_ms, t1, t2);
+    (void)hipEventElapsedTime(&tm->scatter_ms, t2, t3);
+    (void)hipEventElapsedTime(&tm->total_ms, t0, t3);
+  }
+  return RA_OK;
+}
+
 ra_status check_bwd_problem(const ra_problem* p) {
   RA_TRY(check_problem(p));
   if (p->dtype != RA_BF16 || p->d != 128)
@@ -519,6 +622,26 @@ int64_t ra_allowed_pairs_packed(const ra_problem* p, int32_t q_shard, int32_t kv
       }
     }
   return total;
+}
+
+size_t ra_ulysses_fwd_workspace(const ra_problem* p) {
+  if (check_ulysses(p) != RA_OK) return 0;
+  const ra_problem lp = ulysses_local(p);
+  if (check_problem(&lp) != RA_OK) return 0;
+  return ulysses_ws(p).total;
+}
+
+ra_status ra_ulysses_fwd(const ra_problem* p, int32_t head_group, const void* q_all, const void* k_all,
+                         const void* v_all, void* o_all, float* lse_all, void* ws, size_t ws_bytes,
+                         ra_stream stream) {
+  return ulysses_fwd_impl(p, head_group, q_all, k_all, v_all, o_all, lse_all, ws, ws_bytes, stream, nullptr);
+}
+
+ra_status ra_ulysses_fwd_timed(const ra_problem* p, int32_t head_group, const void* q_all, const void* k_all,
+                               const void* v_all, void* o_all, float* lse_all, void* ws, size_t ws_bytes,
+                               ra_stream stream, ra_ulysses_timing* t) {
+  if (!t) return fail(RA_ERR_INVALID_ARG, "timing is NULL");
+  return ulysses_fwd_impl(p, head_group, q_all, k_all, v_all, o_all, lse_all, ws, ws_bytes, stream, t);
 }
 
 ra_status ra_document_ranges(const ra_problem* p, int32_t shard, const int32_t* bounds,

@@ -25,6 +25,29 @@ __host__ __device__ inline int64_t global_pos(int layout, int N, int L, int p, i
   return (int64_t)p * L + t;
 }
 
+// Inverse of global_pos: the shard j and local index t holding global position P
+// (0 <= P < N L).
+__host__ __device__ inline void owner_of(int layout, int N, int L, int64_t P, int& j, int& t) {
+  if (layout == RA_LAYOUT_STRIPED) {
+    j = (int)(P % N);
+    t = (int)(P / N);
+  } else if (layout == RA_LAYOUT_ZIGZAG) {
+    const int C = L / 2;
+    const int c = (int)(P / C);
+    const int off = (int)(P - (int64_t)c * C);
+    if (c < N) {
+      j = c;
+      t = off;
+    } else {
+      j = 2 * N - 1 - c;
+      t = C + off;
+    }
+  } else {
+    j = (int)(P / L);
+    t = (int)(P - (int64_t)j * L);
+  }
+}
+
 __host__ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
@@ -165,6 +188,16 @@ hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
 hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n_elems,
                            hipStream_t s);
 hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s);
+// Head-group exchange of the all-to-all sequence-parallel scheme, one device's side.
+// Gather: rows [b][S][Hg][d] (element bytes es) of heads head0 .. head0+Hg-1, in global
+// position order, from the N shards src_all [N][b][L][H][d] in their own layout order.
+hipError_t launch_ulysses_gather(void* dst, const void* src_all, int b, int L, int N, int layout,
+                                 int H, int Hg, int head0, int d, int es, hipStream_t s);
+// Scatter: fp32 rows [b][S][Hg][d] back to heads head0 .. of the shards' dst_all
+// [N][b][L][H][d] (converted to dtype), and LSE [b][Hg][S] to lse_all [N][b][H][L].
+hipError_t launch_ulysses_scatter(void* dst_all, float* lse_all, const float* o, const float* lse,
+                                  int b, int L, int N, int layout, int H, int Hg, int head0, int d,
+                                  int dtype, hipStream_t s);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
                                  hipStream_t s);
 // Adds this step's contributions: dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32).

@@ -1,0 +1,93 @@
+"""CPU checks of the all-to-all sequence-parallel path (page 3, sections 4.2 and 7): its byte
+and work model against the page's printed figures, and the C-ABI's validation of it.  No
+kernel is launched."""
+import ctypes
+
+import pytest
+
+from ring_attention_long_amd import _lib, accounting
+from test_abi_cpu import FAKE, _no_hip_device, _prob
+
+
+def test_alltoall_bytes_match_page3(golden):
+    """Page 3, section 4.2: with GQA (h = 32, n_kv = 8) one device receives ~0.587 GB in the
+    two exchanges against the ring's 0.94 GB (ratio ~0.63); with MHA (n_kv = h) the
+    exchanges come to 0.94 GB."""
+    g = golden("alltoall_accounting.json")
+    S, N, b, h, n_kv, d, p = g["S"], g["N"], g["b"], g["h"], g["n_kv"], g["d"], g["bytes_per_element"]
+    u = accounting.ulysses_bytes_per_device(b, S, N, h, n_kv, d, p)
+    r = accounting.ring_kv_bytes_per_pass(b, S, N, n_kv, d, p)
+    assert u / 1e9 == pytest.approx(g["ulysses_gb_gqa"], abs=0.0005)
+    assert r / 1e9 == pytest.approx(g["ring_gb_gqa"], abs=0.005)
+    # exactly (2h + 2 n_kv) / (2 N n_kv) = 0.625; the page rounds 0.587 / 0.94 = 0.6245 to 0.63
+    assert u / r == pytest.approx(g["ulysses_over_ring_gqa"], abs=0.01)
+    assert accounting.ulysses_bytes_per_device(b, S, N, h, h, d, p) / 1e9 == pytest.approx(g["ulysses_gb_mha"], abs=0.005)
+    # the ring's bytes scale with n_kv, the exchanges' with h + n_kv
+    assert accounting.ring_kv_bytes_per_pass(b, S, N, h, d, p) == 4 * r
+
+
+def test_alltoall_work_equals_ring_work_per_device():
+    """Page 3, section 7: a device's attention after the exchange, 4 b S^2 (h/N) d, equals a
+    ring device's N steps of 4 b L S h d (L = S/N)."""
+    for (b, S, N, h, d) in ((1, 262144, 8, 32, 128), (2, 4096, 4, 8, 64)):
+        L = S // N
+        ring = N * 4 * b * L * L * h * d
+        assert accounting.ulysses_flops_noncausal(b, S, N, h, d) == ring
+
+
+def test_ulysses_workspace_size():
+    """Gathered Q (h/N heads) and K, V (n_kv/N heads) of the whole sequence in the input
+    dtype, an fp32 output and the fp32 LSE, each padded to 256 bytes."""
+    lib = _lib.lib()
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for dtype, es in ((1, 2), (0, 4)):
+        p = _prob(b=2, L=100, h=8, n_kv=4, N=4, dtype=dtype, layout=1)
+        S = 400
+        want = (pad(2 * S * 2 * 128 * es) + 2 * pad(2 * S * 1 * 128 * es) + pad(2 * S * 2 * 128 * 4)
+                + pad(2 * 2 * S * 4))
+        assert lib.ra_ulysses_fwd_workspace(ctypes.byref(p)) == want
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=6, n_kv=2, N=4), _lib.RA_ERR_INVALID_ARG),      # h not a multiple of N
+    (dict(h=8, n_kv=2, N=4), _lib.RA_ERR_INVALID_ARG),      # n_kv not a multiple of N
+    (dict(d=96), _lib.RA_ERR_UNSUPPORTED),
+    (dict(layout=2, L=127), _lib.RA_ERR_INVALID_ARG),
+])
+def test_ulysses_rejects_bad_problems(kw, status):
+    lib = _lib.lib()
+    base = dict(h=8, n_kv=4, N=4)
+    base.update(kw)
+    p = _prob(**base)
+    assert lib.ra_ulysses_fwd_workspace(ctypes.byref(p)) == 0
+    st = lib.ra_ulysses_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+    assert lib.ra_last_error()
+
+
+def test_ulysses_rejects_bad_arguments():
+    lib = _lib.lib()
+    p = _prob(h=8, n_kv=4, N=4)
+    need = lib.ra_ulysses_fwd_workspace(ctypes.byref(p))
+    assert need > 0
+    call = lambda g, q=FAKE, ws=need, lse=FAKE: lib.ra_ulysses_fwd(  # noqa: E731
+        ctypes.byref(p), g, q, FAKE, FAKE, FAKE, lse, FAKE, ws, None)
+    assert call(4) == _lib.RA_ERR_INVALID_ARG and b"head_group" in lib.ra_last_error()
+    assert call(-1) == _lib.RA_ERR_INVALID_ARG
+    assert call(0, q=None) == _lib.RA_ERR_INVALID_ARG and b"q_all is NULL" in lib.ra_last_error()
+    assert call(0, q=ctypes.c_void_p(0x10008)) == _lib.RA_ERR_INVALID_ARG
+    assert call(0, ws=need - 1) == _lib.RA_ERR_WORKSPACE
+    tm = _lib.RaUlyssesTiming()
+    assert lib.ra_ulysses_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None,
+                                    None) == _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_ulysses_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None,
+                                    ctypes.byref(tm)) == _lib.RA_ERR_WORKSPACE
+    # packed documents are not part of this path
+    pd = _prob(h=8, n_kv=4, N=4)
+    pd.doc_begin = pd.doc_end = FAKE.value
+    assert lib.ra_ulysses_fwd_workspace(ctypes.byref(pd)) == 0
+    assert lib.ra_ulysses_fwd(ctypes.byref(pd), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == \
+        _lib.RA_ERR_UNSUPPORTED
+    if _no_hip_device():                      # valid arguments reach the first launch
+        assert call(3) == _lib.RA_ERR_HIP
+        assert b"device" in lib.ra_last_error().lower()
