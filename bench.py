@@ -53,6 +53,15 @@ BWD_WORKLOADS = {
                               "bf16, shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
                               "striped", True, 0, 1005),
 }
+# all-to-all sequence parallelism (page 3, sections 4.2 and 7): one device's share, the same
+# sequence and heads as the ring workloads; the last field is the device (head group)
+ULYSSES_WORKLOADS = {
+    "ulysses_striped_causal_32k": ("ulysses_fwd striped causal, S=262144 N=8 L=32768 h=32 n_kv=8 "
+                                   "d=128 bf16, head group 0 (4 query heads, 1 KV head)",
+                                   dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "striped", True, 0, 1007),
+}
+ULYSSES_METRIC = ("all-to-all sequence-parallel attention TFLOP/s (bf16, causal), one device's share, "
+                  "and % of MI355X MFMA peak")
 # packed-document workloads (page 3, section 5): the same shapes with documents of lognormal
 # length packed into the window; value counts only pairs inside a document
 WORKLOADS["packed_striped_causal_32k"] = (
@@ -389,6 +398,90 @@ def run_backward(args):
     print(json.dumps(result), flush=True)
 
 
+def run_ulysses(args):
+    import torch
+
+    import ring_attention_long_amd as ra
+    import synth
+    from ring_attention_long_amd import accounting
+
+    desc, cfg, layout, causal, group, seed = ULYSSES_WORKLOADS[args.workload]
+    b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
+    S = N * L
+    log(f"[bench] workload {args.workload}: {desc}")
+    q_np = np.stack([synth.normal((b, L, h, d), seed=seed, name="q", shard=j) for j in range(N)])
+    base = synth.shard_inputs(**cfg, q_shard=0, seed=seed, dtype="bf16")
+    dev = torch.device("cuda:0")
+    q_all = torch.from_numpy(q_np).to(dev, torch.bfloat16)
+    k_all = torch.from_numpy(base["k_all"]).to(dev, torch.bfloat16)
+    v_all = torch.from_numpy(base["v_all"]).to(dev, torch.bfloat16)
+    o_all = torch.zeros((N, b, L, h, d), device=dev, dtype=torch.bfloat16)
+    lse_all = torch.full((N, b, h, L), float("-inf"), device=dev, dtype=torch.float32)
+    ws = torch.empty(ra.ulysses_workspace_bytes(q_all, k_all, causal=causal, layout=layout), device=dev,
+                     dtype=torch.uint8)
+    # the device's work: every allowed pair of the whole sequence, for its h/N heads
+    pairs = sum(ra.allowed_pairs(b=b, L=L, N=N, q_shard=j, causal=causal, layout=layout) for j in range(N))
+    flops = accounting.flops_from_pairs(pairs, h // N, d)
+    compute = torch.cuda.current_stream()
+
+    def one_pass():
+        ra.ulysses_fwd(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout, workspace=ws,
+                       out=o_all, lse_out=lse_all)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+    parts = [ra.ulysses_fwd_timed(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout,
+                                  workspace=ws, out=o_all, lse_out=lse_all)[2] for _ in range(3)]
+    tm = {k: float(np.median([t[k] for t in parts])) for k in parts[0]}
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    achieved = flops / (tm["attend_ms"] * 1e-3) / 1e12
+    es, hg, kg = 2, h // N, n_kv // N
+    gather_bytes = 2 * b * S * (hg + 2 * kg) * d * es             # read and write
+    scatter_bytes = b * S * hg * d * (4 + es) + 2 * b * hg * S * 4  # fp32 O in, dtype O out, LSE
+    a2a = accounting.ulysses_bytes_per_device(b, S, N, h, n_kv, d, es)
+    ring = accounting.ring_kv_bytes_per_pass(b, S, N, n_kv, d, es)
+    result = {
+        "metric": ULYSSES_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "pass_ms": pass_stats,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) bf16 Q/K/V from seeded numpy PCG64",
+        "config": {"workload": desc, "S": S, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv, "d": d,
+                   "layout": layout, "causal": causal, "head_group": group,
+                   "useful_tflop_per_pass": round(flops / 1e12, 4),
+                   "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "step_fwd_bf16_kernel<MODE_PART> over the whole sequence",
+                     "launches": 1, "avg_launch_ms": round(tm["attend_ms"], 4)},
+        "exchange": {"gather_ms": round(tm["gather_ms"], 4), "scatter_ms": round(tm["scatter_ms"], 4),
+                     "gather_GBps": round(gather_bytes / (tm["gather_ms"] * 1e-3) / 1e9, 1),
+                     "scatter_GBps": round(scatter_bytes / (tm["scatter_ms"] * 1e-3) / 1e9, 1),
+                     "alltoall_bytes_per_device": int(a2a), "ring_kv_bytes_per_pass": int(ring),
+                     "alltoall_xgmi_model_ms": round(a2a / (N - 1) / (XGMI_LINK_GBPS * 1e9) * 1e3, 4),
+                     "ring_xgmi_model_ms_per_step": round(ring / (N - 1) / (XGMI_LINK_GBPS * 1e9) * 1e3, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        inp = {"q": q_np[0], "k_all": base["k_all"], "v_all": base["v_all"]}
+        cb = cpu_baseline(inp, cfg, layout, causal, 0, args.cpu_budget)
+        cb["sample"] += "; the same rows and keys a device of this scheme attends for its heads"
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
 def run_sweep(args):
     """Where the time goes across sizes and shards (timing only: inputs are seeded
     torch.randn bf16 on the GPU; attention time does not depend on the values)."""
@@ -538,7 +631,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS) + sorted(ULYSSES_WORKLOADS))
     ap.add_argument("--oracle-timing", action="store_true",
                     help="CPU only: time the fp64 oracle on each configuration (full or a bounded "
                          "sample, extrapolated) and describe the host")
@@ -564,6 +658,8 @@ def main():
         return run_sweep(args)
     if args.workload in BWD_WORKLOADS:
         return run_backward(args)
+    if args.workload in ULYSSES_WORKLOADS:
+        return run_ulysses(args)
 
     import torch
 

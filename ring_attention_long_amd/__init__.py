@@ -238,6 +238,15 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
     return o, lse, timing
 
 
+def ulysses_workspace_bytes(q_all, k_all, *, causal=False, layout="contiguous", scale=None) -> int:
+    """Workspace of ulysses_fwd for q_all [N, b, L, h, d], k_all [N, b, L, n_kv, d] (0 if the
+    problem is not valid for the all-to-all path)."""
+    N, b, L, h, d = q_all.shape
+    p = make_problem(b=b, L=L, h=h, n_kv=k_all.shape[3], d=d, N=N, causal=causal, layout=layout,
+                     dtype=q_all.dtype, scale=scale)
+    return int(_lib.lib().ra_ulysses_fwd_workspace(ctypes.byref(p)))
+
+
 def _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out):
     N, b, L, h, d = q_all.shape
     n_kv = k_all.shape[3]
