@@ -53,6 +53,14 @@ BWD_WORKLOADS = {
                               "bf16, shard 0", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8),
                               "striped", True, 0, 1005),
 }
+# the other gradient schedule (page 1, "The Backward Pass and Gradient Exchange"): keys and
+# values stay, the query shards pass by; the last field is the device (its KV shard)
+BWD_STATIONARY_WORKLOADS = {
+    "bwd_kv_stationary_striped_causal_8k": ("ring_bwd_kv_stationary striped causal, S=65536 N=8 L=8192 "
+                                            "h=32 n_kv=8 d=128 bf16, KV shard 0",
+                                            dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8), "striped", True, 0,
+                                            1005),
+}
 # all-to-all sequence parallelism (page 3, sections 4.2 and 7): one device's share, the same
 # sequence and heads as the ring workloads; the last field is the device (head group)
 ULYSSES_WORKLOADS = {
@@ -398,6 +406,94 @@ def run_backward(args):
     print(json.dumps(result), flush=True)
 
 
+def run_backward_stationary(args):
+    import torch
+
+    import ring_attention_long_amd as ra
+    import synth
+    from ring_attention_long_amd import accounting
+
+    desc, cfg, layout, causal, ks, seed = BWD_STATIONARY_WORKLOADS[args.workload]
+    b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
+    log(f"[bench] workload {args.workload}: {desc}")
+    dev = torch.device("cuda:0")
+    host = {name: np.stack([synth.normal(shape, seed=seed, name=name, shard=j) for j in range(N)])
+            for name, shape in (("q", (b, L, h, d)), ("do", (b, L, h, d)), ("k", (b, L, n_kv, d)),
+                                ("v", (b, L, n_kv, d)))}
+    q_all, dout_all, k_all, v_all = (torch.from_numpy(host[n]).to(dev, torch.bfloat16) for n in ("q", "do", "k", "v"))
+    # what every home device holds before the backward: its shard's O, LSE and D
+    lse_l, delta_l, o_l = [], [], []
+    for i in range(N):
+        o, lse = ra.ring_fwd(q_all[i].contiguous(), k_all, v_all, q_shard=i, causal=causal, layout=layout)
+        o_l.append(o)
+        lse_l.append(lse)
+        delta_l.append(ra.bwd_preprocess(o, dout_all[i].contiguous()))
+    lse_all, delta_all = torch.stack(lse_l), torch.stack(delta_l)
+    k, v = k_all[ks].contiguous(), v_all[ks].contiguous()
+    out = (torch.empty((N, b, L, h, d), device=dev, dtype=torch.float32),
+           torch.empty((b, L, n_kv, d), device=dev, dtype=torch.float32),
+           torch.empty((b, L, n_kv, d), device=dev, dtype=torch.float32))
+    pairs = sum(ra.allowed_pairs(b=b, L=L, N=N, q_shard=i, kv_shard=ks, causal=causal, layout=layout)
+                for i in range(N))
+    flops = 10.0 * h * d * pairs
+    compute = torch.cuda.current_stream()
+
+    def one_pass():
+        ra.ring_bwd_kv_stationary(k, v, q_all, dout_all, lse_all, delta_all, kv_shard=ks, causal=causal,
+                                  layout=layout, out=out)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+    # the key/value-rotating schedule of device ks on the same box, for comparison
+    rq = q_all[ks].contiguous()
+    rout = (torch.empty((b, L, h, d), device=dev, dtype=torch.float32),
+            torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32),
+            torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32))
+    rot = lambda: ra.ring_bwd(rq, k_all, v_all, o_l[ks], dout_all[ks].contiguous(), lse_l[ks], q_shard=ks,  # noqa: E731
+                              causal=causal, layout=layout, out=rout)
+    rot()
+    torch.cuda.synchronize()
+    rot_ms, _ = timed_passes(rot, args.steps, compute)
+    rot_pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=ks, causal=causal, layout=layout)
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    bytes_rot = accounting.bwd_bytes_per_step_kv_rotating(b, L, n_kv, d, 2)
+    bytes_sta = accounting.bwd_bytes_per_step_kv_stationary(b, L, h, d, 2)
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "pass_ms": pass_stats,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) bf16 Q/K/V/dO from seeded numpy PCG64",
+        "config": {"workload": desc, "S": N * L, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv, "d": d,
+                   "layout": layout, "causal": causal, "kv_shard": ks,
+                   "useful_tflop_per_pass": round(flops / 1e12, 4),
+                   "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        "schedules": {
+            "kv_rotating_pass_ms": round(rot_ms, 4),
+            "kv_rotating_tflops": round(10.0 * h * d * rot_pairs / (rot_ms * 1e-3) / 1e12, 2),
+            "bytes_per_step_kv_rotating": bytes_rot, "bytes_per_step_kv_stationary": bytes_sta,
+            "xgmi_model_ms_per_step_kv_rotating": round(bytes_rot / (XGMI_LINK_GBPS * 1e9) * 1e3, 4),
+            "xgmi_model_ms_per_step_kv_stationary": round(bytes_sta / (XGMI_LINK_GBPS * 1e9) * 1e3, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        inp = {"q": host["q"][0], "k_all": host["k"], "v_all": host["v"], "dout": host["do"][0]}
+        result["cpu_baseline"] = cpu_baseline_bwd(inp, cfg, layout, causal, 0, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def run_ulysses(args):
     import torch
 
@@ -632,7 +728,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS) + sorted(ULYSSES_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS) + sorted(BWD_STATIONARY_WORKLOADS)
+                    + sorted(ULYSSES_WORKLOADS))
     ap.add_argument("--oracle-timing", action="store_true",
                     help="CPU only: time the fp64 oracle on each configuration (full or a bounded "
                          "sample, extrapolated) and describe the host")
@@ -660,6 +757,8 @@ def main():
         return run_backward(args)
     if args.workload in ULYSSES_WORKLOADS:
         return run_ulysses(args)
+    if args.workload in BWD_STATIONARY_WORKLOADS:
+        return run_backward_stationary(args)
 
     import torch
 

@@ -196,6 +196,26 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t q_shard, const void* q, const
                       float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
                       ra_stream compute, ra_stream copy);
 
+/* ra_ring_bwd_kv_stationary — the other gradient schedule (page 1, "The Backward Pass and
+ * Gradient Exchange": output gradients circulate in reverse ring order while keys and
+ * values stay where they are): device kv_shard keeps its k, v [b][L][n_kv][d] and, at step
+ * s, holds query shard (kv_shard + s) mod N with what its gradients need, Q, dO, the
+ * forward's LSE and D = rowsum(dO * O), each computed on its home device:
+ *   q_all, dout_all [N][b][L][h][d] (dtype), lse_all, delta_all [N][b][h][L] (fp32).
+ * Writes dk, dv [b][L][n_kv][d] (this KV shard's complete gradients) and dq_all
+ * [N][b][L][h][d] (this device's contributions to every shard's dQ; on a real ring each
+ * travels with its queries back home), all fp32, overwriting them.  The incoming query
+ * shard is staged into the idle half of a double buffer on `copy` while the current step
+ * computes, as in ra_ring_fwd; steps with no allowed pair are skipped.  Summing dq_all over
+ * all N devices gives the same dQ as ra_ring_bwd.  bf16, d = 128; no packed documents
+ * (RA_ERR_UNSUPPORTED: their bounds describe one query shard's rows).  Workspace:
+ * ra_ring_bwd_kv_stationary_workspace(p) bytes (two staging buffers), 0 if p is invalid. */
+size_t ra_ring_bwd_kv_stationary_workspace(const ra_problem* p);
+ra_status ra_ring_bwd_kv_stationary(const ra_problem* p, int32_t kv_shard, const void* k, const void* v,
+                                    const void* q_all, const void* dout_all, const float* lse_all,
+                                    const float* delta_all, float* dq_all, float* dk, float* dv, void* ws,
+                                    size_t ws_bytes, ra_stream compute, ra_stream copy);
+
 /* ---- All-to-all sequence parallelism, one device's share (page 3, sections 4.2 and 7) ----
  * The other way of spreading attention over N devices: each device starts with one shard
  * of the sequence for every head, trades it in an all-to-all exchange for the whole

@@ -14,6 +14,8 @@ Entry points (same names as the C-ABI, without the ``ra_`` prefix):
     bwd_preprocess  delta = rowsum(dO * O)
     step_bwd      one backward ring step (accumulates dQ, dK, dV)
     ring_bwd      the whole backward ring pass of one device
+    ring_bwd_kv_stationary  the other gradient schedule: keys and values stay, the query
+                  shards (Q, dO, LSE, D) pass by and dQ contributions travel with them
     allowed_pairs   host-side count of allowed (query, key) pairs (useful-FLOP accounting)
     ulysses_fwd   one device's share of all-to-all sequence parallelism: whole-sequence
                   attention for a group of h/N heads, exchanged in and out by copy kernels
@@ -33,7 +35,8 @@ from . import _lib
 from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, RaUlyssesTiming, check
 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
-           "bwd_preprocess", "step_bwd", "ring_bwd", "ulysses_fwd", "ulysses_fwd_timed",
+           "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_kv_stationary", "ulysses_fwd",
+           "ulysses_fwd_timed", "ulysses_workspace_bytes",
            "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
@@ -372,6 +375,50 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
                                  _ptr(workspace), workspace.numel(), _stream(stream),
                                  ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
           "ra_ring_bwd")
+    return dq, dk, dv
+
+
+def ring_bwd_kv_stationary(k, v, q_all, dout_all, lse_all, delta_all, *, kv_shard, causal=False,
+                           layout="contiguous", scale=None, stream=None, copy_stream="auto",
+                           workspace=None, out=None):
+    """Backward ring pass with keys and values stationary, device kv_shard's share: k, v
+    [b, L, n_kv, d] (bf16) stay, every query shard passes by with q_all, dout_all
+    [N, b, L, h, d], lse_all and delta_all [N, b, h, L] (fp32, D from bwd_preprocess on each
+    shard's home).  Returns fp32 (dq_all [N, b, L, h, d]: this device's contributions to
+    every shard's dQ, dk, dv [b, L, n_kv, d]: its KV shard's gradients), into `out` if given."""
+    N, b, L, h, d = q_all.shape
+    n_kv = k.shape[2]
+    _need(k, "k", (b, L, n_kv, d), q_all.dtype)
+    _need(v, "v", (b, L, n_kv, d), q_all.dtype)
+    _need(q_all, "q_all", (N, b, L, h, d), q_all.dtype)
+    _need(dout_all, "dout_all", (N, b, L, h, d), q_all.dtype)
+    _need(lse_all, "lse_all", (N, b, h, L), torch.float32)
+    _need(delta_all, "delta_all", (N, b, h, L), torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q_all.dtype, scale=scale)
+    need = int(_lib.lib().ra_ring_bwd_kv_stationary_workspace(ctypes.byref(p)))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ring_bwd_kv_stationary_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q_all.device, dtype=torch.uint8)
+    if out is None:
+        dq = torch.empty((N, b, L, h, d), device=q_all.device, dtype=torch.float32)
+        dk = torch.empty((b, L, n_kv, d), device=q_all.device, dtype=torch.float32)
+        dv = torch.empty((b, L, n_kv, d), device=q_all.device, dtype=torch.float32)
+    else:
+        dq, dk, dv = out
+        _need(dq, "dq_all", (N, b, L, h, d), torch.float32)
+        _need(dk, "dk", (b, L, n_kv, d), torch.float32)
+        _need(dv, "dv", (b, L, n_kv, d), torch.float32)
+    _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    if workspace.numel() < need:
+        raise RaError(int(_lib.RA_ERR_WORKSPACE), "ra_ring_bwd_kv_stationary")
+    cs = copy_stream_for(q_all.device) if copy_stream == "auto" else copy_stream
+    check(_lib.lib().ra_ring_bwd_kv_stationary(
+        ctypes.byref(p), kv_shard, _ptr(k), _ptr(v), _ptr(q_all), _ptr(dout_all), _ptr(lse_all),
+        _ptr(delta_all), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+        _stream(stream), ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
+        "ra_ring_bwd_kv_stationary")
     return dq, dk, dv
 
 

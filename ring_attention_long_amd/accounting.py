@@ -60,3 +60,17 @@ def ulysses_bytes_per_device(b: int, S: int, N: int, h: int, n_kv: int, d: int, 
 def ulysses_flops_noncausal(b: int, S: int, N: int, h: int, d: int) -> int:
     """Attention work of one device after the exchange: whole sequence, h/N heads."""
     return 4 * b * S * S * (h // N) * d
+
+
+def bwd_bytes_per_step_kv_rotating(b: int, L: int, n_kv: int, d: int, elem_bytes: int,
+                                   acc_bytes: int = 4) -> int:
+    """Backward ring step with K, V and their gradient accumulators rotating (page 4, "The
+    Backward Pass: Symmetric Ring Operation": (k, v, dk, dv) move together)."""
+    return b * L * n_kv * d * (2 * elem_bytes + 2 * acc_bytes)
+
+
+def bwd_bytes_per_step_kv_stationary(b: int, L: int, h: int, d: int, elem_bytes: int,
+                                     acc_bytes: int = 4) -> int:
+    """Backward ring step with K, V stationary (page 1, "The Backward Pass and Gradient
+    Exchange"): a query shard's Q and dO, its LSE and D (fp32) and its dQ accumulator move."""
+    return b * L * h * d * (2 * elem_bytes + acc_bytes) + 2 * 4 * b * h * L

@@ -394,6 +394,20 @@ ra_status check_bwd_problem(const ra_problem* p) {
   return RA_OK;
 }
 
+// Staging buffers of the key/value-stationary backward: per buffer one query shard's Q and
+// dO (dtype) and its LSE and D (fp32).
+struct QStage {
+  size_t q, lse, one, total;
+};
+QStage qstage_ws(const ra_problem* p) {
+  QStage w;
+  w.q = align_up((size_t)p->b * p->L * p->h * p->d * elem_size(p), 256);
+  w.lse = align_up((size_t)p->b * p->h * p->L * 4, 256);
+  w.one = 2 * w.q + 2 * w.lse;
+  w.total = 2 * w.one;
+  return w;
+}
+
 size_t ring_bwd_workspace(const ra_problem* p) {
   const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
   return 4 * align_up(shard_bytes, 256) + align_up((size_t)p->b * p->h * p->L * 4, 256);
@@ -587,6 +601,96 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t qs, const void* q, const void
       const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, nullptr, nullptr);
       if ((e = ra::launch_step_bwd_bf16(a, dout, lse, delta, dq, dk_all + (size_t)src * shard_elems,
                                         dv_all + (size_t)src * shard_elems, cs)) != hipSuccess)
+        return hip_fail(e, "backward step kernel launch");
+    }
+    if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return RA_OK;
+}
+
+size_t ra_ring_bwd_kv_stationary_workspace(const ra_problem* p) {
+  if (check_bwd_problem(p) != RA_OK || p->doc_begin) return 0;
+  return qstage_ws(p).total;
+}
+
+ra_status ra_ring_bwd_kv_stationary(const ra_problem* p, int32_t ks, const void* k_home, const void* v_home,
+                                    const void* q_all, const void* dout_all, const float* lse_all,
+                                    const float* delta_all, float* dq_all, float* dk, float* dv, void* ws,
+                                    size_t ws_bytes, ra_stream compute, ra_stream copy) {
+  RA_TRY(check_bwd_problem(p));
+  if (p->doc_begin)   // the bounds describe one query shard's rows; here every step has another
+    return fail(RA_ERR_UNSUPPORTED, "packed documents are not supported with stationary keys and values");
+  RA_TRY(check_shard(p, ks, "kv_shard"));
+  RA_TRY(check_ptr(k_home, "k", 16));
+  RA_TRY(check_ptr(v_home, "v", 16));
+  RA_TRY(check_ptr(q_all, "q_all", 16));
+  RA_TRY(check_ptr(dout_all, "dout_all", 16));
+  RA_TRY(check_ptr(lse_all, "lse_all", 4));
+  RA_TRY(check_ptr(delta_all, "delta_all", 4));
+  RA_TRY(check_ptr(dq_all, "dq_all", 16));
+  RA_TRY(check_ptr(dk, "dk", 16));
+  RA_TRY(check_ptr(dv, "dv", 16));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const QStage w = qstage_ws(p);
+  if (ws_bytes < w.total) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+  const int N = p->N;
+  if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
+
+  const size_t q_elems = (size_t)p->b * p->L * p->h * p->d;
+  const size_t q_bytes = q_elems * elem_size(p);
+  const size_t row_elems = (size_t)p->b * p->h * p->L;
+  const size_t kv_elems = (size_t)p->b * p->L * p->n_kv * p->d;
+  char* buf[2] = {(char*)ws, (char*)ws + w.one};
+  const hipStream_t cs = (hipStream_t)compute;
+  const hipStream_t ps = copy ? (hipStream_t)copy : cs;
+  const bool split = ps != cs;
+
+  Events ev;
+  hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
+  hipError_t e;
+  if ((e = ev.make(&entry, false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  for (int k = 0; k < N; ++k) {
+    if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if ((e = ra::launch_fill_lse(dq_all, (int64_t)(q_elems * N), 0.f, cs)) != hipSuccess ||
+      (e = ra::launch_fill_lse(dk, (int64_t)kv_elems, 0.f, cs)) != hipSuccess ||
+      (e = ra::launch_fill_lse(dv, (int64_t)kv_elems, 0.f, cs)) != hipSuccess)
+    return hip_fail(e, "fill kernel launch");
+  if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (split && (e = hipStreamWaitEvent(ps, entry, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+
+  const char* qc = (const char*)q_all;
+  const char* oc = (const char*)dout_all;
+  auto shard_of = [&](int step) { return (ks + step) % N; };   // query shard held at this step
+  for (int k = 0; k < N; ++k) {
+    if (k + 1 < N) {
+      // stage query shard (ks + k + 1) mod N into buffer (k + 1) % 2, last read by step k - 1
+      const int i = shard_of(k + 1);
+      char* dst = buf[(k + 1) & 1];
+      if (split && k - 1 >= 1 && (e = hipStreamWaitEvent(ps, consumed[k - 1], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      if ((e = hipMemcpyAsync(dst, qc + (size_t)i * q_bytes, q_bytes, hipMemcpyDeviceToDevice, ps)) != hipSuccess ||
+          (e = hipMemcpyAsync(dst + w.q, oc + (size_t)i * q_bytes, q_bytes, hipMemcpyDeviceToDevice, ps)) !=
+              hipSuccess ||
+          (e = hipMemcpyAsync(dst + 2 * w.q, lse_all + (size_t)i * row_elems, row_elems * 4, hipMemcpyDeviceToDevice,
+                              ps)) != hipSuccess ||
+          (e = hipMemcpyAsync(dst + 2 * w.q + w.lse, delta_all + (size_t)i * row_elems, row_elems * 4,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(query shard)");
+      if ((e = hipEventRecord(staged[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if (split && k >= 1 && (e = hipStreamWaitEvent(cs, staged[k], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    const int i = shard_of(k);
+    const char* b = buf[k & 1];
+    const void* qp = k == 0 ? (const void*)(qc + (size_t)i * q_bytes) : (const void*)b;
+    const void* op = k == 0 ? (const void*)(oc + (size_t)i * q_bytes) : (const void*)(b + w.q);
+    const float* lp = k == 0 ? lse_all + (size_t)i * row_elems : (const float*)(b + 2 * w.q);
+    const float* dp = k == 0 ? delta_all + (size_t)i * row_elems : (const float*)(b + 2 * w.q + w.lse);
+    if (step_is_live(p, i, ks)) {
+      const ra::StepArgs a = step_args(p, i, ks, qp, k_home, v_home, nullptr, nullptr);
+      if ((e = ra::launch_step_bwd_bf16(a, op, lp, dp, dq_all + (size_t)i * q_elems, dk, dv, cs)) != hipSuccess)
         return hip_fail(e, "backward step kernel launch");
     }
     if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
