@@ -252,6 +252,22 @@ ra_status ra_ulysses_fwd_timed(const ra_problem* p, int32_t head_group, const vo
                                const void* k_all, const void* v_all, void* o_all, float* lse_all,
                                void* ws, size_t ws_bytes, ra_stream stream, ra_ulysses_timing* t);
 
+/* ra_ulysses_bwd — the backward of device head_group's share: gathers its heads' Q, K, V,
+ * O, dO (dtype) and LSE of the whole sequence from every shard (q_all, o_all, dout_all
+ * [N][b][L][h][d], k_all, v_all [N][b][L][n_kv][d], lse_all [N][b][h][L], each shard in its
+ * own layout order), runs the backward of the whole-sequence attention (the same step
+ * kernels as ra_step_bwd, D = rowsum(dO * O) included) and sends the gradients back: writes
+ * query heads [head_group h/N, ..) of dq_all [N][b][L][h][d] and KV heads
+ * [head_group n_kv/N, ..) of dk_all, dv_all [N][b][L][n_kv][d], fp32, overwriting them;
+ * other heads are untouched.  With GQA a device holds every query head of its KV heads, so
+ * their dK, dV are complete.  bf16, d = 128.  Workspace: ra_ulysses_bwd_workspace(p)
+ * bytes, 0 if p is invalid for this path. */
+size_t ra_ulysses_bwd_workspace(const ra_problem* p);
+ra_status ra_ulysses_bwd(const ra_problem* p, int32_t head_group, const void* q_all, const void* k_all,
+                         const void* v_all, const void* o_all, const void* dout_all, const float* lse_all,
+                         float* dq_all, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
+                         ra_stream stream);
+
 /* Host-only (no GPU work): number of (query, key) pairs shard q_shard may attend to in KV
  * shard kv_shard (or the whole sequence when kv_shard = -1), summed over the batch.  Useful
  * FLOPs of the forward are 4 * d * h * pairs (page 3, section 2: two GEMMs, 2 FLOPs per

@@ -20,6 +20,7 @@ Entry points (same names as the C-ABI, without the ``ra_`` prefix):
     ulysses_fwd   one device's share of all-to-all sequence parallelism: whole-sequence
                   attention for a group of h/N heads, exchanged in and out by copy kernels
     ulysses_fwd_timed  ulysses_fwd plus the time of its gather, attention and scatter
+    ulysses_bwd   the backward of that share (gradients of the group's heads, sent back)
 
 Tensor layouts (page 1, "Practical Implementation Patterns": batch, sequence, heads, dim):
     q, o [b, L, h, d];  k, v [b, L, n_kv, d];  k_all, v_all [N, b, L, n_kv, d];
@@ -36,7 +37,7 @@ from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, 
 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
            "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_kv_stationary", "ulysses_fwd",
-           "ulysses_fwd_timed", "ulysses_workspace_bytes",
+           "ulysses_fwd_timed", "ulysses_workspace_bytes", "ulysses_bwd",
            "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
@@ -296,6 +297,42 @@ def ulysses_fwd_timed(q_all, k_all, v_all, *, head_group, causal=False, layout="
                                           _stream(stream), ctypes.byref(tm)), "ra_ulysses_fwd_timed")
     return o, lse, {"gather_ms": tm.gather_ms, "attend_ms": tm.attend_ms,
                     "scatter_ms": tm.scatter_ms, "total_ms": tm.total_ms}
+
+
+def ulysses_bwd(q_all, k_all, v_all, o_all, dout_all, lse_all, *, head_group, causal=False,
+                layout="contiguous", scale=None, stream=None, workspace=None, out=None):
+    """Backward of device head_group's share of the all-to-all scheme.  q_all, o_all, dout_all
+    [N, b, L, h, d] (bf16), k_all, v_all [N, b, L, n_kv, d], lse_all [N, b, h, L] fp32.  Writes
+    the group's heads of (dq_all [N, b, L, h, d], dk_all, dv_all [N, b, L, n_kv, d]) fp32
+    (allocated as zeros if out is None) and returns them; call it for every head group to
+    fill them."""
+    N, b, L, h, d = q_all.shape
+    n_kv = k_all.shape[3]
+    for t, n, shp in ((q_all, "q_all", (N, b, L, h, d)), (o_all, "o_all", (N, b, L, h, d)),
+                      (dout_all, "dout_all", (N, b, L, h, d)), (k_all, "k_all", (N, b, L, n_kv, d)),
+                      (v_all, "v_all", (N, b, L, n_kv, d))):
+        _need(t, n, shp, q_all.dtype)
+    _need(lse_all, "lse_all", (N, b, h, L), torch.float32)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q_all.dtype, scale=scale)
+    need = int(_lib.lib().ra_ulysses_bwd_workspace(ctypes.byref(p)))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ulysses_bwd_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q_all.device, dtype=torch.uint8)
+    if out is None:
+        out = (torch.zeros((N, b, L, h, d), device=q_all.device, dtype=torch.float32),
+               torch.zeros((N, b, L, n_kv, d), device=q_all.device, dtype=torch.float32),
+               torch.zeros((N, b, L, n_kv, d), device=q_all.device, dtype=torch.float32))
+    dq, dk, dv = out
+    _need(dq, "dq_all", (N, b, L, h, d), torch.float32)
+    _need(dk, "dk_all", (N, b, L, n_kv, d), torch.float32)
+    _need(dv, "dv_all", (N, b, L, n_kv, d), torch.float32)
+    check(_lib.lib().ra_ulysses_bwd(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all),
+                                    _ptr(o_all), _ptr(dout_all), _ptr(lse_all), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
+          "ra_ulysses_bwd")
+    return dq, dk, dv
 
 
 def bwd_preprocess(o, dout, *, stream=None):

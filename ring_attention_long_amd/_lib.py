@@ -69,6 +69,8 @@ SIGNATURES = [
     ("ra_ulysses_fwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V]),
     ("ra_ulysses_fwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V,
                                   ctypes.POINTER(RaUlyssesTiming)]),
+    ("ra_ulysses_bwd_workspace", _S, [_P]),
+    ("ra_ulysses_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V]),
     ("ra_allowed_pairs", ctypes.c_int64, [_P, _I, _I]),
     ("ra_allowed_pairs_packed", ctypes.c_int64, [_P, _I, _I, _V, _V]),
     ("ra_document_ranges", _I, [_P, _I, _V, _I, _V, _V]),

@@ -384,6 +384,26 @@ ra_status ulysses_fwd_impl(const ra_problem* p, int32_t group, const void* q_all
   return RA_OK;
 }
 
+ra_status check_bwd_problem(const ra_problem* p);
+
+// Backward of the all-to-all path: the head group's Q, K, V, O, dO (dtype) and LSE, D (fp32)
+// of the whole sequence, and its fp32 dQ, dK, dV.
+struct UlyssesBwdWs {
+  size_t q, kv, lse, dq, dkv, total;
+};
+UlyssesBwdWs ulysses_bwd_ws(const ra_problem* p) {
+  const size_t S = (size_t)p->N * p->L, es = elem_size(p);
+  const size_t Hg = p->h / p->N, Kg = p->n_kv / p->N;
+  UlyssesBwdWs w;
+  w.q = align_up((size_t)p->b * S * Hg * p->d * es, 256);
+  w.kv = align_up((size_t)p->b * S * Kg * p->d * es, 256);
+  w.lse = align_up((size_t)p->b * Hg * S * 4, 256);
+  w.dq = align_up((size_t)p->b * S * Hg * p->d * 4, 256);
+  w.dkv = align_up((size_t)p->b * S * Kg * p->d * 4, 256);
+  w.total = 3 * w.q + 2 * w.kv + 2 * w.lse + w.dq + 2 * w.dkv;   // q, o, dO; k, v; lse, D; dq; dk, dv
+  return w;
+}
+
 ra_status check_bwd_problem(const ra_problem* p) {
   RA_TRY(check_problem(p));
   if (p->dtype != RA_BF16 || p->d != 128)
@@ -726,6 +746,83 @@ int64_t ra_allowed_pairs_packed(const ra_problem* p, int32_t q_shard, int32_t kv
       }
     }
   return total;
+}
+
+size_t ra_ulysses_bwd_workspace(const ra_problem* p) {
+  if (check_ulysses(p) != RA_OK) return 0;
+  const ra_problem lp = ulysses_local(p);
+  if (check_bwd_problem(&lp) != RA_OK) return 0;
+  return ulysses_bwd_ws(p).total;
+}
+
+ra_status ra_ulysses_bwd(const ra_problem* p, int32_t group, const void* q_all, const void* k_all,
+                         const void* v_all, const void* o_all, const void* dout_all, const float* lse_all,
+                         float* dq_all, float* dk_all, float* dv_all, void* ws, size_t ws_bytes, ra_stream stream) {
+  RA_TRY(check_ulysses(p));
+  RA_TRY(check_shard(p, group, "head_group"));
+  const ra_problem lp = ulysses_local(p);
+  RA_TRY(check_bwd_problem(&lp));
+  RA_TRY(check_ptr(q_all, "q_all", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o_all, "o_all", 16));
+  RA_TRY(check_ptr(dout_all, "dout_all", 16));
+  RA_TRY(check_ptr(lse_all, "lse_all", 4));
+  RA_TRY(check_ptr(dq_all, "dq_all", 16));
+  RA_TRY(check_ptr(dk_all, "dk_all", 16));
+  RA_TRY(check_ptr(dv_all, "dv_all", 16));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const UlyssesBwdWs w = ulysses_bwd_ws(p);
+  if (ws_bytes < w.total) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+
+  char* c = (char*)ws;
+  void* q_g = c;
+  void* o_g = c + w.q;
+  void* do_g = c + 2 * w.q;
+  void* k_g = c + 3 * w.q;
+  void* v_g = c + 3 * w.q + w.kv;
+  float* lse_g = (float*)(c + 3 * w.q + 2 * w.kv);
+  float* dl_g = (float*)(c + 3 * w.q + 2 * w.kv + w.lse);
+  float* dq_g = (float*)(c + 3 * w.q + 2 * w.kv + 2 * w.lse);
+  float* dk_g = (float*)(c + 3 * w.q + 2 * w.kv + 2 * w.lse + w.dq);
+  float* dv_g = (float*)(c + 3 * w.q + 2 * w.kv + 2 * w.lse + w.dq + w.dkv);
+  const hipStream_t s = (hipStream_t)stream;
+  const int Hg = p->h / p->N, Kg = p->n_kv / p->N, es = (int)elem_size(p);
+  const int64_t S = (int64_t)p->N * p->L;
+  hipError_t e;
+  // first exchange: the head group's inputs of the whole sequence
+  if ((e = ra::launch_ulysses_gather(q_g, q_all, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather(o_g, o_all, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather(do_g, dout_all, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, p->d, es,
+                                     s)) != hipSuccess ||
+      (e = ra::launch_ulysses_gather(k_g, k_all, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather(v_g, v_all, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d, es, s)) !=
+          hipSuccess ||
+      (e = ra::launch_ulysses_gather_rows(lse_g, lse_all, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, s)) !=
+          hipSuccess)
+    return hip_fail(e, "gather kernel launch");
+  // the backward of the whole-sequence attention
+  if ((e = ra::launch_bwd_preprocess(o_g, do_g, dl_g, p->b, (int)S, Hg, s)) != hipSuccess)
+    return hip_fail(e, "preprocess kernel launch");
+  if ((e = ra::launch_fill_lse(dq_g, (int64_t)p->b * S * Hg * p->d, 0.f, s)) != hipSuccess ||
+      (e = ra::launch_fill_lse(dk_g, (int64_t)p->b * S * Kg * p->d, 0.f, s)) != hipSuccess ||
+      (e = ra::launch_fill_lse(dv_g, (int64_t)p->b * S * Kg * p->d, 0.f, s)) != hipSuccess)
+    return hip_fail(e, "fill kernel launch");
+  const ra::StepArgs a = step_args(&lp, 0, 0, q_g, k_g, v_g, nullptr, nullptr);
+  if ((e = ra::launch_step_bwd_bf16(a, do_g, lse_g, dl_g, dq_g, dk_g, dv_g, s)) != hipSuccess)
+    return hip_fail(e, "backward step kernel launch");
+  // second exchange: the gradients back to the shards
+  if ((e = ra::launch_ulysses_scatter_rows(dq_all, dq_g, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg, p->d,
+                                           RA_F32, s)) != hipSuccess ||
+      (e = ra::launch_ulysses_scatter_rows(dk_all, dk_g, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d,
+                                           RA_F32, s)) != hipSuccess ||
+      (e = ra::launch_ulysses_scatter_rows(dv_all, dv_g, p->b, p->L, p->N, p->layout, p->n_kv, Kg, group * Kg, p->d,
+                                           RA_F32, s)) != hipSuccess)
+    return hip_fail(e, "scatter kernel launch");
+  return RA_OK;
 }
 
 size_t ra_ulysses_fwd_workspace(const ra_problem* p) {

@@ -198,6 +198,12 @@ hipError_t launch_ulysses_gather(void* dst, const void* src_all, int b, int L, i
 hipError_t launch_ulysses_scatter(void* dst_all, float* lse_all, const float* o, const float* lse,
                                   int b, int L, int N, int layout, int H, int Hg, int head0, int d,
                                   int dtype, hipStream_t s);
+// Per-row statistics [N][b][H][L] (heads head0 ..) -> [b][Hg][S] in global position order.
+hipError_t launch_ulysses_gather_rows(float* dst, const float* src_all, int b, int L, int N, int layout, int H,
+                                      int Hg, int head0, hipStream_t s);
+// Rows [b][S][Hg][d] fp32 -> heads head0 .. of dst_all [N][b][L][H][d] (converted to dtype).
+hipError_t launch_ulysses_scatter_rows(void* dst_all, const float* src, int b, int L, int N, int layout, int H,
+                                       int Hg, int head0, int d, int dtype, hipStream_t s);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
                                  hipStream_t s);
 // Adds this step's contributions: dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32).

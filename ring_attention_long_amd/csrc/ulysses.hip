@@ -4,8 +4,9 @@
 // way.  On one GPU the N devices' shards are resident buffers and one device's side of each
 // exchange is a copy kernel: the gather builds the whole sequence of the device's heads in
 // global position order (so the attention that follows masks by position alone), the
-// scatter writes the device's heads of every shard's output and LSE.  Both are plain
-// HBM-bound copies, 16 bytes per thread on the wide side.
+// scatter writes the device's heads of every shard's output and LSE.  The backward uses
+// the same exchanges for O, dO and the LSE on the way in and the gradients on the way
+// out.  All are plain HBM-bound copies, 16 bytes per thread on the wide side.
 #include "ra_internal.h"
 
 namespace ra {
@@ -83,6 +84,21 @@ __global__ __launch_bounds__(256) void ulysses_scatter_lse_kernel(float* __restr
   dst[(((int64_t)j * b + bi) * H + head0 + hh) * L + t] = src[((int64_t)bi * Hg + hh) * S + P];
 }
 
+// Per-row statistics the other way: src [N][b][H][L] (fp32) -> dst [b][Hg][S].
+__global__ __launch_bounds__(256) void ulysses_gather_rows_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                                  int b, int L, int N, int layout, int H, int Hg,
+                                                                  int head0) {
+  const int bi = blockIdx.y;
+  const int64_t S = (int64_t)N * L;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= S * Hg) return;
+  const int hh = (int)(idx / S);
+  const int64_t P = idx - (int64_t)hh * S;
+  int j, t;
+  owner_of(layout, N, L, P, j, t);
+  dst[((int64_t)bi * Hg + hh) * S + P] = src[(((int64_t)j * b + bi) * H + head0 + hh) * L + t];
+}
+
 dim3 grid_for(int64_t threads, int b) { return dim3((unsigned)((threads + 255) / 256), (unsigned)b); }
 
 }  // namespace
@@ -97,20 +113,34 @@ hipError_t launch_ulysses_gather(void* dst, const void* src_all, int b, int L, i
   return hipGetLastError();
 }
 
+hipError_t launch_ulysses_gather_rows(float* dst, const float* src_all, int b, int L, int N, int layout, int H,
+                                      int Hg, int head0, hipStream_t s) {
+  const int64_t threads = (int64_t)N * L * Hg;
+  if ((threads + 255) / 256 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(ulysses_gather_rows_kernel, grid_for(threads, b), dim3(256), 0, s, dst, src_all, b, L, N,
+                     layout, H, Hg, head0);
+  return hipGetLastError();
+}
+
+hipError_t launch_ulysses_scatter_rows(void* dst_all, const float* src, int b, int L, int N, int layout, int H,
+                                       int Hg, int head0, int d, int dtype, hipStream_t s) {
+  const int E = dtype == RA_BF16 ? 8 : 4;
+  const int64_t threads = (int64_t)N * L * Hg * (d / E);
+  if ((threads + 255) / 256 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(ulysses_scatter_o_kernel<RA_BF16>, grid_for(threads, b), dim3(256), 0, s, dst_all, src, b, L,
+                       N, layout, H, Hg, head0, d);
+  else
+    hipLaunchKernelGGL(ulysses_scatter_o_kernel<RA_F32>, grid_for(threads, b), dim3(256), 0, s, dst_all, src, b, L,
+                       N, layout, H, Hg, head0, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_ulysses_scatter(void* dst_all, float* lse_all, const float* o, const float* lse,
                                   int b, int L, int N, int layout, int H, int Hg, int head0, int d,
                                   int dtype, hipStream_t s) {
-  const int E = dtype == RA_BF16 ? 8 : 4;
-  const int64_t threads = (int64_t)N * L * Hg * (d / E);
   const int64_t lse_threads = (int64_t)N * L * Hg;
-  if ((threads + 255) / 256 > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (dtype == RA_BF16)
-    hipLaunchKernelGGL(ulysses_scatter_o_kernel<RA_BF16>, grid_for(threads, b), dim3(256), 0, s, dst_all, o, b, L,
-                       N, layout, H, Hg, head0, d);
-  else
-    hipLaunchKernelGGL(ulysses_scatter_o_kernel<RA_F32>, grid_for(threads, b), dim3(256), 0, s, dst_all, o, b, L,
-                       N, layout, H, Hg, head0, d);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_ulysses_scatter_rows(dst_all, o, b, L, N, layout, H, Hg, head0, d, dtype, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ulysses_scatter_lse_kernel, grid_for(lse_threads, b), dim3(256), 0, s, lse_all, lse, b, L, N,
                      layout, H, Hg, head0);

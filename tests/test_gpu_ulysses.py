@@ -115,3 +115,76 @@ def test_ulysses_full_size_sampled():
         idx = torch.from_numpy(rows).cuda()
         check_bf16(out[j][:, idx][:, :, heads], lse[j][:, heads][:, :, idx], O[:, :, heads], LSE[:, heads],
                    f"ulysses full size shard {j}")
+
+
+def _dout_all(*, b, L, h, d, N, seed):
+    return np.stack([synth.normal((b, L, h, d), seed=seed, name="do", shard=j) for j in range(N)])
+
+
+@pytest.mark.parametrize("layout,causal", [("contiguous", False), ("contiguous", True), ("striped", True),
+                                           ("zigzag", True)])
+def test_ulysses_bwd_every_shard(layout, causal):
+    """Every head group's backward fills dQ of every shard and dK, dV of every KV shard; each
+    must equal the exact gradients (the forward's O and LSE come from the same scheme)."""
+    from test_gpu_bwd import check_grad
+    from oracle import shard_grads
+    cfg = dict(b=1, L=100, h=8, n_kv=4, d=128, N=4)
+    announce("ulysses bwd", layout, "causal", causal, cfg)
+    q, k, v = all_shards(**cfg, seed=211, dtype="bf16")
+    do = _dout_all(b=1, L=100, h=8, d=128, N=4, seed=211)
+    qg, kg, vg, dog = (to_gpu(x, "bf16") for x in (q, k, v, do))
+    o, lse = run_all_groups(qg, kg, vg, N=4, causal=causal, layout=layout)
+    out = None
+    for g in range(4):
+        out = ra.ulysses_bwd(qg, kg, vg, o, dog, lse, head_group=g, causal=causal, layout=layout, out=out)
+    torch.cuda.synchronize()
+    dq, dk, dv = out
+    x = [a.astype(np.float64) for a in (q, k, v, do)]
+    rdk, rdv = np.zeros(k.shape), np.zeros(v.shape)
+    for i in range(4):
+        rq, rk, rv = shard_grads(x[0][i], x[1], x[2], x[3][i], N=4, shard=i, layout=layout, causal=causal)
+        check_grad(dq[i], rq, f"ulysses dq shard {i} {layout} {causal}")
+        rdk += rk
+        rdv += rv
+    for j in range(4):
+        check_grad(dk[j], rdk[j], f"ulysses dk shard {j} {layout} {causal}")
+        check_grad(dv[j], rdv[j], f"ulysses dv shard {j} {layout} {causal}")
+
+
+def test_ulysses_bwd_full_size():
+    """S = 65536 (N = 8, L = 8192, h = 32, n_kv = 8, d = 128, bf16), striped causal, head group
+    2: its heads' dQ, dK, dV against the key/value-rotating ring backward of every shard
+    (itself checked against the oracle), and sampled dQ rows against the oracle."""
+    from test_gpu_bwd import check_grad
+    from oracle import shard_dq_rows
+    N, L, h, n_kv, d, grp = 8, 8192, 32, 8, 128, 2
+    hs, ks = slice(4 * grp, 4 * grp + 4), slice(grp, grp + 1)
+    announce("ulysses bwd full size: inputs")
+    q, k, v = all_shards(b=1, L=L, h=h, n_kv=n_kv, d=d, N=N, seed=212, dtype="bf16")
+    do = _dout_all(b=1, L=L, h=h, d=d, N=N, seed=212)
+    qg, kg, vg, dog = (to_gpu(x, "bf16") for x in (q, k, v, do))
+    announce("ulysses bwd full size: forward and backward of head group 2")
+    o, lse = ra.ulysses_fwd(qg, kg, vg, head_group=grp, causal=True, layout="striped")
+    dq, dk, dv = ra.ulysses_bwd(qg, kg, vg, o, dog, lse, head_group=grp, causal=True, layout="striped")
+    announce("ulysses bwd full size: rotating ring backward of every shard")
+    rdk = torch.zeros_like(dk)
+    rdv = torch.zeros_like(dv)
+    rdq = []
+    for i in range(N):
+        oi, li = ra.ring_fwd(qg[i].contiguous(), kg, vg, q_shard=i, causal=True, layout="striped")
+        dq_i, dk_i, dv_i = ra.ring_bwd(qg[i].contiguous(), kg, vg, oi, dog[i].contiguous(), li, q_shard=i,
+                                       causal=True, layout="striped")
+        rdq.append(dq_i[:, :, hs].clone())
+        rdk += dk_i
+        rdv += dv_i
+    torch.cuda.synchronize()
+    for i in (0, 3, 7):
+        check_grad(dq[i][:, :, hs], f64(rdq[i]), f"full size dq shard {i} vs ring")
+    check_grad(dk[:, :, :, ks], f64(rdk[:, :, :, ks]), "full size dk vs ring")
+    check_grad(dv[:, :, :, ks], f64(rdv[:, :, :, ks]), "full size dv vs ring")
+    x = [a.astype(np.float64) for a in (q, k, v, do)]
+    rows = np.array([0, 1, 63, 64, 4095, L - 2, L - 1])
+    for i in (0, 5):
+        announce(f"ulysses bwd full size: oracle dQ rows of shard {i}")
+        ref = shard_dq_rows(x[0][i], x[1], x[2], x[3][i], rows, N=N, shard=i, layout="striped", causal=True)
+        check_grad(dq[i][:, torch.from_numpy(rows).cuda()][:, :, hs], ref[:, :, hs], f"full size dq rows shard {i}")

@@ -91,3 +91,27 @@ def test_ulysses_rejects_bad_arguments():
     if _no_hip_device():                      # valid arguments reach the first launch
         assert call(3) == _lib.RA_ERR_HIP
         assert b"device" in lib.ra_last_error().lower()
+
+
+def test_ulysses_bwd_workspace_and_validation():
+    """The backward's workspace: Q, O, dO (h/N heads) and K, V (n_kv/N heads) of the whole
+    sequence in bf16, LSE and D, and the fp32 dQ, dK, dV, each padded to 256 bytes."""
+    lib = _lib.lib()
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    p = _prob(b=1, L=100, h=8, n_kv=4, N=4)
+    S = 400
+    want = (3 * pad(S * 2 * 128 * 2) + 2 * pad(S * 1 * 128 * 2) + 2 * pad(2 * S * 4) + pad(S * 2 * 128 * 4)
+            + 2 * pad(S * 1 * 128 * 4))
+    need = lib.ra_ulysses_bwd_workspace(ctypes.byref(p))
+    assert need == want
+    call = lambda g, prob=p, ws=need, q=FAKE: lib.ra_ulysses_bwd(  # noqa: E731
+        ctypes.byref(prob), g, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert call(4) == _lib.RA_ERR_INVALID_ARG
+    assert call(0, q=None) == _lib.RA_ERR_INVALID_ARG
+    assert call(0, ws=need - 1) == _lib.RA_ERR_WORKSPACE
+    bad = _prob(b=1, L=100, h=6, n_kv=2, N=4)
+    assert lib.ra_ulysses_bwd_workspace(ctypes.byref(bad)) == 0 and call(0, prob=bad) == _lib.RA_ERR_INVALID_ARG
+    f32 = _prob(b=1, L=100, h=8, n_kv=4, N=4, dtype=0)
+    assert lib.ra_ulysses_bwd_workspace(ctypes.byref(f32)) == 0 and call(0, prob=f32) == _lib.RA_ERR_UNSUPPORTED
+    if _no_hip_device():
+        assert call(1) == _lib.RA_ERR_HIP
