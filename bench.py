@@ -68,6 +68,9 @@ ULYSSES_WORKLOADS = {
                                    "d=128 bf16, head group 0 (4 query heads, 1 KV head)",
                                    dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "striped", True, 0, 1007),
 }
+ULYSSES_WORKLOADS["ulysses_bwd_striped_causal_8k"] = (
+    "ulysses_bwd striped causal, S=65536 N=8 L=8192 h=32 n_kv=8 d=128 bf16, head group 0 (4 query "
+    "heads, 1 KV head)", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8), "striped", True, 0, 1008)
 ULYSSES_METRIC = ("all-to-all sequence-parallel attention TFLOP/s (bf16, causal), one device's share, "
                   "and % of MI355X MFMA peak")
 # packed-document workloads (page 3, section 5): the same shapes with documents of lognormal
@@ -520,9 +523,25 @@ def run_ulysses(args):
     flops = accounting.flops_from_pairs(pairs, h // N, d)
     compute = torch.cuda.current_stream()
 
-    def one_pass():
+    backward = "bwd" in args.workload
+    if backward:
+        # the forward once (O, LSE), then the timed backward of the device's share
         ra.ulysses_fwd(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout, workspace=ws,
                        out=o_all, lse_out=lse_all)
+        dout_all = torch.from_numpy(np.stack([synth.normal((b, L, h, d), seed=seed, name="do", shard=j)
+                                              for j in range(N)])).to(dev, torch.bfloat16)
+        grads = (torch.zeros((N, b, L, h, d), device=dev, dtype=torch.float32),
+                 torch.zeros((N, b, L, n_kv, d), device=dev, dtype=torch.float32),
+                 torch.zeros((N, b, L, n_kv, d), device=dev, dtype=torch.float32))
+        flops = flops * 10 // 4                      # five products per pair instead of two
+
+    def one_pass():
+        if backward:
+            ra.ulysses_bwd(q_all, k_all, v_all, o_all, dout_all, lse_all, head_group=group, causal=causal,
+                           layout=layout, out=grads)
+        else:
+            ra.ulysses_fwd(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout, workspace=ws,
+                           out=o_all, lse_out=lse_all)
 
     for _ in range(args.warmup):
         one_pass()
@@ -530,6 +549,18 @@ def run_ulysses(args):
     ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+    if backward:
+        result = {"metric": BWD_METRIC + " (all-to-all scheme, one device's share)", "value": round(value, 2),
+                  "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                  "ms_per_step": round(ms, 4), "pass_ms": pass_stats, "higher_is_better": True,
+                  "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                  "data": "synthetic: iid N(0,1) bf16 Q/K/V/dO from seeded numpy PCG64",
+                  "config": {"workload": desc, "S": S, "N": N, "L": L, "b": b, "h": h, "n_kv": n_kv, "d": d,
+                             "layout": layout, "causal": causal, "head_group": group,
+                             "useful_tflop_per_pass": round(flops / 1e12, 4),
+                             "pct_of_bf16_peak": round(100 * value / accounting.MI355X_BF16_DENSE_TFLOPS, 2)}}
+        print(json.dumps(result), flush=True)
+        return
     parts = [ra.ulysses_fwd_timed(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout,
                                   workspace=ws, out=o_all, lse_out=lse_all)[2] for _ in range(3)]
     tm = {k: float(np.median([t[k] for t in parts])) for k in parts[0]}
