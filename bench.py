@@ -328,10 +328,8 @@ def run_backward(args):
     g = lambda name: torch.from_numpy(inp[name]).to(dev, torch.bfloat16)  # noqa: E731
     q, k_all, v_all, dout = g("q"), g("k_all"), g("v_all"), g("dout")
     o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
-    p = ra.make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                        dtype=torch.bfloat16)
-    ws = torch.empty(int(ra._lib.lib().ra_ring_bwd_workspace(__import__("ctypes").byref(p))),
-                     device=dev, dtype=torch.uint8)
+    ws = torch.empty(ra.ring_bwd_workspace_bytes(q, k_all, causal=causal, layout=layout), device=dev,
+                     dtype=torch.uint8)
     out = (torch.empty((b, L, h, d), device=dev, dtype=torch.float32),
            torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32),
            torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32))

@@ -36,9 +36,9 @@ from . import _lib
 from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, RaUlyssesTiming, check
 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
-           "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_kv_stationary", "ulysses_fwd",
-           "ulysses_fwd_timed", "ulysses_workspace_bytes", "ulysses_bwd",
-           "make_problem", "RaError", "library_path"]
+           "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_workspace_bytes",
+           "ring_bwd_kv_stationary", "ulysses_fwd", "ulysses_fwd_timed", "ulysses_workspace_bytes",
+           "ulysses_bwd", "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 _copy_streams: dict[int, torch.cuda.Stream] = {}
@@ -372,6 +372,14 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
                                  _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
                                  _ptr(dv_acc), _stream(stream)), "ra_step_bwd")
     return dq_acc, dk_acc, dv_acc
+
+
+def ring_bwd_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None) -> int:
+    """Workspace of ring_bwd for q [b, L, h, d], k_all [N, b, L, n_kv, d] (0 if invalid)."""
+    N, b, L, n_kv, d = k_all.shape
+    p = make_problem(b=b, L=L, h=q.shape[2], n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale)
+    return int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p)))
 
 
 def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",

@@ -1,0 +1,77 @@
+"""On any error the library enqueues nothing and writes nothing: outputs filled with a
+sentinel keep it when an entry point rejects its arguments on a GPU machine (the errors are
+all found by validation, before any launch)."""
+import ctypes
+
+import pytest
+import torch
+
+import ring_attention_long_amd as ra
+from ring_attention_long_amd import _lib
+from gpu_helpers import announce
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _filled(shape, dtype=torch.float32):
+    return torch.full(shape, SENTINEL, device="cuda", dtype=dtype)
+
+
+def _unchanged(*ts):
+    torch.cuda.synchronize()
+    return all(bool(torch.all(t == SENTINEL)) for t in ts)
+
+
+def test_rejected_calls_write_nothing():
+    lib = _lib.lib()
+    b, L, h, n_kv, d, N = 1, 128, 8, 4, 128, 4
+    q = torch.randn((b, L, h, d), device="cuda", dtype=torch.bfloat16)
+    k_all = torch.randn((N, b, L, n_kv, d), device="cuda", dtype=torch.bfloat16)
+    v_all = torch.randn_like(k_all)
+    p = ra.make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=True, layout="striped")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    announce("errors: ra_step_fwd with q_shard = N")
+    o, lse = _filled((b, L, h, d)), _filled((b, h, L))
+    assert lib.ra_step_fwd(ctypes.byref(p), N, 0, _p(q), _p(k_all[0]), _p(v_all[0]), _p(o), _p(lse), s) == \
+        _lib.RA_ERR_INVALID_ARG
+    assert _unchanged(o, lse)
+
+    announce("errors: ra_ring_fwd with a workspace one byte short")
+    need = lib.ra_ring_fwd_workspace(ctypes.byref(p))
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    o16 = _filled((b, L, h, d), torch.bfloat16)
+    assert lib.ra_ring_fwd(ctypes.byref(p), 0, _p(q), _p(k_all), _p(v_all), _p(o16), _p(lse), _p(ws), need - 1,
+                           s, None) == _lib.RA_ERR_WORKSPACE
+    assert _unchanged(o16, lse)
+
+    announce("errors: ra_step_bwd with kv_shard = -1")
+    dq, dk, dv = _filled((b, L, h, d)), _filled((b, L, n_kv, d)), _filled((b, L, n_kv, d))
+    dl = _filled((b, h, L))
+    assert lib.ra_step_bwd(ctypes.byref(p), 0, -1, _p(q), _p(k_all[0]), _p(v_all[0]), _p(q), _p(lse), _p(dl),
+                           _p(dq), _p(dk), _p(dv), s) == _lib.RA_ERR_INVALID_ARG
+    assert _unchanged(dq, dk, dv)
+
+    announce("errors: ra_ulysses_fwd with head_group = N")
+    q_all = torch.randn((N, b, L, h, d), device="cuda", dtype=torch.bfloat16)
+    o_all, lse_all = _filled((N, b, L, h, d), torch.bfloat16), _filled((N, b, h, L))
+    uws = torch.empty(lib.ra_ulysses_fwd_workspace(ctypes.byref(p)), device="cuda", dtype=torch.uint8)
+    assert lib.ra_ulysses_fwd(ctypes.byref(p), N, _p(q_all), _p(k_all), _p(v_all), _p(o_all), _p(lse_all),
+                              _p(uws), uws.numel(), s) == _lib.RA_ERR_INVALID_ARG
+    assert _unchanged(o_all, lse_all)
+
+    announce("errors: ra_ring_bwd_kv_stationary with a workspace one byte short")
+    need = lib.ra_ring_bwd_kv_stationary_workspace(ctypes.byref(p))
+    sws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    dq_all = _filled((N, b, L, h, d))
+    lse_all2, dl_all = _filled((N, b, h, L)), _filled((N, b, h, L))
+    assert lib.ra_ring_bwd_kv_stationary(ctypes.byref(p), 0, _p(k_all[0]), _p(v_all[0]), _p(q_all), _p(q_all),
+                                         _p(lse_all2), _p(dl_all), _p(dq_all), _p(dk), _p(dv), _p(sws), need - 1,
+                                         s, None) == _lib.RA_ERR_WORKSPACE
+    assert _unchanged(dq_all, dk, dv)
