@@ -188,3 +188,17 @@ def test_ulysses_bwd_full_size():
         announce(f"ulysses bwd full size: oracle dQ rows of shard {i}")
         ref = shard_dq_rows(x[0][i], x[1], x[2], x[3][i], rows, N=N, shard=i, layout="striped", causal=True)
         check_grad(dq[i][:, torch.from_numpy(rows).cuda()][:, :, hs], ref[:, :, hs], f"full size dq rows shard {i}")
+
+
+@pytest.mark.parametrize("cfg", [dict(b=1, L=130, h=4, n_kv=2, d=128, N=1),     # no exchange at all
+                                 dict(b=2, L=64, h=4, n_kv=4, d=128, N=4)])     # one query and one KV head each
+def test_ulysses_edge_shapes(cfg):
+    N = cfg["N"]
+    announce("ulysses edge", cfg)
+    q, k, v = all_shards(**cfg, seed=221, dtype="bf16")
+    out, lse = run_all_groups(to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16"), N=N, causal=True,
+                              layout="zigzag")
+    x = [a.astype(np.float64) for a in (q, k, v)]
+    for j in range(N):
+        O, LSE = shard_attention(x[0][j], x[1], x[2], N=N, shard=j, layout="zigzag", causal=True)
+        check_bf16(out[j], lse[j], O, LSE, f"ulysses edge shard {j}")
