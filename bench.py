@@ -337,42 +337,31 @@ def run_backward(args):
     flops = 10.0 * h * d * pairs
     compute = torch.cuda.current_stream()
 
+    # each pass records HIP events around every step's ra_step_bwd (both kernels) on the
+    # compute stream (ra_ring_bwd_timed): the roofline comes from the timed passes
+    timings = []
+
     def one_pass():
-        ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal, layout=layout,
-                    workspace=ws, out=out)
+        timings.append(ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal,
+                                   layout=layout, workspace=ws, out=out, timed=True)[3])
 
     for i in range(args.warmup):
         one_pass()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
+    timings.clear()
     ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
 
-    # Per-step launches of ra_step_bwd (dQ kernel + dK/dV kernel) on the compute stream,
-    # K/V read in place, timed with HIP events.
-    delta = ra.bwd_preprocess(o, dout)
-    dq, dk, dv = out
     step_ms, step_flops = [], 0
     for k in range(N):
         src = (shard - k) % N
-        pk = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal,
-                              layout=layout)
-        if pk == 0:
+        if timings[0]["step_begin_ms"][k] < 0:
             continue
-        ts = []
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(compute)
-            ra.step_bwd(q, k_all[src], v_all[src], dout, lse, delta, N=N, q_shard=shard,
-                        kv_shard=src, causal=causal, layout=layout, dq_acc=dq, dk_acc=dk[src],
-                        dv_acc=dv[src])
-            e1.record(compute)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        step_ms.append(float(np.median(ts)))
-        step_flops += 10.0 * h * d * pk
+        step_ms.append(float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings])))
+        step_flops += 10.0 * h * d * ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src,
+                                                      causal=causal, layout=layout)
     kern_ms = sum(step_ms)
     achieved = step_flops / (kern_ms * 1e-3) / 1e12
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
@@ -399,7 +388,8 @@ def run_backward(args):
                      "kernel": "ra_step_bwd: bwd_dq_kernel + bwd_dkdv_kernel (10 h d FLOPs per "
                                "allowed pair; the kernels execute 14 h d)",
                      "launches": len(step_ms),
-                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4)},
+                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4),
+                     "timed_over": f"the {len(timings)} timed passes"},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
@@ -533,17 +523,20 @@ def run_ulysses(args):
                  torch.zeros((N, b, L, n_kv, d), device=dev, dtype=torch.float32))
         flops = flops * 10 // 4                      # five products per pair instead of two
 
+    parts = []          # forward: HIP events around the gather, attention and scatter of every pass
+
     def one_pass():
         if backward:
             ra.ulysses_bwd(q_all, k_all, v_all, o_all, dout_all, lse_all, head_group=group, causal=causal,
                            layout=layout, out=grads)
         else:
-            ra.ulysses_fwd(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout, workspace=ws,
-                           out=o_all, lse_out=lse_all)
+            parts.append(ra.ulysses_fwd_timed(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout,
+                                              workspace=ws, out=o_all, lse_out=lse_all)[2])
 
     for _ in range(args.warmup):
         one_pass()
     torch.cuda.synchronize()
+    parts.clear()
     ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
@@ -559,9 +552,7 @@ def run_ulysses(args):
                              "pct_of_bf16_peak": round(100 * value / accounting.MI355X_BF16_DENSE_TFLOPS, 2)}}
         print(json.dumps(result), flush=True)
         return
-    parts = [ra.ulysses_fwd_timed(q_all, k_all, v_all, head_group=group, causal=causal, layout=layout,
-                                  workspace=ws, out=o_all, lse_out=lse_all)[2] for _ in range(3)]
-    tm = {k: float(np.median([t[k] for t in parts])) for k in parts[0]}
+    tm = {k: float(np.mean([t[k] for t in parts])) for k in parts[0]}
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
     achieved = flops / (tm["attend_ms"] * 1e-3) / 1e12
     es, hg, kg = 2, h // N, n_kv // N
@@ -590,7 +581,8 @@ def run_ulysses(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": "step_fwd_bf16_kernel<MODE_PART> over the whole sequence",
-                     "launches": 1, "avg_launch_ms": round(tm["attend_ms"], 4)},
+                     "launches": 1, "avg_launch_ms": round(tm["attend_ms"], 4),
+                     "timed_over": f"the {len(parts)} timed passes"},
         "exchange": {"gather_ms": round(tm["gather_ms"], 4), "scatter_ms": round(tm["scatter_ms"], 4),
                      "gather_GBps": round(gather_bytes / (tm["gather_ms"] * 1e-3) / 1e9, 1),
                      "scatter_GBps": round(scatter_bytes / (tm["scatter_ms"] * 1e-3) / 1e9, 1),
@@ -823,30 +815,31 @@ def main():
     flops = accounting.flops_from_pairs(pairs, h, d)
     compute = torch.cuda.current_stream()
 
+    # Every pass records HIP events around each step kernel and each staging copy on the
+    # streams they run on (ra_ring_fwd_timed); the roofline's launch durations come from
+    # the timed passes themselves.
+    timings = []
+
     def one_pass():
-        ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws,
-                    out=o, lse_out=lse, docs=docs)
+        timings.append(ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
+                                         workspace=ws, out=o, lse_out=lse, docs=docs)[2])
 
     for i in range(args.warmup):
         one_pass()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
     torch.cuda.synchronize()
+    timings.clear()
     ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
 
-    # Per-launch durations of the step kernel, from HIP events on the compute stream.
-    step_ms, live_flops, timings = [], 0, []
-    for _ in range(3):
-        _, _, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
-                                     workspace=ws, out=o, lse_out=lse, docs=docs)
-        timings.append(tm)
-    tm = timings[-1]
+    step_ms, live_flops = [], 0
     for k in range(N):
         src = (shard - k) % N
-        if tm["step_begin_ms"][k] >= 0:
-            step_ms.append(tm["step_end_ms"][k] - tm["step_begin_ms"][k])
+        if timings[0]["step_begin_ms"][k] >= 0:
+            step_ms.append(float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings])))
             live_flops += accounting.flops_from_pairs(pairs_of(src), h, d)
+    tm = sorted(timings, key=lambda t: t["total_ms"])[len(timings) // 2]   # the median pass
     kern_ms = sum(step_ms)
     achieved = live_flops / (kern_ms * 1e-3) / 1e12
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
@@ -890,7 +883,8 @@ def main():
                      "traffic": measured_traffic() if args.workload == DEFAULT_WORKLOAD else None,
                      "kernel": "step_fwd_bf16_kernel<MODE_MERGE/MODE_PART>",
                      "launches": len(step_ms),
-                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4)},
+                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4),
+                     "timed_over": f"the {len(timings)} timed passes"},
         "staging": {"kv_bytes_per_step": kv_bytes,
                     "copy_ms": [round(x, 4) for x in copy_ms],
                     "copy_GBps": [round(2 * kv_bytes / (x * 1e-3) / 1e9, 1) for x in copy_ms if x > 0],

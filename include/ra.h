@@ -196,6 +196,14 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t q_shard, const void* q, const
                       float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
                       ra_stream compute, ra_stream copy);
 
+/* ra_ring_bwd plus per-step timings (as ra_ring_fwd_timed: the step of ring step k is its
+ * ra_step_bwd, the copy that of its KV shard; ms from entry, -1 for skipped steps); waits
+ * for the pass to finish before returning.  N <= RA_MAX_TIMED_STEPS. */
+ra_status ra_ring_bwd_timed(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                            const void* v_all, const void* o, const void* dout, const float* lse,
+                            float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
+                            ra_stream compute, ra_stream copy, ra_ring_timing* t);
+
 /* ra_ring_bwd_kv_stationary — the other gradient schedule (page 1, "The Backward Pass and
  * Gradient Exchange": output gradients circulate in reverse ring order while keys and
  * values stay where they are): device kv_shard keeps its k, v [b][L][n_kv][d] and, at step

@@ -383,10 +383,12 @@ def ring_bwd_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", sca
 
 
 def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",
-             scale=None, stream=None, copy_stream="auto", workspace=None, out=None, docs=None):
+             scale=None, stream=None, copy_stream="auto", workspace=None, out=None, docs=None,
+             timed=False):
     """Backward ring pass of device q_shard.  q, o, dout [b, L, h, d] (bf16), lse [b, h, L]
     from the forward, k_all, v_all [N, b, L, n_kv, d].  Returns fp32 (dq [b, L, h, d],
-    dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d]), written into `out` when given."""
+    dk_all [N, b, L, n_kv, d], dv_all [N, b, L, n_kv, d]), written into `out` when given;
+    timed=True adds per-step timings (as ring_fwd_timed) and synchronises."""
     N, b, L, n_kv, d = k_all.shape
     h = q.shape[2]
     _need(q, "q", (b, L, h, d), q.dtype)
@@ -415,12 +417,18 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
     if workspace.numel() < need:
         raise RaError(int(_lib.RA_ERR_WORKSPACE), "ra_ring_bwd")
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
-    check(_lib.lib().ra_ring_bwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
-                                 _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 _ptr(workspace), workspace.numel(), _stream(stream),
-                                 ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
-          "ra_ring_bwd")
-    return dq, dk, dv
+    args = (ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all), _ptr(o), _ptr(dout), _ptr(lse),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream),
+            ctypes.c_void_p(cs.cuda_stream) if cs is not None else None)
+    if not timed:
+        check(_lib.lib().ra_ring_bwd(*args), "ra_ring_bwd")
+        return dq, dk, dv
+    tm = RaRingTiming()
+    check(_lib.lib().ra_ring_bwd_timed(*args, ctypes.byref(tm)), "ra_ring_bwd_timed")
+    n = tm.n_steps
+    return dq, dk, dv, {"step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
+                        "copy_begin_ms": list(tm.copy_begin_ms[:n]), "copy_end_ms": list(tm.copy_end_ms[:n]),
+                        "total_ms": tm.total_ms}
 
 
 def ring_bwd_kv_stationary(k, v, q_all, dout_all, lse_all, delta_all, *, kv_shard, causal=False,

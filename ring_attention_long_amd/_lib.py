@@ -63,6 +63,8 @@ SIGNATURES = [
     ("ra_step_bwd", _I, [_P, _I, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     ("ra_ring_bwd_workspace", _S, [_P]),
     ("ra_ring_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
+    ("ra_ring_bwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V,
+                               ctypes.POINTER(RaRingTiming)]),
     ("ra_ring_bwd_kv_stationary_workspace", _S, [_P]),
     ("ra_ring_bwd_kv_stationary", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_ulysses_fwd_workspace", _S, [_P]),

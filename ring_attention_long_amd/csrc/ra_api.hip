@@ -433,6 +433,127 @@ size_t ring_bwd_workspace(const ra_problem* p) {
   return 4 * align_up(shard_bytes, 256) + align_up((size_t)p->b * p->h * p->L * 4, 256);
 }
 
+// The backward ring pass (ra_ring_bwd), optionally timed per step as ra_ring_fwd_timed.
+ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all, const void* v_all,
+                        const void* o, const void* dout, const float* lse, float* dq, float* dk_all, float* dv_all,
+                        void* ws, size_t ws_bytes, ra_stream compute, ra_stream copy, ra_ring_timing* tm) {
+  RA_TRY(check_bwd_problem(p));
+  RA_TRY(check_shard(p, qs, "q_shard"));
+  RA_TRY(check_ptr(q, "q", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o, "o", 16));
+  RA_TRY(check_ptr(dout, "dout", 16));
+  RA_TRY(check_ptr(lse, "lse", 4));
+  RA_TRY(check_ptr(dq, "dq", 16));
+  RA_TRY(check_ptr(dk_all, "dk_all", 16));
+  RA_TRY(check_ptr(dv_all, "dv_all", 16));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const size_t need = ring_bwd_workspace(p);
+  if (ws_bytes < need) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const int N = p->N;
+  if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
+  if (tm && N > RA_MAX_TIMED_STEPS)
+    return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
+  const bool timing = tm != nullptr;
+
+  const size_t shard_elems = (size_t)p->b * p->L * p->n_kv * p->d;
+  const size_t shard_bytes = shard_elems * elem_size(p);
+  const size_t A = align_up(shard_bytes, 256);
+  char* wsc = (char*)ws;
+  char* kbuf[2] = {wsc, wsc + 2 * A};
+  char* vbuf[2] = {wsc + A, wsc + 3 * A};
+  float* delta = (float*)(wsc + 4 * A);
+  const hipStream_t cs = (hipStream_t)compute;
+  const hipStream_t ps = copy ? (hipStream_t)copy : cs;
+  const bool split = ps != cs;
+
+  Events ev;
+  hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
+  hipEvent_t t_sb[RA_MAX_TIMED_STEPS], t_se[RA_MAX_TIMED_STEPS], t_cb[RA_MAX_TIMED_STEPS],
+      t_ce[RA_MAX_TIMED_STEPS];
+  hipError_t e;
+  if ((e = ev.make(&entry, timing)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  for (int k = 0; k < N; ++k) {
+    if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  bool live[kMaxRing];
+  if (timing) {
+    tm->n_steps = N;
+    for (int k = 0; k < N; ++k) {
+      tm->step_begin_ms[k] = tm->step_end_ms[k] = tm->copy_begin_ms[k] = tm->copy_end_ms[k] = -1.f;
+      if ((e = ev.make(&t_sb[k], true)) != hipSuccess || (e = ev.make(&t_se[k], true)) != hipSuccess ||
+          (e = ev.make(&t_cb[k], true)) != hipSuccess || (e = ev.make(&t_ce[k], true)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+    }
+  }
+  // zero the gradient outputs, then D = rowsum(dO * O)
+  const int64_t n_q = (int64_t)p->b * p->L * p->h * p->d;
+  if ((e = ra::launch_fill_lse(dq, n_q, 0.f, cs)) != hipSuccess) return hip_fail(e, "fill kernel launch");
+  if ((e = ra::launch_fill_lse(dk_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
+    return hip_fail(e, "fill kernel launch");
+  if ((e = ra::launch_fill_lse(dv_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
+    return hip_fail(e, "fill kernel launch");
+  if ((e = ra::launch_bwd_preprocess(o, dout, delta, p->b, p->L, p->h, cs)) != hipSuccess)
+    return hip_fail(e, "preprocess kernel launch");
+  if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (split && (e = hipStreamWaitEvent(ps, entry, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+
+  const char* kc = (const char*)k_all;
+  const char* vc = (const char*)v_all;
+  for (int k = 0; k < N; ++k) {
+    if (k + 1 < N) {
+      const int dst = (k + 1) & 1;
+      const int src = ((qs - (k + 1)) % N + N) % N;
+      if (split && k - 1 >= 1 && (e = hipStreamWaitEvent(ps, consumed[k - 1], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      if (timing && (e = hipEventRecord(t_cb[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipMemcpyAsync(kbuf[dst], kc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(K)");
+      if ((e = hipMemcpyAsync(vbuf[dst], vc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(V)");
+      if (timing && (e = hipEventRecord(t_ce[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipEventRecord(staged[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if (split && k >= 1 && (e = hipStreamWaitEvent(cs, staged[k], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+    const int src = ((qs - k) % N + N) % N;
+    const void* kp = k == 0 ? (const void*)(kc + (size_t)qs * shard_bytes) : (const void*)kbuf[k & 1];
+    const void* vp = k == 0 ? (const void*)(vc + (size_t)qs * shard_bytes) : (const void*)vbuf[k & 1];
+    live[k] = step_is_live(p, qs, src);
+    if (live[k]) {
+      if (timing && (e = hipEventRecord(t_sb[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, nullptr, nullptr);
+      if ((e = ra::launch_step_bwd_bf16(a, dout, lse, delta, dq, dk_all + (size_t)src * shard_elems,
+                                        dv_all + (size_t)src * shard_elems, cs)) != hipSuccess)
+        return hip_fail(e, "backward step kernel launch");
+      if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if (timing) {
+    hipEvent_t done;
+    if ((e = ev.make(&done, true)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventRecord(done, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipEventSynchronize(done)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    (void)hipEventElapsedTime(&tm->total_ms, entry, done);
+    for (int k = 0; k < N; ++k) {
+      if (live[k]) {
+        (void)hipEventElapsedTime(&tm->step_begin_ms[k], entry, t_sb[k]);
+        (void)hipEventElapsedTime(&tm->step_end_ms[k], entry, t_se[k]);
+      }
+      if (k >= 1) {
+        (void)hipEventElapsedTime(&tm->copy_begin_ms[k], entry, t_cb[k]);
+        (void)hipEventElapsedTime(&tm->copy_end_ms[k], entry, t_ce[k]);
+      }
+    }
+  }
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -548,84 +669,16 @@ ra_status ra_ring_bwd(const ra_problem* p, int32_t qs, const void* q, const void
                       const void* v_all, const void* o, const void* dout, const float* lse,
                       float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
                       ra_stream compute, ra_stream copy) {
-  RA_TRY(check_bwd_problem(p));
-  RA_TRY(check_shard(p, qs, "q_shard"));
-  RA_TRY(check_ptr(q, "q", 16));
-  RA_TRY(check_ptr(k_all, "k_all", 16));
-  RA_TRY(check_ptr(v_all, "v_all", 16));
-  RA_TRY(check_ptr(o, "o", 16));
-  RA_TRY(check_ptr(dout, "dout", 16));
-  RA_TRY(check_ptr(lse, "lse", 4));
-  RA_TRY(check_ptr(dq, "dq", 16));
-  RA_TRY(check_ptr(dk_all, "dk_all", 16));
-  RA_TRY(check_ptr(dv_all, "dv_all", 16));
-  RA_TRY(check_ptr(ws, "ws", 16));
-  const size_t need = ring_bwd_workspace(p);
-  if (ws_bytes < need) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-  const int N = p->N;
-  if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
+  return ring_bwd_impl(p, qs, q, k_all, v_all, o, dout, lse, dq, dk_all, dv_all, ws, ws_bytes, compute, copy,
+                       nullptr);
+}
 
-  const size_t shard_elems = (size_t)p->b * p->L * p->n_kv * p->d;
-  const size_t shard_bytes = shard_elems * elem_size(p);
-  const size_t A = align_up(shard_bytes, 256);
-  char* wsc = (char*)ws;
-  char* kbuf[2] = {wsc, wsc + 2 * A};
-  char* vbuf[2] = {wsc + A, wsc + 3 * A};
-  float* delta = (float*)(wsc + 4 * A);
-  const hipStream_t cs = (hipStream_t)compute;
-  const hipStream_t ps = copy ? (hipStream_t)copy : cs;
-  const bool split = ps != cs;
-
-  Events ev;
-  hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
-  hipError_t e;
-  if ((e = ev.make(&entry, false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-  for (int k = 0; k < N; ++k) {
-    if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-    if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-  }
-  // zero the gradient outputs, then D = rowsum(dO * O)
-  const int64_t n_q = (int64_t)p->b * p->L * p->h * p->d;
-  if ((e = ra::launch_fill_lse(dq, n_q, 0.f, cs)) != hipSuccess) return hip_fail(e, "fill kernel launch");
-  if ((e = ra::launch_fill_lse(dk_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
-    return hip_fail(e, "fill kernel launch");
-  if ((e = ra::launch_fill_lse(dv_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
-    return hip_fail(e, "fill kernel launch");
-  if ((e = ra::launch_bwd_preprocess(o, dout, delta, p->b, p->L, p->h, cs)) != hipSuccess)
-    return hip_fail(e, "preprocess kernel launch");
-  if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (split && (e = hipStreamWaitEvent(ps, entry, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-
-  const char* kc = (const char*)k_all;
-  const char* vc = (const char*)v_all;
-  for (int k = 0; k < N; ++k) {
-    if (k + 1 < N) {
-      const int dst = (k + 1) & 1;
-      const int src = ((qs - (k + 1)) % N + N) % N;
-      if (split && k - 1 >= 1 && (e = hipStreamWaitEvent(ps, consumed[k - 1], 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-      if ((e = hipMemcpyAsync(kbuf[dst], kc + (size_t)src * shard_bytes, shard_bytes,
-                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(K)");
-      if ((e = hipMemcpyAsync(vbuf[dst], vc + (size_t)src * shard_bytes, shard_bytes,
-                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(V)");
-      if ((e = hipEventRecord(staged[k + 1], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
-    if (split && k >= 1 && (e = hipStreamWaitEvent(cs, staged[k], 0)) != hipSuccess)
-      return hip_fail(e, "hipStreamWaitEvent");
-    const int src = ((qs - k) % N + N) % N;
-    const void* kp = k == 0 ? (const void*)(kc + (size_t)qs * shard_bytes) : (const void*)kbuf[k & 1];
-    const void* vp = k == 0 ? (const void*)(vc + (size_t)qs * shard_bytes) : (const void*)vbuf[k & 1];
-    if (step_is_live(p, qs, src)) {
-      const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, nullptr, nullptr);
-      if ((e = ra::launch_step_bwd_bf16(a, dout, lse, delta, dq, dk_all + (size_t)src * shard_elems,
-                                        dv_all + (size_t)src * shard_elems, cs)) != hipSuccess)
-        return hip_fail(e, "backward step kernel launch");
-    }
-    if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  return RA_OK;
+ra_status ra_ring_bwd_timed(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
+                            const void* v_all, const void* o, const void* dout, const float* lse,
+                            float* dq, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
+                            ra_stream compute, ra_stream copy, ra_ring_timing* t) {
+  if (!t) return fail(RA_ERR_INVALID_ARG, "timing output is NULL");
+  return ring_bwd_impl(p, qs, q, k_all, v_all, o, dout, lse, dq, dk_all, dv_all, ws, ws_bytes, compute, copy, t);
 }
 
 size_t ra_ring_bwd_kv_stationary_workspace(const ra_problem* p) {

@@ -101,6 +101,11 @@ def test_ring_fwd_rejects_small_workspace():
     assert st == _lib.RA_ERR_WORKSPACE
     assert lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                                  None, None, None) == _lib.RA_ERR_INVALID_ARG
+    bneed = lib.ra_ring_bwd_workspace(ctypes.byref(p))
+    assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 bneed, None, None, None) == _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 bneed - 1, None, None, ctypes.byref(tm)) == _lib.RA_ERR_WORKSPACE
 
 
 def _no_hip_device():

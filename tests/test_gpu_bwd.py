@@ -136,3 +136,23 @@ def test_config5_full_size(shard):
         valid = first < L
         want[j][valid] = suffix[first[valid]]
     check_grad(dv0[:, 0], want, "config5 dV closed form (Q = 0)")
+
+
+def test_ring_bwd_timed_matches_untimed():
+    """The timed pass gives bit-identical gradients; every live step has an interval inside the
+    pass, skipped steps report -1, and each staged copy ends before its step begins."""
+    cfg = dict(b=1, L=192, h=8, n_kv=2, d=128, N=4)
+    inp = make_inputs(**cfg, q_shard=1, seed=97, dtype="bf16", with_dout=True)
+    q, k_all, v_all, dout = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all", "dout"))
+    o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=1, causal=True, layout="contiguous")
+    announce("ring_bwd timed vs untimed, contiguous causal shard 1")
+    a = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=1, causal=True, layout="contiguous")
+    *b, tm = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=1, causal=True, layout="contiguous", timed=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    live = [k for k in range(4) if tm["step_begin_ms"][k] >= 0]
+    assert live == [0, 1]          # contiguous causal: shard 1 sees shards 1 and 0 only
+    for k in live:
+        assert 0 <= tm["step_begin_ms"][k] < tm["step_end_ms"][k] <= tm["total_ms"]
+        if k >= 1:
+            assert tm["copy_end_ms"][k] <= tm["step_begin_ms"][k] + 1e-3
