@@ -599,6 +599,46 @@ def run_ulysses(args):
     print(json.dumps(result), flush=True)
 
 
+def run_hbm_kernels(args):
+    """The HBM-bound pieces alone, at the S = 262144, N = 8 one-device shapes (L = 32768,
+    h = 32, n_kv = 8, d = 128): the standalone LSE merge (ra_merge_lse), the finalize
+    (ra_finalize, fp32 -> bf16), and a device-to-device copy of one K (or V) shard, the same
+    runtime copy the ring's staging issues.  GB/s from HIP events over `steps` calls each."""
+    import torch
+
+    import ring_attention_long_amd as ra
+    from ring_attention_long_amd import accounting
+
+    b, L, h, n_kv, d = 1, 32768, 32, 8, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1009)
+    oa = torch.randn((b, L, h, d), device=dev, generator=gen)
+    op = torch.randn((b, L, h, d), device=dev, generator=gen)
+    la = torch.randn((b, h, L), device=dev, generator=gen)
+    lp = torch.randn((b, h, L), device=dev, generator=gen)
+    kv = torch.randn((b, L, n_kv, d), device=dev, generator=gen).to(torch.bfloat16)
+    kv_dst = torch.empty_like(kv)
+
+    def rate(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        return {"ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+    res = {"merge_lse": rate(lambda: ra.merge_lse(oa, la, op, lp), accounting.merge_bytes(b, L, h, d)),
+           "finalize_bf16": rate(lambda: ra.finalize(oa), 6 * b * L * h * d),
+           "kv_shard_copy": rate(lambda: kv_dst.copy_(kv), 2 * kv.numel() * 2)}
+    print(json.dumps({"hbm_kernels": res, "peak_GBps": accounting.MI355X_HBM_GBPS, "steps": args.steps,
+                      "shapes": {"b": b, "L": L, "h": h, "n_kv": n_kv, "d": d}}), flush=True)
+
+
 def run_sweep(args):
     """Where the time goes across sizes and shards (timing only: inputs are seeded
     torch.randn bf16 on the GPU; attention time does not depend on the values)."""
@@ -757,6 +797,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of one workload: L sweep of the striped causal ring pass, every "
                          "shard of each causal layout at L=32768, copy interference, merge GB/s")
+    ap.add_argument("--hbm-kernels", action="store_true",
+                    help="instead of a workload: the LSE merge, the finalize and a K/V shard copy "
+                         "alone, with their HBM GB/s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -774,6 +817,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         return run_sweep(args)
+    if args.hbm_kernels:
+        return run_hbm_kernels(args)
     if args.workload in BWD_WORKLOADS:
         return run_backward(args)
     if args.workload in ULYSSES_WORKLOADS:
