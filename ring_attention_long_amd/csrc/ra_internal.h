@@ -83,6 +83,37 @@ __host__ __device__ inline int kv_limit(int causal, int layout, int N, int L, in
   return (int)clamp64(P - (int64_t)ks * L + 1, 0, L);
 }
 
+// The same limit as two clamped linear pieces, for kernels that evaluate it per tile on the
+// scalar unit: kv_limit(t) = clamp(t + o1, 0, c1) + clamp(t + o2, 0, c2), with (o1, o2) =
+// (o1a, o2a) for t < split and (o1b, o2b) otherwise.  Zigzag needs both pieces (the shard's
+// two chunks, split at L/2); the other layouts one.  Offsets are clamped to [-(L+2), L+2],
+// which leaves every clamp of t + o for 0 <= t < L unchanged.
+struct KvForm {
+  int split, o1a, o2a, o1b, o2b, c1, c2;
+};
+inline KvForm make_kv_form(int causal, int layout, int N, int L, int qs, int ks) {
+  auto c = [&](int64_t o) { return (int)clamp64(o, -(int64_t)L - 2, (int64_t)L + 2); };
+  if (!causal) return KvForm{0, 0, 0, L, 0, L, 0};
+  if (layout == RA_LAYOUT_STRIPED) {
+    const int o = qs >= ks ? 1 : 0;
+    return KvForm{0, o, 0, o, 0, L, 0};
+  }
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    const int64_t C = L / 2;
+    return KvForm{(int)C,
+                  c((int64_t)(qs - ks) * C + 1), c((int64_t)(qs + ks - 2 * N + 1) * C + 1),
+                  c((int64_t)(2 * N - 2 - qs - ks) * C + 1), c((int64_t)(ks - qs - 1) * C + 1),
+                  (int)C, (int)C};
+  }
+  const int o = c((int64_t)(qs - ks) * L + 1);
+  return KvForm{0, o, 0, o, 0, L, 0};
+}
+__host__ __device__ inline int kv_form_eval(const KvForm& f, int t) {
+  const bool lo = t < f.split;
+  const int a = t + (lo ? f.o1a : f.o1b), b = t + (lo ? f.o2a : f.o2b);
+  return (a < 0 ? 0 : (a > f.c1 ? f.c1 : a)) + (b < 0 ? 0 : (b > f.c2 ? f.c2 : b));
+}
+
 // ---------------------------------------------------------------------------------------
 // Asynchronous global -> LDS copy (buffer_load_dwordx4 ... lds): every lane moves the 16
 // bytes at voffset + soffset of the buffer to LDS address lds_base + 16 * lane.  Reads at

@@ -13,10 +13,10 @@
 //    dO^T resident in VGPRs; lane l holds one query's scores, so LSE and D are one value
 //    per lane; dQ^T += K^T dS^T with K^T read by the transposing LDS load.  Eight waves in
 //    the forward's ping-pong.
-//  * dK/dV kernel (key-major): each wave keeps K and V rows of 32 keys in VGPRs and walks
-//    the query tiles of every head of its KV group; S = Q K^T and dP = dO V^T put one key
-//    per lane, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and Q^T from transposing LDS
-//    loads.  No atomics: every workgroup owns its keys.
+//  * dK/dV kernel (key-major): each wave keeps the K rows of 32 keys in VGPRs (their V rows
+//    in LDS) and walks the query tiles of every head of its KV group; S = Q K^T and
+//    dP = dO V^T put one key per lane, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and
+//    Q^T from transposing LDS loads.  No atomics: every workgroup owns its keys.
 // Recomputing S and dP in both kernels costs two extra products per pair (7 instead of 5)
 // and buys two independent kernels with no transposes of dS.
 //
@@ -126,10 +126,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
 // Wave w owns keys 32 (w % 4) .. +31 of the workgroup and rows 32 (w / 4) .. +31 of each
 // query tile, so the two waves on a SIMD share their keys and split the rows.  Per tile a
 // wave runs a matrix phase (dV^T += dO^T P and dK^T += Q^T dS of the previous tile, then
-// S = Q K^T and dP = dO V^T of this tile: 32 products) and a vector phase (P, dS of this
-// tile).  The two groups (w / 4 = 0, 1) run half a tile apart, separated by workgroup
-// barriers, so that while one wave of a SIMD issues products the other does its vector
-// work.  The two row halves' dK and dV are summed through LDS at the end.
+// S = Q K^T and dP = dO V^T of this tile: 32 products, plus 2 that subtract the row's
+// LSE / scale and D, see xq_lds) and a vector phase (P, dS of this tile, no memory reads
+// outside diagonal tiles).  The two groups (w / 4 = 0, 1) run half a tile apart, separated
+// by workgroup barriers, so that while one wave of a SIMD issues products the other does
+// its vector work.  The two row halves' dK and dV are summed through LDS at the end.
 // K rows stay in VGPRs; V rows of the 128 keys stay in LDS.  Q and dO tiles rotate
 // through three LDS stages (a tile is read during four consecutive half steps and loaded
 // during the two before).
@@ -153,12 +154,20 @@ __device__ __forceinline__ void barrier_no_fence() {
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, const __bf16* __restrict__ dout,
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ delta,
-                                                                 float* __restrict__ dk, float* __restrict__ dv) {
+                                                                 float* __restrict__ dk, float* __restrict__ dv,
+                                                                 KvForm kf) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
-  __shared__ __attribute__((aligned(16))) float lse_lds[N_STAGE][TILE_ROWS];   // -LSE log2(e)
-  __shared__ __attribute__((aligned(16))) float dlt_lds[N_STAGE][TILE_ROWS];
+  // Per row of a staged tile, one more 16-wide k-step for the products S = Q K^T and
+  // dP = dO V^T: columns 0 and 1 hold the bf16 pair (hi, lo) of -LSE / scale (S) or -D (dP),
+  // the other columns zeros, and the matching K^T / V^T rows are ones.  The products then
+  // come out as S - LSE / scale and dP - D, so the vector phase reads no statistics.
+  __shared__ __attribute__((aligned(16))) __bf16 xq_lds[N_STAGE][TILE_ROWS][16];
+  __shared__ __attribute__((aligned(16))) __bf16 xo_lds[N_STAGE][TILE_ROWS][16];
   __shared__ __attribute__((aligned(16))) int lo_lds[N_STAGE][TILE_ROWS];   // allowed keys [lo, hi)
   __shared__ __attribute__((aligned(16))) int hi_lds[N_STAGE][TILE_ROWS];
+  // per stage and 32-row half: the key bounds of the half's first and last row inside the
+  // shard, (lo_first, hi_first, lo_last, hi_last)
+  __shared__ __attribute__((aligned(16))) int cls_lds[N_STAGE][2][4];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = wave & 3, grp = wave >> 2;
@@ -174,7 +183,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // allowed keys of query row t: [lo, hi), both nondecreasing in t (see key_range)
   const bool packed = a.doc_begin != nullptr;
   auto range_of = [&](int row, int64_t db, int64_t de) {
-    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+    // the shard indices pass through an empty asm so that what is derived from them is
+    // recomputed here rather than kept in registers through the main loop
+    int qs = a.q_shard, ks = a.kv_shard;
+    __asm__ volatile("" : "+s"(qs), "+s"(ks));
+    return key_range(a.causal, a.layout, a.N, L, qs, ks, row, packed, db, de);
   };
   auto range = [&](int row) {
     int64_t db = 0, de = 0;
@@ -251,25 +264,56 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     }
   };
   const Cursor first = {g * G, qt_first * TILE_ROWS};
-  auto stage_dma = [&](const Cursor& c, int buf) {   // group 1 only: Q and dO rows of a tile
-    const int64_t base = ((int64_t)bi * L * a.h + c.hq) * D;
-    char* dst = smem + buf * STAGE_BYTES;
-    dma_tile(rows_rsrc((const __bf16*)a.q + base, L, q_stride), dst, q_lane_off, (unsigned)c.tq0 * q_stride,
-             q_stride, wq);
-    dma_tile(rows_rsrc(dout + base, L, q_stride), dst + TILE_BYTES, q_lane_off, (unsigned)c.tq0 * q_stride,
-             q_stride, wq);
+  // Q and dO rows of batch bi: one descriptor each over its L rows of all heads, so that
+  // rows past the shard end read zeros; the head and row go into the scalar offset.
+  const dma_rsrc q_rsrc = make_dma_rsrc((const __bf16*)a.q + (int64_t)bi * L * a.h * D, (unsigned)L * q_stride);
+  const dma_rsrc o_rsrc = make_dma_rsrc(dout + (int64_t)bi * L * a.h * D, (unsigned)L * q_stride);
+  // Load k (0..7) of this wave's share of a tile: k < 4 the Q rows, k >= 4 the dO rows;
+  // load i = wq + 4 (k % 4) of the 16 that fill a tile (see dma_tile).
+  auto stage_dma_one = [&](const Cursor& c, int buf, int k) __attribute__((always_inline)) {
+    const int i = wq + 4 * (k & 3);
+    char* dst = smem + buf * STAGE_BYTES + (k >> 2) * TILE_BYTES + 1024 * i;
+    dma16_to_lds(k < 4 ? q_rsrc : o_rsrc, dst, q_lane_off,
+                 (unsigned)c.hq * ROW_BYTES + (unsigned)(c.tq0 + 4 * i) * q_stride);
+  };
+  auto stage_dma = [&](const Cursor& c, int buf) {   // group 1: all eight
+#pragma unroll
+    for (int k = 0; k < 8; ++k) stage_dma_one(c, buf, k);
   };
   auto stats_index = [&](const Cursor& c) {
     return ((int64_t)bi * a.h + c.hq) * L + min(c.tq0 + lane, L - 1);
   };
   auto doc_index = [&](const Cursor& c) { return (int64_t)bi * L + min(c.tq0 + lane, L - 1); };
+  const float inv_scale = 1.0f / a.scale;
   auto stats_store = [&](const Cursor& c, int buf, float l, float dl, int db, int de) {
     const int row = c.tq0 + lane;
-    lse_lds[buf][lane] = (row < L && l > -INFINITY) ? -l * LOG2E : -INFINITY;
-    dlt_lds[buf][lane] = dl;
+    // exp2(c2 (S + hi + lo)) = exp(scale S - LSE) with hi + lo = -LSE / scale to about 16
+    // bits; rows past the shard end, or with no key anywhere, get -1e30 (weights 0)
+    const float xs = (row < L && l > -INFINITY) ? -l * inv_scale : -1e30f;
+    const float xd = -dl;
+    const __bf16 xs_hi = (__bf16)xs, xd_hi = (__bf16)xd;
+    bf16x8 vs = {}, vd = {};
+    vs[0] = xs_hi;
+    vs[1] = (__bf16)(xs - (float)xs_hi);
+    vd[0] = xd_hi;
+    vd[1] = (__bf16)(xd - (float)xd_hi);
+    *(bf16x8*)&xq_lds[buf][lane][0] = vs;
+    *(bf16x8*)&xq_lds[buf][lane][8] = bf16x8{};
+    *(bf16x8*)&xo_lds[buf][lane][0] = vd;
+    *(bf16x8*)&xo_lds[buf][lane][8] = bf16x8{};
+    if (!packed) return;                    // key bounds from kf instead
     const KeyRange r = row < L ? range_of(row, db, de) : KeyRange{0, 0};
     lo_lds[buf][lane] = r.lo;
     hi_lds[buf][lane] = r.hi;
+    const int half = lane >> 5;
+    if ((lane & 31) == 0) {
+      cls_lds[buf][half][0] = r.lo;
+      cls_lds[buf][half][1] = r.hi;
+    }
+    if (lane == min(32 * half + 31, L - 1 - c.tq0)) {   // the half's last row in the shard
+      cls_lds[buf][half][2] = r.lo;
+      cls_lds[buf][half][3] = r.hi;
+    }
   };
   auto doc_b = [&](const Cursor& c) { return packed ? a.doc_begin[doc_index(c)] : 0; };
   auto doc_e = [&](const Cursor& c) { return packed ? a.doc_end[doc_index(c)] : 0; };
@@ -290,12 +334,25 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   Cursor cc = first;                          // tile of the current step
   Cursor cs = first;                          // next tile to stage
   if (grp == 1) stage_dma(cs, 0);
-  if (wave == 4) {
+  float st_l = 0.f, st_d = 0.f;             // statistics of a later tile in flight (wave 0)
+  int st_b = 0, st_e = 0;
+  auto stats_load = [&](const Cursor& c) {
+    const int64_t si = stats_index(c);
+    st_l = lse[si];
+    st_d = delta[si];
+    if (packed) {
+      st_b = a.doc_begin[doc_index(c)];
+      st_e = a.doc_end[doc_index(c)];
+    }
+  };
+  if (wave == 0) {                          // tiles 0 and 1 in place, tile 2 loading
     stats_store(cs, 0, lse[stats_index(cs)], delta[stats_index(cs)], doc_b(cs), doc_e(cs));
     Cursor c1 = cs;
     advance(c1);
     if (n_iter > 1)
       stats_store(c1, 1, lse[stats_index(c1)], delta[stats_index(c1)], doc_b(c1), doc_e(c1));
+    advance(c1);
+    if (n_iter > 2) stats_load(c1);
   }
   advance(cs);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V rows and tile 0 are in place
@@ -306,17 +363,31 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // extra barrier before the loop and group 0 one after it, so that between barriers 2j and
   // 2j+1 group 0 runs matrix phase j and group 1 vector phase j-1, and between 2j+1 and
   // 2j+2 group 0 runs vector phase j and group 1 matrix phase j.  Tile j (stage j % 3) is
-  // read from interval 2j+1 to 2j+4.  Group 1 starts the DMA of tile j as it enters its
-  // vector phase j-2 (interval 2j-1; the stage last held tile j-3, read up to interval 2j-2) and waits
-  // for it at the end of its matrix phase j-1 (interval 2j), one interval before tile j is
-  // first read.  Wave 4 loads the tile's statistics with it and stores them after the wait
-  // (first read in interval 2j+2).
+  // read from interval 2j+1 to 2j+4.  Group 1 starts the DMA of tile j in its vector phase
+  // j-2 (interval 2j-1; the stage last held tile j-3, read up to interval 2j-2) and waits for
+  // it at the end of its matrix phase j-1 (interval 2j), one interval before tile j is first
+  // read.  Wave 0 loads the tile's statistics in its vector phase j-2 (interval 2j-2) and
+  // stores them in its vector phase j-1 (interval 2j; first read in interval 2j+1).
   // Matrix phase of tile j (stage BCUR; the previous tile is in stage (BCUR + 2) % 3): 16
   // slots of two products, first dV^T += dO^T P and dK^T += Q^T dS of tile j - 1, then
   // S = Q K^T and dP = dO V^T of tile j.  Slot x issues the LDS reads of slot x + 2, then
   // its products; scheduling fences keep that order so the LDS latency hides behind four
   // products.  The LDS offsets are rebuilt from three base registers each phase (keeping
   // all of them live would not fit the 256 VGPRs of two waves per SIMD).
+  // The B operand [k][n = key] of the extra k-step: ones in rows 0 and 1 (and in rows 8 and
+  // 9, which meet the zero columns 8 and 9 of the A operand: one constant for every lane).
+  // Built where it is used: volatile moves are not hoisted, so the constant does not hold
+  // four VGPRs through the loop.
+  auto ones_op = []() __attribute__((always_inline)) {
+    unsigned w0, w1, w2, w3;
+    __asm__ volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(w0));
+    __asm__ volatile("v_mov_b32 %0, 0" : "=v"(w1));
+    __asm__ volatile("v_mov_b32 %0, 0" : "=v"(w2));
+    __asm__ volatile("v_mov_b32 %0, 0" : "=v"(w3));
+    return __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+  };
+  const unsigned x_off = (unsigned)lk * 32 + (unsigned)lg * 16;   // row lk, columns 8 lg ..
+  i32x4 cls_v = {};                                               // key bounds of the tile's half
   auto matrix_phase = [&](int bcur) __attribute__((always_inline)) {
     const int bprev = bcur == 0 ? 2 : bcur - 1;
     unsigned rb = r_base, tb0 = t_base[0], tb1 = t_base[1];
@@ -334,69 +405,77 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     const char* qp = smem + bprev * STAGE_BYTES + grp * 32 * ROW_BYTES;
     const char* op = qp + TILE_BYTES;
     const char* vt = smem + V_OFF + slot * 32 * ROW_BYTES;
+    const char* xq = (const char*)&xq_lds[bcur][32 * grp][0] + x_off;
+    const char* xo = (const char*)&xo_lds[bcur][32 * grp][0] + x_off;
     bf16x8 ra[3], rbv[3], rv[3];
     auto load = [&](int y) {
       if (y < 8) {
         ra[y % 3] = tr_op(op, y >> 2, y & 3);
         rbv[y % 3] = tr_op(qp, y >> 2, y & 3);
-      } else {
+      } else if (y < 16) {
         ra[y % 3] = row_op(qc, y - 8);
         rbv[y % 3] = row_op(oc, y - 8);
         rv[y % 3] = row_op(vt, y - 8);
+      } else {
+        ra[y % 3] = *(const bf16x8*)xq;
+        rbv[y % 3] = *(const bf16x8*)xo;
       }
     };
     load(0);
     load(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      if (x + 2 < 16) load(x + 2);
+    for (int x = 0; x < 17; ++x) {
+      if (x + 2 < 17) load(x + 2);
       if (x < 8) {
         dva[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], pb[x >> 2], dva[x & 3], 0, 0, 0);
         dka[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], ds[x >> 2], dka[x & 3], 0, 0, 0);
       } else if (x == 8) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], kop[0], f32x16{}, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], rv[x % 3], f32x16{}, 0, 0, 0);
-      } else {
+      } else if (x < 16) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], kop[x - 8], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], rv[x % 3], dp, 0, 0, 0);
+      } else {                                // S - LSE / scale, dP - D
+        const bf16x8 ones = ones_op();
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[x % 3], ones, sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rbv[x % 3], ones, dp, 0, 0, 0);
       }
+      // the tile's key bounds for the vector phase, read once the operand ring drains
+      if (x == 15) cls_v = *(const i32x4*)&cls_lds[bcur][grp][0];
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // accumulator layout: lane = key u, register i = row 8 (i / 4) + 4 lg + (i % 4) of the
-  // wave's 32-row half
-  auto vector_phase = [&](int j, int bcur) __attribute__((always_inline)) {
+  // wave's 32-row half.  sc and dp arrive as S - LSE / scale and dP - D.  `stage` (group 1's
+  // loads for a later tile) goes first so that its copies start early.
+  auto vector_phase = [&](int j, int bcur, auto&& stage) __attribute__((always_inline)) {
+    stage();
+    __builtin_amdgcn_sched_barrier(0);
     const int r0 = cc.tq0 + 32 * grp;
-    bool skip = j >= n_iter || r0 >= L;
-    bool full = false;
-    if (!skip) {
-      // the half's first row and last row inside the shard bound its key ranges
-      const int i0 = 32 * grp, i1 = min(32 * grp + 31, L - 1 - cc.tq0);
-      const int lo_first = __builtin_amdgcn_readfirstlane(lo_lds[bcur][i0]);
-      const int hi_first = __builtin_amdgcn_readfirstlane(hi_lds[bcur][i0]);
-      const int lo_last = __builtin_amdgcn_readfirstlane(lo_lds[bcur][i1]);
-      const int hi_last = __builtin_amdgcn_readfirstlane(hi_lds[bcur][i1]);
-      skip = hi_last <= uw || lo_first >= uw + 32;
-      full = hi_first >= uw + 32 && lo_last <= uw;   // rows past the shard end have LSE = -inf
+    // key bounds of the half's first and last row inside the shard: from the two-piece
+    // limit on the scalar unit, or with packed documents from the record of the tile
+    int lo_first = 0, hi_first, lo_last = 0, hi_last;
+    if (packed) {
+      lo_first = __builtin_amdgcn_readfirstlane(cls_v[0]);
+      hi_first = __builtin_amdgcn_readfirstlane(cls_v[1]);
+      lo_last = __builtin_amdgcn_readfirstlane(cls_v[2]);
+      hi_last = __builtin_amdgcn_readfirstlane(cls_v[3]);
+    } else {
+      hi_first = kv_form_eval(kf, r0);
+      hi_last = kv_form_eval(kf, min(r0 + 31, L - 1));
     }
-    skip = __builtin_amdgcn_readfirstlane((int)skip) != 0;
+    const bool skip = j >= n_iter || r0 >= L || hi_last <= uw || lo_first >= uw + 32;
+    const bool full = hi_first >= uw + 32 && lo_last <= uw;   // rows past the shard end have weight 0
     if (skip) {
       pb[0] = pb[1] = ds[0] = ds[1] = bf16x8{};
       return;
     }
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int rr = 32 * grp + 8 * q4 + 4 * lg;
-      const f32x4 l4 = *(const f32x4*)&lse_lds[bcur][rr];
-      const f32x4 d4 = *(const f32x4*)&dlt_lds[bcur][rr];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = 4 * q4 + x;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, l4[x]));
-        sc[i] = p;
-        dp[i] = p * (dp[i] - d4[x]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sc[i] * c2);
+      sc[i] = p;
+      dp[i] = p * dp[i];
     }
     if (!full) {
       // keep this a real (scalar) branch: only diagonal and boundary tiles pay for the mask
@@ -404,12 +483,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int rr = 32 * grp + 8 * q4 + 4 * lg;
-        const i32x4 lo4 = *(const i32x4*)&lo_lds[bcur][rr];
-        const i32x4 hi4 = *(const i32x4*)&hi_lds[bcur][rr];
+        i32x4 lo4 = {}, hi4;
+        if (packed) {
+          lo4 = *(const i32x4*)&lo_lds[bcur][rr];
+          hi4 = *(const i32x4*)&hi_lds[bcur][rr];
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) hi4[x] = kv_form_eval(kf, cc.tq0 + rr + x);
+        }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = 4 * q4 + x;
-          if (u >= hi4[x] || u < lo4[x]) {
+          if (u >= hi4[x] || u < lo4[x] || cc.tq0 + rr + x >= L) {
             sc[i] = 0.f;
             dp[i] = 0.f;
           }
@@ -425,8 +510,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
       }
   };
 
-  float st_l = 0.f, st_d = 0.f;             // statistics in flight (wave 4)
-  int st_b = 0, st_e = 0;
   if (grp == 1) {
     if (n_iter > 1) stage_dma(cs, 1);
     barrier_no_fence();
@@ -438,30 +521,28 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     __builtin_amdgcn_s_setprio(1);          // matrix phase first in the SIMD's issue arbitration
     matrix_phase(bcur);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads for tile j + 1 landed
-      if (wave == 4 && j >= 1 && j + 1 < n_iter) {
-        Cursor c1 = cc;
-        advance(c1);
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads for tile j + 1 landed
+    barrier_no_fence();
+    vector_phase(j, bcur, [&]() __attribute__((always_inline)) {
+      if (grp == 1 && j + 2 < n_iter) {
+        advance(cs);                        // cs: tile j + 2
+        stage_dma(cs, bnext2);
+      }
+    });
+    // Wave 0 stores the statistics of tile j + 1 (first read after the next barrier; its
+    // stage held tile j - 2, whose last reader finished at least two barriers earlier) and
+    // starts loading those of tile j + 2.  Group 0's vector phase is the short one.
+    if (wave == 0 && j >= 1) {
+      Cursor c1 = cc;
+      advance(c1);
+      if (j + 1 < n_iter) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the statistics of tile j + 1 landed
         stats_store(c1, bnext, st_l, st_d, st_b, st_e);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the barrier
       }
+      advance(c1);
+      if (j + 2 < n_iter) stats_load(c1);
     }
-    barrier_no_fence();
-    if (grp == 1 && j + 2 < n_iter) {
-      advance(cs);                          // cs: tile j + 2
-      stage_dma(cs, bnext2);
-      if (wave == 4) {
-        const int64_t si = stats_index(cs);
-        st_l = lse[si];
-        st_d = delta[si];
-        if (packed) {
-          st_b = a.doc_begin[doc_index(cs)];
-          st_e = a.doc_end[doc_index(cs)];
-        }
-      }
-    }
-    vector_phase(j, bcur);
     advance(cc);
     bcur = bnext;
     barrier_no_fence();
@@ -782,8 +863,9 @@ hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float
                      (const __bf16*)dout, lse, delta, dq, Hw, n_qb, inner);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const KvForm kf = make_kv_form(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_k), dim3(KV_THREADS), 0, s, a,
-                     (const __bf16*)dout, lse, delta, dk, dv);
+                     (const __bf16*)dout, lse, delta, dk, dv, kf);
   return hipGetLastError();
 }
 
