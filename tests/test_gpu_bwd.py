@@ -66,6 +66,42 @@ def test_ring_bwd_batch_and_tiny_shards():
             check_grad(dv, rdv, "dv edge")
 
 
+@pytest.mark.parametrize("layout", ["striped", "contiguous"])
+def test_ring_bwd_large_logits(layout):
+    """Q x 4 (exact in bf16): logits up to ~15 and |LSE| / scale ~ 150, where the dK/dV
+    kernel's bf16 (hi, lo) pair of -LSE / scale carries the most absolute error.  dQ and dV
+    pass the usual gates.  dK's largest error grows with the logit scale in bf16 (dS rounded
+    to bf16 meets larger Q): max abs 6.4e-2 at x4 and 0.16 at x8 on these inputs, the same
+    to three digits with the statistics read per row from LDS instead of folded into the
+    products, above the generic max gate; dK is held to the mean gate.  The normalisation of
+    P, which a wrong LSE would break, is checked by sum over keys of dV = sum over the
+    group's rows of dO (the dK identity's residual, bf16 noise of dS times Q, grows with
+    the scale of Q and is checked at unit scale in the full-size test)."""
+    cfg = dict(b=1, L=160, h=8, n_kv=2, d=128, N=4)
+    N, L, h, n_kv = 4, 160, 8, 2
+    shard = 2
+    inp = make_inputs(**cfg, q_shard=shard, seed=97, dtype="bf16", with_dout=True)
+    inp["q"] = inp["q"] * 4.0
+    q, k_all, v_all, dout = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all", "dout"))
+    announce("ring_bwd large logits", layout, cfg)
+    o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout)
+    dq, dk, dv = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=True, layout=layout)
+    torch.cuda.synchronize()
+    x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
+    rdq, rdk, rdv = shard_grads(x["q"], x["k_all"], x["v_all"], x["dout"], N=N, shard=shard,
+                                layout=layout, causal=True)
+    check_grad(dq, rdq, f"dq large logits {layout}")
+    check_grad(dv, rdv, f"dv large logits {layout}")
+    err = np.abs(f64(dk) - rdk)
+    scale = max(1.0, float(np.sqrt(np.mean(rdk ** 2))))
+    announce(f"dk large logits {layout}: max abs {err.max():.3e} mean abs {err.mean():.3e} (rms ref {scale:.3f})")
+    assert err.mean() <= 2e-3 * scale
+    dv_sum = f64(dv.sum(dim=(0, 2)))                       # [b, n_kv, d], over every key seen
+    do_sum = x["dout"].sum(axis=1).reshape(1, n_kv, h // n_kv, 128).sum(axis=2)
+    announce(f"sum dV err {np.abs(dv_sum - do_sum).max():.3e}")
+    assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.sqrt(L)
+
+
 def test_step_bwd_sums_to_ring_bwd():
     """ra_step_bwd over the ring order, with ra_bwd_preprocess, equals ra_ring_bwd."""
     cfg = dict(b=1, L=160, h=8, n_kv=2, d=128, N=4)
