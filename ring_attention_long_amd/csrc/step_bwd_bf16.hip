@@ -286,7 +286,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   auto doc_index = [&](const Cursor& c) { return (int64_t)bi * L + min(c.tq0 + lane, L - 1); };
   const float inv_scale = 1.0f / a.scale;
   auto stats_store = [&](const Cursor& c, int buf, float l, float dl, int db, int de) {
-    const int row = c.tq0 + lane;
+    // the lane index passes through an empty asm so that the LDS addresses below are formed
+    // here instead of being kept (and spilled) through the main loop
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int row = c.tq0 + ln;
     // exp2(c2 (S + hi + lo)) = exp(scale S - LSE) with hi + lo = -LSE / scale to about 16
     // bits; rows past the shard end, or with no key anywhere, get -1e30 (weights 0)
     const float xs = (row < L && l > -INFINITY) ? -l * inv_scale : -1e30f;
@@ -297,20 +301,20 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     vs[1] = (__bf16)(xs - (float)xs_hi);
     vd[0] = xd_hi;
     vd[1] = (__bf16)(xd - (float)xd_hi);
-    *(bf16x8*)&xq_lds[buf][lane][0] = vs;
-    *(bf16x8*)&xq_lds[buf][lane][8] = bf16x8{};
-    *(bf16x8*)&xo_lds[buf][lane][0] = vd;
-    *(bf16x8*)&xo_lds[buf][lane][8] = bf16x8{};
+    *(bf16x8*)&xq_lds[buf][ln][0] = vs;
+    *(bf16x8*)&xq_lds[buf][ln][8] = bf16x8{};
+    *(bf16x8*)&xo_lds[buf][ln][0] = vd;
+    *(bf16x8*)&xo_lds[buf][ln][8] = bf16x8{};
     if (!packed) return;                    // key bounds from kf instead
     const KeyRange r = row < L ? range_of(row, db, de) : KeyRange{0, 0};
-    lo_lds[buf][lane] = r.lo;
-    hi_lds[buf][lane] = r.hi;
-    const int half = lane >> 5;
-    if ((lane & 31) == 0) {
+    lo_lds[buf][ln] = r.lo;
+    hi_lds[buf][ln] = r.hi;
+    const int half = ln >> 5;
+    if ((ln & 31) == 0) {
       cls_lds[buf][half][0] = r.lo;
       cls_lds[buf][half][1] = r.hi;
     }
-    if (lane == min(32 * half + 31, L - 1 - c.tq0)) {   // the half's last row in the shard
+    if (ln == min(32 * half + 31, L - 1 - c.tq0)) {   // the half's last row in the shard
       cls_lds[buf][half][2] = r.lo;
       cls_lds[buf][half][3] = r.hi;
     }
