@@ -43,9 +43,10 @@
 //    wave skips every key tile at or beyond its largest limit, runs maskless below its
 //    smallest limit, and masks only the diagonal tiles in between.
 //  * K/V tiles rotate through three LDS stages each and are staged by DMA
-//    (buffer_load ... lds): no VGPRs and no vector instructions.  Each wave issues its
-//    four loads of a tile at the start of its softmax phase (group 0 V tiles, group 1 K
-//    tiles) and waits for them a whole step later.  V is stored row-major and read with
+//    (buffer_load ... lds): no VGPRs and no vector instructions.  Each wave's share of a
+//    tile is four 1 KB loads (group 0 V tiles, group 1 K tiles): two at the start of its
+//    softmax phase and two at the start of its next matrix phase, which balances the two
+//    phases; it waits for them at the end of the softmax phase after that.  V is stored row-major and read with
 //    the gfx950 transposing LDS load, which yields the V^T operand directly.
 //  * Workgroups are launched heaviest query block first (causal work grows with the query
 //    position), with the KV head as the fastest-varying index so that neighbouring
@@ -212,13 +213,14 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
       dma16_to_lds(rsrc, dst + 1024 * i, off, (unsigned)(j * BN + 4 * i) * row_stride);
     }
   };
-  // In the main loop each wave issues its four loads of a tile at the start of its softmax
-  // phase: group 0 stages V tiles, group 1 K tiles.  (Measured against this: the loads
-  // between the exponential chains, 11 % slower; in the matrix phase, where each costs
-  // ~55 cycles instead of ~37 and leaves less time to land, 4 % slower.)  Loads of tiles
-  // past the wave's last one point beyond the buffer (zeros, no memory traffic) into a
-  // stage nobody reads again, so every softmax phase issues exactly four loads and the
-  // waits can count them.
+  // In the main loop each wave issues loads 0 and 1 of its share of a tile at the start of
+  // its softmax phase and loads 2 and 3 at the start of its next matrix phase (an LDS-DMA
+  // load costs the issuing wave ~45-55 cycles in either phase; the split balances them:
+  // -2 % cycles per tile against all four in the softmax phase).  (Measured against this:
+  // the loads between the exponential chains, 11 % slower; all four in the matrix phase,
+  // 4 % slower.)  Group 0 stages V tiles, group 1 K tiles.  Loads of tiles past the wave's
+  // last one point beyond the buffer (zeros, no memory traffic) into a stage nobody reads
+  // again, so every phase issues exactly two loads and the waits can count them.
   const dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
   const unsigned my_dma_off = group ? k_dma_off : v_dma_off;
   char* const my_lds = group ? &k_lds[0][0] : &v_lds[0][0];
@@ -269,8 +271,13 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // keep one home: where the wave has no tile j-1, P is zero (the V buffer holds finite
   // data: a real tile, or zeros before the first); where it has no tile j, the scores
   // are computed from whatever K buffer is there and never used.
-  auto matrix_phase = [&](auto stage_c) __attribute__((always_inline)) {
+  auto matrix_phase = [&](int j, auto stage_c) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_c)::value;     // compile-time: LDS addresses fold
+    // the second half of the tile whose first half the previous softmax phase loaded:
+    // group 0 V(j) into this step's stage, group 1 K(j+2) into the stage of K(j-1)
+    const bool dma_now = j > j_begin;
+    const int dma_tile_idx = group ? j + 2 : j;
+    constexpr int dma_stage_g0 = stage, dma_stage_g1 = (stage + 2) % 3;
     const char* vt = v_lds[(stage + 2) % 3];            // V(j-1)
     const char* kt = k_lds[stage];                      // K(j)
     sc[0] = f32x16{};
@@ -293,6 +300,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
       }
       acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % (PREFETCH + 1)], pb[x >> 2], acc[x & 3], 0, 0, 0);
       sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (PREFETCH + 1)], qop[x >> 1], sc[x & 1], 0, 0, 0);
+      if (x < 2 && dma_now) issue_one(dma_tile_idx, group ? dma_stage_g1 : dma_stage_g0, 2 + x);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     const int dma_tile_idx = group ? j + 3 : j + 1;
     const int dma_stage = group ? stage : (stage == 2 ? 0 : stage + 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) issue_one(dma_tile_idx, dma_stage, t);
+    for (int t = 0; t < 2; ++t) issue_one(dma_tile_idx, dma_stage, t);   // the other two: next matrix phase
     if (j >= wave_tiles || j < wave_first) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) pb[c] = bf16x8{};
@@ -385,13 +393,16 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // 2j+2 group 0's softmax phase j and group 1's matrix phase j.  K(j) is read in
   // intervals 2j+1 and 2j+2, V(j) in 2j+3 and 2j+4; tile j lives in stage (j - j_begin) % 3
   // (j_begin: the workgroup's first key tile; the steps below count from it).
-  // Staging: in its softmax phase j (interval 2j+2) group 0 loads V(j+1), first read in
-  // interval 2j+5; in its softmax phase j (interval 2j+3) group 1 loads K(j+3), first read
-  // in interval 2j+7.  Each wave waits for its loads at the end of its next softmax phase
-  // (vmcnt(4): only the four just issued may still be in flight), before the barrier that
-  // opens the first interval reading them.  The prologue loads the first two K tiles and
-  // the first V tile completely and starts the third K tile, which group 1's first wait
-  // covers.
+  // Staging: group 0 loads V(j+1) in halves, at the start of its softmax phase j
+  // (interval 2j+2) and of its matrix phase j+1 (interval 2j+3), into the stage of V(j-2)
+  // (last read in interval 2j); first read in interval 2j+5.  Group 1 loads K(j+3) in
+  // halves in its softmax phase j (interval 2j+3) and matrix phase j+1 (interval 2j+4),
+  // into the stage of K(j) (last read in interval 2j+2); first read in interval 2j+7.  Each
+  // wave waits at the end of its softmax phase j+1 (vmcnt(2): only the two loads that phase
+  // just issued may still be in flight), before the barrier that opens the first interval
+  // reading the tile.  The prologue loads the first two K tiles and the first V tile
+  // completely and starts the third K tile, which group 1's first wait covers; the first
+  // matrix phase issues no loads.
   {
     u32x4* z = (u32x4*)v_lds[2];        // read by the (zero-P) PV of step 0
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
@@ -410,11 +421,13 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   }
   auto step = [&](int j, auto stage_c) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);        // matrix phase first in the SIMD's issue arbitration
-    matrix_phase(stage_c);
+    matrix_phase(j, stage_c);
     __builtin_amdgcn_s_setprio(0);
     barrier_no_fence();
     softmax_phase(j, decltype(stage_c)::value);
-    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4): this wave's loads of its previous softmax phase landed
+    // vmcnt(2): everything but the two loads this softmax phase just issued has landed,
+    // i.e. the tile split over the previous softmax phase and this step's matrix phase
+    __builtin_amdgcn_s_waitcnt(0x0F72);
     barrier_no_fence();
   };
   // unrolled by the three stages so that every LDS address in the matrix phase is a
