@@ -18,7 +18,7 @@ token's original position).  It never tiles over keys and never uses the online 
 except in ``online_blocks``, which is the pages' recurrence written out on purpose so the
 tests can check that recurrence against the plain definition.
 
-Readings taken where the pages are silent or garbled (each also listed in the design doc):
+Readings taken where the pages are silent or garbled:
   * LSE = m + ln(l): natural log of the softmax denominator, in units of the *scaled* logit.
   * scale = 1/sqrt(d) with d the per-head dimension.
   * causal is inclusive: a token attends to itself (page 1, "j <= i").

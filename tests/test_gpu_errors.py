@@ -1,6 +1,6 @@
 """On any error the library enqueues nothing and writes nothing: outputs filled with a
-sentinel keep it when an entry point rejects its arguments on a GPU machine (the errors are
-all found by validation, before any launch)."""
+sentinel keep it when an entry point rejects its arguments on a GPU (the errors are all
+found by validation, before any launch)."""
 import ctypes
 
 import pytest
