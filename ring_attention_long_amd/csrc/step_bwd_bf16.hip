@@ -280,32 +280,37 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
 #pragma unroll
     for (int k = 0; k < 8; ++k) stage_dma_one(c, buf, k);
   };
-  auto stats_index = [&](const Cursor& c) {
-    return ((int64_t)bi * a.h + c.hq) * L + min(c.tq0 + lane, L - 1);
-  };
   auto doc_index = [&](const Cursor& c) { return (int64_t)bi * L + min(c.tq0 + lane, L - 1); };
-  const float inv_scale = 1.0f / a.scale;
-  auto stats_store = [&](const Cursor& c, int buf, float l, float dl, int db, int de) {
+  // The statistics of a tile are written by three waves of group 0 (whose vector phase is
+  // the short one), one part each: wave 0 the LSE pairs, wave 1 the D pairs and, with packed
+  // documents, wave 2 the key bounds.  `x` is the wave's value for this lane's row.
+  const int stat_waves = packed ? 3 : 2;
+  auto stats_store = [&](const Cursor& c, int buf, float x, int db, int de) {
     // the lane index passes through an empty asm so that the LDS addresses below are formed
     // here instead of being kept (and spilled) through the main loop
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
     const int row = c.tq0 + ln;
-    // exp2(c2 (S + hi + lo)) = exp(scale S - LSE) with hi + lo = -LSE / scale to about 16
-    // bits; rows past the shard end, or with no key anywhere, get -1e30 (weights 0)
-    const float xs = (row < L && l > -INFINITY) ? -l * inv_scale : -1e30f;
-    const float xd = -dl;
-    const __bf16 xs_hi = (__bf16)xs, xd_hi = (__bf16)xd;
-    bf16x8 vs = {}, vd = {};
-    vs[0] = xs_hi;
-    vs[1] = (__bf16)(xs - (float)xs_hi);
-    vd[0] = xd_hi;
-    vd[1] = (__bf16)(xd - (float)xd_hi);
-    *(bf16x8*)&xq_lds[buf][ln][0] = vs;
-    *(bf16x8*)&xq_lds[buf][ln][8] = bf16x8{};
-    *(bf16x8*)&xo_lds[buf][ln][0] = vd;
-    *(bf16x8*)&xo_lds[buf][ln][8] = bf16x8{};
-    if (!packed) return;                    // key bounds from kf instead
+    if (wave < 2) {
+      // exp2(c2 (S + hi + lo)) = exp(scale S - LSE) with hi + lo = -LSE / scale to about 16
+      // bits; rows past the shard end, or with no key anywhere, get -1e30 (weights 0).
+      // dP - D the same way with hi + lo = -D.
+      // 1 / scale from the hardware reciprocal (within an ulp, far inside the pair's 16
+      // bits), formed here: the empty asm keeps it from being hoisted into a register held
+      // (and spilled) through the main loop
+      float s_ = a.scale;
+      __asm__ volatile("" : "+v"(s_));
+      const float inv_scale = __builtin_amdgcn_rcpf(s_);
+      const float xv = wave == 1 ? -x : (row < L && x > -INFINITY) ? -x * inv_scale : -1e30f;
+      const __bf16 x_hi = (__bf16)xv;
+      bf16x8 pair = {};
+      pair[0] = x_hi;
+      pair[1] = (__bf16)(xv - (float)x_hi);
+      __bf16* dst = wave == 0 ? &xq_lds[buf][ln][0] : &xo_lds[buf][ln][0];
+      *(bf16x8*)dst = pair;
+      *(bf16x8*)(dst + 8) = bf16x8{};
+      return;
+    }
     const KeyRange r = row < L ? range_of(row, db, de) : KeyRange{0, 0};
     lo_lds[buf][ln] = r.lo;
     hi_lds[buf][ln] = r.hi;
@@ -338,25 +343,17 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   Cursor cc = first;                          // tile of the current step
   Cursor cs = first;                          // next tile to stage
   if (grp == 1) stage_dma(cs, 0);
-  float st_l = 0.f, st_d = 0.f;             // statistics of a later tile in flight (wave 0)
-  int st_b = 0, st_e = 0;
-  auto stats_load = [&](const Cursor& c) {
-    const int64_t si = stats_index(c);
-    st_l = lse[si];
-    st_d = delta[si];
-    if (packed) {
-      st_b = a.doc_begin[doc_index(c)];
-      st_e = a.doc_end[doc_index(c)];
-    }
+  // this wave's part of the statistics of a tile (waves 0 and 1: LSE and D of the lane's row),
+  // addressed by a 32-bit offset from the batch's [h][L] slice (h L < 2^23 for the backward)
+  const float* stat_src = (wave == 0 ? lse : delta) + (int64_t)bi * a.h * L;
+  auto stat_value = [&](const Cursor& c) {
+    return stat_src[(unsigned)(min(c.hq, a.h - 1) * L + min(c.tq0 + lane, L - 1))];
   };
-  if (wave == 0) {                          // tiles 0 and 1 in place, tile 2 loading
-    stats_store(cs, 0, lse[stats_index(cs)], delta[stats_index(cs)], doc_b(cs), doc_e(cs));
+  if (wave < stat_waves) {                  // tiles 0 and 1
+    stats_store(cs, 0, stat_value(cs), doc_b(cs), doc_e(cs));
     Cursor c1 = cs;
     advance(c1);
-    if (n_iter > 1)
-      stats_store(c1, 1, lse[stats_index(c1)], delta[stats_index(c1)], doc_b(c1), doc_e(c1));
-    advance(c1);
-    if (n_iter > 2) stats_load(c1);
+    if (n_iter > 1) stats_store(c1, 1, stat_value(c1), doc_b(c1), doc_e(c1));
   }
   advance(cs);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V rows and tile 0 are in place
@@ -370,8 +367,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // read from interval 2j+1 to 2j+4.  Group 1 starts the DMA of tile j in its vector phase
   // j-2 (interval 2j-1; the stage last held tile j-3, read up to interval 2j-2) and waits for
   // it at the end of its matrix phase j-1 (interval 2j), one interval before tile j is first
-  // read.  Wave 0 loads the tile's statistics in its vector phase j-2 (interval 2j-2) and
-  // stores them in its vector phase j-1 (interval 2j; first read in interval 2j+1).
+  // read.  Waves 0-2 load the tile's statistics and store them in their vector phase j-1
+  // (interval 2j; first read in interval 2j+1).
   // Matrix phase of tile j (stage BCUR; the previous tile is in stage (BCUR + 2) % 3): 16
   // slots of two products, first dV^T += dO^T P and dK^T += Q^T dS of tile j - 1, then
   // S = Q K^T and dP = dO V^T of tile j.  Slot x issues the LDS reads of slot x + 2, then
@@ -451,9 +448,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     }
   };
   // accumulator layout: lane = key u, register i = row 8 (i / 4) + 4 lg + (i % 4) of the
-  // wave's 32-row half.  sc and dp arrive as S - LSE / scale and dP - D.  `stage` (group 1's
-  // loads for a later tile) goes first so that its copies start early.
-  auto vector_phase = [&](int j, int bcur, auto&& stage) __attribute__((always_inline)) {
+  // wave's 32-row half.  sc and dp arrive as S - LSE / scale and dP - D.  `stage` (loads for a
+  // later tile) goes first so that its copies start early; `mid` runs after the
+  // exponentials, by when those loads have had time to land.
+  auto vector_phase = [&](int j, int bcur, auto&& stage, auto&& mid) __attribute__((always_inline)) {
     stage();
     __builtin_amdgcn_sched_barrier(0);
     const int r0 = cc.tq0 + 32 * grp;
@@ -471,15 +469,23 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     }
     const bool skip = j >= n_iter || r0 >= L || hi_last <= uw || lo_first >= uw + 32;
     const bool full = hi_first >= uw + 32 && lo_last <= uw;   // rows past the shard end have weight 0
+    if (!skip) {
+      // all products first (in place), then the exponentials: sixteen independent
+      // transcendental ops instead of product-exponential pairs through one temporary
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] *= c2;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[i]);
+        sc[i] = p;
+        dp[i] = p * dp[i];
+      }
+    }
+    mid();                                  // one call site, on every path
     if (skip) {
       pb[0] = pb[1] = ds[0] = ds[1] = bf16x8{};
       return;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(sc[i] * c2);
-      sc[i] = p;
-      dp[i] = p * dp[i];
     }
     if (!full) {
       // keep this a real (scalar) branch: only diagonal and boundary tiles pay for the mask
@@ -527,26 +533,38 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads for tile j + 1 landed
     barrier_no_fence();
-    vector_phase(j, bcur, [&]() __attribute__((always_inline)) {
-      if (grp == 1 && j + 2 < n_iter) {
-        advance(cs);                        // cs: tile j + 2
-        stage_dma(cs, bnext2);
-      }
-    });
-    // Wave 0 stores the statistics of tile j + 1 (first read after the next barrier; its
-    // stage held tile j - 2, whose last reader finished at least two barriers earlier) and
-    // starts loading those of tile j + 2.  Group 0's vector phase is the short one.
-    if (wave == 0 && j >= 1) {
-      Cursor c1 = cc;
-      advance(c1);
-      if (j + 1 < n_iter) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the statistics of tile j + 1 landed
-        stats_store(c1, bnext, st_l, st_d, st_b, st_e);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the barrier
-      }
-      advance(c1);
-      if (j + 2 < n_iter) stats_load(c1);
-    }
+    // Group 1 starts the loads of tile j + 2 first in its vector phase.  Waves 0 and 1 (and 2
+    // with packed documents) load their part of the statistics of tile j + 1 at the start of
+    // theirs and store it after the exponentials (first read after the next barrier; the
+    // stage held tile j - 2, whose last reader finished at least two barriers earlier).  The
+    // values live only within the phase, so no register carries them across the loop.
+    const bool stat_tile = wave < stat_waves && j >= 1 && j + 1 < n_iter;
+    Cursor c1 = cc;
+    advance(c1);
+    // (left unset on the other paths: an initialiser there would make the compiler wait for
+    // every outstanding load before writing these registers)
+    float st_x;
+    int st_b, st_e;
+    vector_phase(
+        j, bcur,
+        [&]() __attribute__((always_inline)) {
+          if (grp == 1) {
+            if (j + 2 < n_iter) {
+              advance(cs);                  // cs: tile j + 2
+              stage_dma(cs, bnext2);
+            }
+          } else {
+            st_x = stat_value(c1);
+            if (packed) {
+              st_b = a.doc_begin[doc_index(c1)];
+              st_e = a.doc_end[doc_index(c1)];
+            }
+          }
+        },
+        [&]() __attribute__((always_inline)) {
+          if (stat_tile) stats_store(c1, bnext, st_x, st_b, st_e);
+        });
+    if (wave < stat_waves) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): visible after the barrier
     advance(cc);
     bcur = bnext;
     barrier_no_fence();
