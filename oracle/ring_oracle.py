@@ -86,11 +86,6 @@ def shard_tokens(layout: str, N: int, L: int) -> list[np.ndarray]:
     return [np.concatenate([chunks[p], chunks[2 * N - 1 - p]]) for p in range(N)]
 
 
-def positions(layout: str, N: int, L: int, shard: int) -> np.ndarray:
-    """Global positions of shard `shard`'s local tokens 0..L-1 (see shard_tokens)."""
-    return shard_tokens(layout, N, L)[shard]
-
-
 def ring_order(N: int, shard: int) -> list[int]:
     """KV shard held at ring step k = 0..N-1 by device `shard`.
 
@@ -365,6 +360,62 @@ def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous",
             dS = P * (dP - D[:, None])
             dq[bi, :, hq] = sc * (dS @ Kh)
     return dq
+
+
+def key_grads(q_shards, dout_shards, k_all, v_all, *, N, query_shards, kv_head, cols,
+              layout="contiguous", causal=False, scale=None, docs=None, rows=None, row_block=32):
+    """dK and dV of selected keys of one KV head (same definition as shard_grads), summed
+    over the KV group's query heads and over the rows `rows` (default: every row) of each
+    of the listed query shards.
+
+    q_shards, dout_shards [Q, b, L, h, d] hold the queries and output gradients of the
+    query shards named by `query_shards` (length Q, same order); k_all, v_all
+    [N, b, L, n_kv, d] every shard's keys and values; `cols` lists keys as (kv shard,
+    local index) pairs.  Returns dk, dv [b, C, d] for those C keys.  Both are sums over
+    rows, so disjoint row sets may be evaluated separately and added.
+
+    A key's gradients need P and D of every row that may attend to it, and those need the
+    row's softmax over the whole sequence: so each row is evaluated against every key
+    (s, the mask, P = softmax over the allowed keys, O = P V, D = dO . O), and only the
+    selected keys' columns of P and dS = P * (dP - D) are kept:
+        dV_c = sum_r P[r,c] dO_r,   dK_c = scale * sum_r dS[r,c] Q_r.
+    Rows are taken `row_block` at a time (each row's quantities depend on that row alone);
+    keys that no row of the block may attend carry weight zero and are left out.
+    """
+    Nk, b, L, n_kv, d = k_all.shape
+    h = q_shards.shape[3]
+    group = _gqa_group(h, n_kv)
+    sc = _default_scale(d, scale)
+    toks = shard_tokens(layout, N, L)
+    pos_k = np.concatenate(toks)                            # key j*L + u is (shard j, local u)
+    sel = np.asarray([j * L + u for j, u in cols], dtype=np.int64)
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    dk = np.zeros((b, sel.size, d))
+    dv = np.zeros((b, sel.size, d))
+    g = kv_head
+    for qi, i in enumerate(query_shards):
+        for r0 in range(0, rows.size, row_block):
+            rr = rows[r0:r0 + row_block]
+            allowed = allowed_mask(toks[i][rr], pos_k, causal=causal, docs=docs)   # [R, S]
+            keep = np.flatnonzero(allowed.any(axis=0) | np.isin(np.arange(pos_k.size), sel))
+            allowed = allowed[:, keep]
+            where_sel = np.searchsorted(keep, sel)                  # selected keys among `keep`
+            for bi in range(b):
+                Kh, Vh = k_all[keep // L, bi, keep % L, g], v_all[keep // L, bi, keep % L, g]
+                for hq in range(g * group, (g + 1) * group):
+                    Qr, dOr = q_shards[qi, bi, rr, hq], dout_shards[qi, bi, rr, hq]
+                    s = np.where(allowed, (Qr @ Kh.T) * sc, -np.inf)
+                    m = s.max(axis=1, initial=-np.inf)
+                    m = np.where(np.isfinite(m), m, 0.0)
+                    e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+                    den = e.sum(axis=1)
+                    P = np.where(den[:, None] > 0, e / np.where(den > 0, den, 1.0)[:, None], 0.0)
+                    D = np.sum(dOr * (P @ Vh), axis=1)
+                    Pc = P[:, where_sel]
+                    dS = Pc * (dOr @ Vh[where_sel].T - D[:, None])
+                    dk[bi] += sc * (dS.T @ Qr)
+                    dv[bi] += Pc.T @ dOr
+    return dk, dv
 
 
 # --------------------------------------------------------------------------------------

@@ -111,3 +111,70 @@ def test_dq_rows_match_finite_differences():
                 fm = _loss(q, k_all, v_all, dout, **kw)
                 q[0, r, hq, e] = orig
                 assert got[0, ri, hq, e] == pytest.approx((fp - fm) / (2 * eps), rel=1e-6, abs=1e-8)
+
+
+def _key_loss(q_sh, do_sh, k_all, v_all, shards, **kw):
+    """sum over the listed query shards of sum(dO_i * O_i)."""
+    return sum(float(np.sum(shard_attention(q_sh[n], k_all, v_all, shard=i, **kw)[0] * do_sh[n]))
+               for n, i in enumerate(shards))
+
+
+@pytest.mark.parametrize("layout,causal", [("striped", True), ("zigzag", True), ("contiguous", False)])
+def test_key_grads_match_central_differences(layout, causal):
+    """key_grads (selected keys, summed over two query shards and the GQA group) against
+    central differences of the forward with respect to those keys' K and V entries."""
+    from oracle import key_grads
+    N, b, L, h, n_kv, d = 3, 1, 4, 4, 2, 3
+    shards = [0, 2]
+    q_sh = RNG.standard_normal((2, b, L, h, d))
+    do_sh = RNG.standard_normal((2, b, L, h, d))
+    k_all = RNG.standard_normal((N, b, L, n_kv, d))
+    v_all = RNG.standard_normal((N, b, L, n_kv, d))
+    cols = [(0, 0), (1, 3), (2, 1)]
+    g = 1
+    kw = dict(N=N, layout=layout, causal=causal)
+    dk, dv = key_grads(q_sh, do_sh, k_all, v_all, query_shards=shards, kv_head=g, cols=cols,
+                       row_block=3, **kw)
+    eps = 1e-6
+    for ci, (j, u) in enumerate(cols):
+        for x, got in ((k_all, dk), (v_all, dv)):
+            for e in range(d):
+                orig = x[j, 0, u, g, e]
+                x[j, 0, u, g, e] = orig + eps
+                fp = _key_loss(q_sh, do_sh, k_all, v_all, shards, **kw)
+                x[j, 0, u, g, e] = orig - eps
+                fm = _key_loss(q_sh, do_sh, k_all, v_all, shards, **kw)
+                x[j, 0, u, g, e] = orig
+                assert got[0, ci, e] == pytest.approx((fp - fm) / (2 * eps), rel=1e-6, abs=1e-8)
+
+
+@pytest.mark.parametrize("layout,causal,docs", [("striped", True, None), ("contiguous", True, None),
+                                                ("zigzag", True, [0, 5, 6, 13, 24]),
+                                                ("contiguous", False, None)])
+def test_key_grads_equal_summed_shard_grads(layout, causal, docs):
+    """Every key of every shard, over all query shards, b = 2, with small row blocks (so the
+    per-block key trimming is exercised) and split row sets added together: equals the sum
+    of shard_grads' per-KV-shard dK, dV over the query shards."""
+    from oracle import key_grads
+    N, b, L, h, n_kv, d = 3, 2, 8, 6, 2, 4
+    q_sh = RNG.standard_normal((N, b, L, h, d))
+    do_sh = RNG.standard_normal((N, b, L, h, d))
+    k_all = RNG.standard_normal((N, b, L, n_kv, d))
+    v_all = RNG.standard_normal((N, b, L, n_kv, d))
+    kw = dict(N=N, layout=layout, causal=causal, docs=docs)
+    want_k = np.zeros_like(k_all)
+    want_v = np.zeros_like(v_all)
+    for i in range(N):
+        _, rk, rv = shard_grads(q_sh[i], k_all, v_all, do_sh[i], shard=i, **kw)
+        want_k += rk
+        want_v += rv
+    cols = [(j, u) for j in range(N) for u in range(L)]
+    for g in range(n_kv):
+        parts = [key_grads(q_sh, do_sh, k_all, v_all, query_shards=list(range(N)), kv_head=g,
+                           cols=cols, rows=rr, row_block=2, **kw)
+                 for rr in (np.arange(0, 3), np.arange(3, L))]
+        dk = parts[0][0] + parts[1][0]
+        dv = parts[0][1] + parts[1][1]
+        for ci, (j, u) in enumerate(cols):
+            np.testing.assert_allclose(dk[:, ci], want_k[j, :, u, g], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(dv[:, ci], want_v[j, :, u, g], rtol=1e-10, atol=1e-12)
