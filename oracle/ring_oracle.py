@@ -363,7 +363,7 @@ def shard_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout="contiguous",
 
 
 def key_grads(q_shards, dout_shards, k_all, v_all, *, N, query_shards, kv_head, cols,
-              layout="contiguous", causal=False, scale=None, docs=None, rows=None, row_block=32):
+              layout="contiguous", causal=False, scale=None, docs=None, rows=None, row_block=128):
     """dK and dV of selected keys of one KV head (same definition as shard_grads), summed
     over the KV group's query heads and over the rows `rows` (default: every row) of each
     of the listed query shards.

@@ -9,7 +9,9 @@ import pytest
 import torch
 
 import ring_attention_long_amd as ra
-from gpu_helpers import announce, f64, make_inputs, to_gpu
+from gpu_helpers import (BWD_FULL, BWD_FULL_KV_HEAD, BWD_FULL_SEED, announce, bwd_full_cols,
+                         bwd_full_key_grads, f64, full_size_rows, gather_cols, make_inputs, run_threads,
+                         to_gpu)
 from oracle import LAYOUTS, ring_order, shard_dq_rows, shard_grads, shard_tokens
 
 pytestmark = pytest.mark.gpu
@@ -132,28 +134,51 @@ def test_bwd_preprocess_is_rowsum_of_products():
 
 
 # ------------------------------------------------------------------ full size (config 5)
+def oracle_dq_rows(q, k_all, v_all, dout, rows, *, N, shard, layout, causal):
+    """shard_dq_rows (float64 inputs) with one KV group per thread."""
+    h, n_kv = q.shape[2], k_all.shape[3]
+    G = h // n_kv
+
+    def one(g):
+        hs = slice(g * G, (g + 1) * G)
+        return shard_dq_rows(q[:, :, hs], k_all[:, :, :, g:g + 1], v_all[:, :, :, g:g + 1], dout[:, :, hs], rows,
+                             N=N, shard=shard, layout=layout, causal=causal)
+    return np.concatenate(run_threads(one, list(range(n_kv))), axis=2)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("shard", [0, 7])
 def test_config5_full_size(shard):
-    """S = 65536, N = 8 (L = 8192), h = 32, n_kv = 8, d = 128, bf16, causal striped."""
-    cfg = dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8)
+    """S = 65536, N = 8 (L = 8192), h = 32, n_kv = 8, d = 128, bf16, causal striped: dQ of
+    ~300 sampled rows (every head) and dK, dV of 144 keys spread over all 8 KV shards (KV
+    head 2) against the oracle, element by element; plus the Q = 0 closed form for dV of
+    every key."""
+    cfg = dict(BWD_FULL)
     N, L, h, n_kv = 8, 8192, 32, 8
     announce("config5 ring_bwd full size, shard", shard)
-    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=1005)
-    # (1) dQ of sampled rows against the oracle
-    rows = np.array([0, 1, 63, 64, 4095, L - 1])
+    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=BWD_FULL_SEED)
     x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
-    rdq = shard_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard,
-                        layout="striped", causal=True)
-    check_grad(dq[:, torch.as_tensor(rows, device="cuda")], rdq, "config5 dq sampled rows")
-    # (2) identities over all keys: sum dK = 0 per KV head (key-shift invariance); sum dV =
+    # (1) dQ of sampled rows
+    rows = full_size_rows(L, 5005 + shard)
+    announce(f"oracle dQ on {rows.size} rows")
+    rdq = oracle_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard, layout="striped",
+                         causal=True)
+    check_grad(dq[:, torch.as_tensor(rows, device="cuda")], rdq, f"config5 dq {rows.size} sampled rows")
+    # (2) dK, dV of sampled keys of every KV shard
+    cols = bwd_full_cols()
+    announce(f"oracle dK, dV of {len(cols)} keys (KV head {BWD_FULL_KV_HEAD}) from shard {shard}'s rows")
+    rdk, rdv = bwd_full_key_grads([shard])
+    check_grad(gather_cols(dk, cols, BWD_FULL_KV_HEAD), rdk, "config5 dk sampled keys")
+    check_grad(gather_cols(dv, cols, BWD_FULL_KV_HEAD), rdv, "config5 dv sampled keys")
+    # (3) identities over all keys: sum dK = 0 per KV head (key-shift invariance); sum dV =
     #     sum of dO over the group's query rows (softmax rows sum to one)
     dk_sum = f64(dk.sum(dim=(0, 2)))                       # [b, n_kv, d]
     dv_sum = f64(dv.sum(dim=(0, 2)))
-    do_sum = inp["dout"].astype(np.float64).sum(axis=1).reshape(1, n_kv, h // n_kv, 128).sum(axis=2)
+    do_sum = x["dout"].sum(axis=1).reshape(1, n_kv, h // n_kv, 128).sum(axis=2)
     announce(f"sum dK max abs {np.abs(dk_sum).max():.3e}; sum dV err {np.abs(dv_sum - do_sum).max():.3e}")
     assert np.abs(dk_sum).max() <= 2e-2 * np.sqrt(L)
     assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.sqrt(L)
-    # (3) Q = 0: uniform weights 1/n_r; dK = 0 exactly and dV_c = sum over rows r that see
+    # (4) Q = 0: uniform weights 1/n_r; dK = 0 exactly and dV_c = sum over rows r that see
     #     key c of dO_r / n_r (summed over the group's heads), every key of every shard
     q0 = torch.zeros_like(q)
     o0, lse0 = ra.ring_fwd(q0, k_all, v_all, q_shard=shard, causal=True, layout="striped")
@@ -163,7 +188,7 @@ def test_config5_full_size(shard):
     assert float(dk0.abs().max()) == 0.0
     toks = shard_tokens("striped", N, L)
     pos_q = toks[shard]                                    # increasing
-    w = inp["dout"].astype(np.float64)[0] / (pos_q + 1.0)[:, None, None]   # [L, h, d]
+    w = x["dout"][0] / (pos_q + 1.0)[:, None, None]        # [L, h, d]
     wg = w.reshape(L, n_kv, h // n_kv, 128).sum(axis=2)   # [L, n_kv, d]
     suffix = np.cumsum(wg[::-1], axis=0)[::-1]             # suffix[r] = sum over rows >= r
     want = np.zeros((N, L, n_kv, 128))

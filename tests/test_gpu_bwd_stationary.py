@@ -9,9 +9,10 @@ import torch
 
 import ring_attention_long_amd as ra
 import synth
-from gpu_helpers import announce, f64, to_gpu
-from oracle import shard_dq_rows, shard_grads
-from test_gpu_bwd import check_grad
+from gpu_helpers import (BWD_FULL, BWD_FULL_KV_HEAD, announce, bwd_full_cols, bwd_full_inputs, bwd_full_key_grads,
+                         f64, full_size_rows, gather_cols, to_gpu)
+from oracle import shard_grads
+from test_gpu_bwd import check_grad, oracle_dq_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -71,36 +72,29 @@ def test_kv_stationary_matches_oracle(layout, causal):
         check_grad(dv[j], rdv[j], f"dv shard {j} {layout} {causal}")
 
 
+@pytest.mark.timeout(900)
 def test_kv_stationary_full_size():
-    """S = 65536 (N = 8, L = 8192, h = 32, n_kv = 8, d = 128, bf16), striped causal: summed dQ
-    on sampled rows of two shards against the oracle, and dK, dV of every shard against the
-    per-shard sums of the key/value-rotating schedule (itself checked against the oracle)."""
-    N, L, h, n_kv, d = 8, 8192, 32, 8, 128
+    """S = 65536 (N = 8, L = 8192, h = 32, n_kv = 8, d = 128, bf16), striped causal, every
+    device's stationary pass: dK, dV of 144 keys spread over all 8 KV shards (KV head 2) and
+    the summed dQ of ~300 sampled rows of two shards against the oracle, element by element."""
+    N, L = BWD_FULL["N"], BWD_FULL["L"]
     announce("kv-stationary full size: inputs")
-    q, do, k, v = all_shards(b=1, L=L, h=h, n_kv=n_kv, d=d, N=N, seed=302)
+    q, do, k, v = bwd_full_inputs()
     qg, dog, kg, vg = (to_gpu(x, "bf16") for x in (q, do, k, v))
     announce("kv-stationary full size: forward of every shard")
     lse_all, delta_all = forward_all(qg, kg, vg, dog, causal=True, layout="striped")
     announce("kv-stationary full size: stationary pass of every device")
     dq, dk, dv = stationary_all(qg, kg, vg, dog, lse_all, delta_all, causal=True, layout="striped")
-    announce("kv-stationary full size: rotating pass of every device")
-    rdk = torch.zeros_like(dk)
-    rdv = torch.zeros_like(dv)
-    for i in range(N):
-        o, lse = ra.ring_fwd(qg[i].contiguous(), kg, vg, q_shard=i, causal=True, layout="striped")
-        _, dk_i, dv_i = ra.ring_bwd(qg[i].contiguous(), kg, vg, o, dog[i].contiguous(), lse, q_shard=i,
-                                    causal=True, layout="striped")
-        rdk += dk_i
-        rdv += dv_i
-    torch.cuda.synchronize()
-    for name, a, bb in (("dk", dk, rdk), ("dv", dv, rdv)):
-        ref = f64(bb)
-        check_grad(a, ref, f"full size {name} vs rotating schedule")
+    cols = bwd_full_cols()
+    announce(f"kv-stationary full size: oracle dK, dV of {len(cols)} keys from every query shard")
+    rdk, rdv = bwd_full_key_grads(list(range(N)))
+    check_grad(gather_cols(dk, cols, BWD_FULL_KV_HEAD), rdk, "full size dk sampled keys")
+    check_grad(gather_cols(dv, cols, BWD_FULL_KV_HEAD), rdv, "full size dv sampled keys")
     x = [a.astype(np.float64) for a in (q, do, k, v)]
     for i in (0, 5):
-        rows = np.array([0, 1, 63, 64, 4095, L - 2, L - 1])
-        announce(f"kv-stationary full size: oracle dQ rows of shard {i}")
-        ref = shard_dq_rows(x[0][i], x[2], x[3], x[1][i], rows, N=N, shard=i, layout="striped", causal=True)
+        rows = full_size_rows(L, 6006 + i)
+        announce(f"kv-stationary full size: oracle dQ of {rows.size} rows of shard {i}")
+        ref = oracle_dq_rows(x[0][i], x[2], x[3], x[1][i], rows, N=N, shard=i, layout="striped", causal=True)
         check_grad(dq[i][:, torch.from_numpy(rows).cuda()], ref, f"full size dq shard {i} sampled rows")
 
 

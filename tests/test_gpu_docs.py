@@ -8,8 +8,9 @@ import torch
 
 import ring_attention_long_amd as ra
 import synth
-from gpu_helpers import announce, check_bf16, check_f32, f64, make_inputs, to_gpu
-from oracle import LAYOUTS, shard_attention, shard_dq_rows, shard_grads, shard_tokens, step_attention
+from gpu_helpers import (announce, check_bf16, check_f32, f64, full_size_rows, make_inputs, oracle_ring_rows,
+                         run_threads, to_gpu)
+from oracle import LAYOUTS, key_grads, shard_attention, shard_dq_rows, shard_grads, shard_tokens, step_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +138,7 @@ def _boundary_rows(bounds, layout, N, L, shard, extra):
     return rows[(rows >= 0) & (rows < L)]
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("shard", [0, 5])
 def test_packed_fwd_full_size(shard):
     """S = 262144, N = 8, h = 32, n_kv = 8, bf16, striped causal, documents of mean length 4096."""
@@ -150,17 +152,22 @@ def test_packed_fwd_full_size(shard):
                          to_gpu(inp["v_all"], "bf16"), q_shard=shard, causal=True,
                          layout="striped", docs=docs)
     torch.cuda.synchronize()
-    rows = _boundary_rows(bounds, "striped", N, L, shard, np.array([0, 1, 4095, L - 1]))
-    O, LSE = oracle_ring_docs(inp, [bounds], N=N, shard=shard, layout="striped", causal=True,
-                              rows=rows)
+    rows = _boundary_rows(bounds, "striped", N, L, shard, full_size_rows(L, 1006 + shard))
+    announce(f"oracle on {rows.size} rows")
+    O, LSE = oracle_ring_rows(inp, N=N, shard=shard, layout="striped", causal=True, rows=rows, docs=bounds)
     idx = torch.as_tensor(rows, device="cuda")
-    check_bf16(o[:, idx], lse[:, :, idx], O, LSE, f"packed full size shard {shard}")
+    check_bf16(o[:, idx], lse[:, :, idx], O, LSE, f"packed full size shard {shard} {rows.size} rows")
 
 
+@pytest.mark.timeout(900)
 def test_packed_bwd_full_size():
-    """S = 65536, N = 8, h = 32, n_kv = 8, bf16, striped causal, documents of mean length 2048:
-    sampled dQ rows against the oracle, and the sum identities of dK and dV."""
-    N, L, h, n_kv, shard = 8, 8192, 32, 8, 3
+    """S = 65536, N = 8, h = 32, n_kv = 8, bf16, striped causal, documents of mean length 2048,
+    query shard 3: dQ of sampled rows (every document edge class and ~300 more) and dK, dV of
+    keys at document edges and spread over all 8 KV shards (KV head 2) against the oracle,
+    element by element; and the sum identities of dK and dV."""
+    from test_gpu_bwd import check_grad, oracle_dq_rows
+    from gpu_helpers import bwd_full_cols, gather_cols
+    N, L, h, n_kv, shard, g = 8, 8192, 32, 8, 3, 2
     cfg = dict(b=1, L=L, h=h, n_kv=n_kv, d=128, N=N)
     bounds = synth.document_bounds(N * L, seed=1007, mean_len=2048).astype(np.int32)
     announce("packed full size bwd, documents", bounds.size - 1)
@@ -171,17 +178,41 @@ def test_packed_bwd_full_size():
     dq, dk, dv = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=True,
                              layout="striped", docs=docs)
     torch.cuda.synchronize()
-    rows = _boundary_rows(bounds, "striped", N, L, shard, np.array([0, 1, L - 1]))
     x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
-    rdq = shard_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard,
-                        layout="striped", causal=True, docs=bounds)
+    rows = _boundary_rows(bounds, "striped", N, L, shard, full_size_rows(L, 1107))
+    announce(f"oracle dQ of {rows.size} rows")
+    rdq = oracle_dq_rows_docs(x, rows, N=N, shard=shard, bounds=bounds)
     check_grad(dq[:, torch.as_tensor(rows, device="cuda")], rdq, "packed full size dq rows")
+    toks = shard_tokens("striped", N, L)
+    edge_pos = np.concatenate([bounds[1:-1], bounds[1:-1] - 1])
+    edge_cols = [(j, int(u)) for j in range(N) for u in np.nonzero(np.isin(toks[j], edge_pos))[0][::7]]
+    cols = sorted(set(bwd_full_cols()) | set(edge_cols))
+    announce(f"oracle dK, dV of {len(cols)} keys (KV head {g})")
+    parts = np.array_split(np.arange(L), 32)
+    res = run_threads(lambda rr: key_grads(x["q"][None], x["dout"][None], x["k_all"], x["v_all"], N=N,
+                                           query_shards=[shard], kv_head=g, cols=cols, layout="striped",
+                                           causal=True, docs=bounds, rows=rr), parts)
+    rdk, rdv = sum(r[0] for r in res), sum(r[1] for r in res)
+    check_grad(gather_cols(dk, cols, g), rdk, "packed full size dk sampled keys")
+    check_grad(gather_cols(dv, cols, g), rdv, "packed full size dv sampled keys")
     dk_sum = f64(dk.sum(dim=(0, 2)))
     dv_sum = f64(dv.sum(dim=(0, 2)))
     do_sum = x["dout"].sum(axis=1).reshape(1, n_kv, h // n_kv, 128).sum(axis=2)
     announce(f"sum dK max abs {np.abs(dk_sum).max():.3e}; sum dV err {np.abs(dv_sum - do_sum).max():.3e}")
     assert np.abs(dk_sum).max() <= 2e-2 * np.sqrt(L)
     assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.sqrt(L)
+
+
+def oracle_dq_rows_docs(x, rows, *, N, shard, bounds):
+    """shard_dq_rows with packed documents, one KV group per thread."""
+    h, n_kv = x["q"].shape[2], x["k_all"].shape[3]
+    G = h // n_kv
+
+    def one(g):
+        hs = slice(g * G, (g + 1) * G)
+        return shard_dq_rows(x["q"][:, :, hs], x["k_all"][:, :, :, g:g + 1], x["v_all"][:, :, :, g:g + 1],
+                             x["dout"][:, :, hs], rows, N=N, shard=shard, layout="striped", causal=True, docs=bounds)
+    return np.concatenate(run_threads(one, list(range(n_kv))), axis=2)
 
 
 @pytest.mark.parametrize("causal", [True, False])

@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import ring_attention_long_amd as ra
-from gpu_helpers import (announce, check_bf16, check_f32, f64, make_inputs, oracle_ring,
-                         oracle_step, prefix_means_global, to_gpu)
+from gpu_helpers import (announce, check_bf16, check_f32, f64, full_size_rows, make_inputs, oracle_ring,
+                         oracle_ring_rows, oracle_step, prefix_means_global, to_gpu)
 from oracle import LAYOUTS, merge as oracle_merge, ring_order
 
 pytestmark = pytest.mark.gpu
@@ -197,23 +197,16 @@ def test_edge_large_logits_identical_keys_zero_queries():
 
 
 # ------------------------------------------------------------------ full-size configs
-SAMPLE_ROWS = 6
-
-
-def _sample_rows(L, rng):
-    fixed = [0, L - 1, 63, 64, L // 2]
-    return np.unique(np.concatenate([fixed, rng.integers(0, L, SAMPLE_ROWS)]))
-
-
 def _full_size_check(cfg, *, layout, causal, shard, seed):
     N = cfg["N"]
     inp = make_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16")
     announce("full-size ring_fwd", layout, "causal", causal, "shard", shard, cfg)
     o, lse = _ring(inp, "bf16", N=N, shard=shard, layout=layout, causal=causal)
-    rows = _sample_rows(cfg["L"], np.random.default_rng(seed))
-    O, LSE = oracle_ring(inp, N=N, shard=shard, layout=layout, causal=causal, rows=rows)
-    check_bf16(o[:, torch.as_tensor(rows, device="cuda")], lse[:, :, torch.as_tensor(rows, device="cuda")],
-               O, LSE, f"full {layout} shard {shard} sampled rows")
+    rows = full_size_rows(cfg["L"], seed)
+    announce(f"oracle on {rows.size} rows")
+    O, LSE = oracle_ring_rows(inp, N=N, shard=shard, layout=layout, causal=causal, rows=rows)
+    idx = torch.as_tensor(rows, device="cuda")
+    check_bf16(o[:, idx], lse[:, :, idx], O, LSE, f"full {layout} shard {shard} {rows.size} sampled rows")
     # Q = 0 on the same keys/values: every row against the O(S) prefix-mean closed form
     inp0 = dict(inp, q=np.zeros_like(inp["q"]))
     o0, lse0 = _ring(inp0, "bf16", N=N, shard=shard, layout=layout, causal=causal)
@@ -231,19 +224,39 @@ def _full_size_check(cfg, *, layout, causal, shard, seed):
     assert np.max(np.abs(f64(lse0) - lse_want[None, None, :])) <= 1e-3
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("shard", [0, 5])
 def test_config2_noncausal_gqa_full_size(shard):
     cfg = dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8)
     _full_size_check(cfg, layout="contiguous", causal=False, shard=shard, seed=1002)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("shard", [0, 7])
 def test_config3_causal_contiguous_full_size(shard):
     cfg = dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8)
     _full_size_check(cfg, layout="contiguous", causal=True, shard=shard, seed=1003)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("layout,shard", [("striped", 0), ("striped", 7), ("zigzag", 3)])
 def test_config4_causal_balanced_full_size(layout, shard):
     cfg = dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8)
     _full_size_check(cfg, layout=layout, causal=True, shard=shard, seed=1004)
+
+
+@pytest.mark.timeout(600)
+def test_config4_large_logits_full_size():
+    """Q x 8 (exact in bf16) at S = 262144 striped causal, shard 0: logits ~ N(0, 64), so the
+    softmax's first tiles meet weights far above 2^24 of the running estimate and every row
+    goes through the overflow guard and the lazy rescale over its 512 key tiles."""
+    cfg = dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8)
+    inp = make_inputs(**cfg, q_shard=0, seed=1004, dtype="bf16")
+    inp = dict(inp, q=inp["q"] * 8)
+    announce("full-size ring_fwd, Q x 8, striped causal shard 0")
+    o, lse = _ring(inp, "bf16", N=8, shard=0, layout="striped", causal=True)
+    rows = full_size_rows(cfg["L"], 1104)
+    announce(f"oracle on {rows.size} rows")
+    O, LSE = oracle_ring_rows(inp, N=8, shard=0, layout="striped", causal=True, rows=rows)
+    idx = torch.as_tensor(rows, device="cuda")
+    check_bf16(o[:, idx], lse[:, :, idx], O, LSE, f"full Q x 8 striped shard 0 {rows.size} sampled rows")

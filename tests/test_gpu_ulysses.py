@@ -9,7 +9,7 @@ import torch
 
 import ring_attention_long_amd as ra
 import synth
-from gpu_helpers import announce, check_bf16, check_f32, f64, to_gpu
+from gpu_helpers import announce, check_bf16, check_f32, f64, full_size_rows, oracle_ring_rows, to_gpu
 from oracle import LAYOUTS, shard_attention
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,7 @@ def test_ulysses_matches_ring_fwd():
         assert d_o <= 2e-2 and d_l <= 1e-3
 
 
+@pytest.mark.timeout(600)
 def test_ulysses_full_size_sampled():
     """S = 262144 (N = 8 shards of 32768, h = 32, n_kv = 8, d = 128, bf16), striped causal,
     head group 5, in the launch configuration of the benchmark; sampled rows of two shards
@@ -106,15 +107,14 @@ def test_ulysses_full_size_sampled():
     out, lse = ra.ulysses_fwd(qg, kg, vg, head_group=5, causal=True, layout="striped")
     torch.cuda.synchronize()
     heads = slice(20, 24)
-    kx, vx = k.astype(np.float64), v.astype(np.float64)
     for j in (0, 7):
-        rows = np.array([0, 1, 63, 64, 4095, 16384, L - 2, L - 1])
-        announce(f"ulysses full size: oracle, shard {j}, rows {rows.tolist()}")
-        O, LSE = shard_attention(q[j].astype(np.float64), kx, vx, N=N, shard=j, layout="striped", causal=True,
-                                 rows=rows)
+        rows = full_size_rows(L, 205 + j)
+        announce(f"ulysses full size: oracle, shard {j}, {rows.size} rows")
+        inp = {"q": q[j][:, :, heads], "k_all": k[:, :, :, 5:6], "v_all": v[:, :, :, 5:6]}
+        O, LSE = oracle_ring_rows(inp, N=N, shard=j, layout="striped", causal=True, rows=rows)
         idx = torch.from_numpy(rows).cuda()
-        check_bf16(out[j][:, idx][:, :, heads], lse[j][:, heads][:, :, idx], O[:, :, heads], LSE[:, heads],
-                   f"ulysses full size shard {j}")
+        check_bf16(out[j][:, idx][:, :, heads], lse[j][:, heads][:, :, idx], O, LSE,
+                   f"ulysses full size shard {j} {rows.size} rows")
 
 
 def _dout_all(*, b, L, h, d, N, seed):
@@ -151,43 +151,35 @@ def test_ulysses_bwd_every_shard(layout, causal):
         check_grad(dv[j], rdv[j], f"ulysses dv shard {j} {layout} {causal}")
 
 
+@pytest.mark.timeout(900)
 def test_ulysses_bwd_full_size():
     """S = 65536 (N = 8, L = 8192, h = 32, n_kv = 8, d = 128, bf16), striped causal, head group
-    2: its heads' dQ, dK, dV against the key/value-rotating ring backward of every shard
-    (itself checked against the oracle), and sampled dQ rows against the oracle."""
-    from test_gpu_bwd import check_grad
-    from oracle import shard_dq_rows
-    N, L, h, n_kv, d, grp = 8, 8192, 32, 8, 128, 2
-    hs, ks = slice(4 * grp, 4 * grp + 4), slice(grp, grp + 1)
+    2 (query heads 8..11, KV head 2): dK, dV of 144 keys spread over all 8 KV shards and dQ of
+    ~300 sampled rows of three shards against the oracle, element by element."""
+    from test_gpu_bwd import check_grad, oracle_dq_rows
+    from gpu_helpers import (BWD_FULL, BWD_FULL_KV_HEAD, bwd_full_cols, bwd_full_inputs, bwd_full_key_grads,
+                             full_size_rows, gather_cols)
+    N, L, grp = BWD_FULL["N"], BWD_FULL["L"], BWD_FULL_KV_HEAD
+    hs = slice(4 * grp, 4 * grp + 4)
     announce("ulysses bwd full size: inputs")
-    q, k, v = all_shards(b=1, L=L, h=h, n_kv=n_kv, d=d, N=N, seed=212, dtype="bf16")
-    do = _dout_all(b=1, L=L, h=h, d=d, N=N, seed=212)
+    q, do, k, v = bwd_full_inputs()
     qg, kg, vg, dog = (to_gpu(x, "bf16") for x in (q, k, v, do))
     announce("ulysses bwd full size: forward and backward of head group 2")
     o, lse = ra.ulysses_fwd(qg, kg, vg, head_group=grp, causal=True, layout="striped")
     dq, dk, dv = ra.ulysses_bwd(qg, kg, vg, o, dog, lse, head_group=grp, causal=True, layout="striped")
-    announce("ulysses bwd full size: rotating ring backward of every shard")
-    rdk = torch.zeros_like(dk)
-    rdv = torch.zeros_like(dv)
-    rdq = []
-    for i in range(N):
-        oi, li = ra.ring_fwd(qg[i].contiguous(), kg, vg, q_shard=i, causal=True, layout="striped")
-        dq_i, dk_i, dv_i = ra.ring_bwd(qg[i].contiguous(), kg, vg, oi, dog[i].contiguous(), li, q_shard=i,
-                                       causal=True, layout="striped")
-        rdq.append(dq_i[:, :, hs].clone())
-        rdk += dk_i
-        rdv += dv_i
     torch.cuda.synchronize()
-    for i in (0, 3, 7):
-        check_grad(dq[i][:, :, hs], f64(rdq[i]), f"full size dq shard {i} vs ring")
-    check_grad(dk[:, :, :, ks], f64(rdk[:, :, :, ks]), "full size dk vs ring")
-    check_grad(dv[:, :, :, ks], f64(rdv[:, :, :, ks]), "full size dv vs ring")
+    cols = bwd_full_cols()
+    announce(f"ulysses bwd full size: oracle dK, dV of {len(cols)} keys from every query shard")
+    rdk, rdv = bwd_full_key_grads(list(range(N)))
+    check_grad(gather_cols(dk, cols, grp), rdk, "full size dk sampled keys")
+    check_grad(gather_cols(dv, cols, grp), rdv, "full size dv sampled keys")
     x = [a.astype(np.float64) for a in (q, k, v, do)]
-    rows = np.array([0, 1, 63, 64, 4095, L - 2, L - 1])
-    for i in (0, 5):
-        announce(f"ulysses bwd full size: oracle dQ rows of shard {i}")
-        ref = shard_dq_rows(x[0][i], x[1], x[2], x[3][i], rows, N=N, shard=i, layout="striped", causal=True)
-        check_grad(dq[i][:, torch.from_numpy(rows).cuda()][:, :, hs], ref[:, :, hs], f"full size dq rows shard {i}")
+    for i in (0, 3, 7):
+        rows = full_size_rows(L, 7007 + i)
+        announce(f"ulysses bwd full size: oracle dQ of {rows.size} rows of shard {i}")
+        ref = oracle_dq_rows(x[0][i][:, :, hs], x[1][:, :, :, grp:grp + 1], x[2][:, :, :, grp:grp + 1],
+                             x[3][i][:, :, hs], rows, N=N, shard=i, layout="striped", causal=True)
+        check_grad(dq[i][:, torch.from_numpy(rows).cuda()][:, :, hs], ref, f"full size dq rows shard {i}")
 
 
 @pytest.mark.parametrize("cfg", [dict(b=1, L=130, h=4, n_kv=2, d=128, N=1),     # no exchange at all
