@@ -30,6 +30,11 @@
  *     logit: LSE = m + ln(sum_j exp(s_j - m)), s_j = scale * q.k_j.  A row with no
  *     allowed key has LSE = -inf and O = 0.
  *   - Thread safety: the library holds no mutable global state; calls are reentrant.
+ *   - Debugging aid: with RA_POISON_STAGING=1 in the environment, the ring passes
+ *     (ra_ring_fwd[_timed], ra_ring_bwd[_timed], ra_ring_bwd_kv_stationary) fill each staging
+ *     buffer with NaN on the copy stream as soon as the step that read it has finished, so a
+ *     step reading a buffer outside the window between its copy and its consumption yields
+ *     NaN.  Off by default; it adds one fill per staged step.
  */
 #ifndef RA_H
 #define RA_H

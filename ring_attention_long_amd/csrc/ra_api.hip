@@ -13,6 +13,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <string>
 
@@ -138,6 +139,26 @@ bool step_is_live(const ra_problem* p, int32_t qs, int32_t ks) {
   return ra::kv_limit(p->causal, p->layout, p->N, p->L, qs, ks, p->L - 1) > 0;
 }
 
+// Debugging aid: with RA_POISON_STAGING=1 in the environment, each KV staging buffer is
+// filled with NaN on the copy stream as soon as the step that read it has finished, so a
+// step that read a buffer outside its staged..consumed window would produce NaN.  Off by
+// default; read on every call.
+bool poison_staging() {
+  const char* v = getenv("RA_POISON_STAGING");
+  return v && v[0] == '1';
+}
+
+// After step k consumed `bytes` at buf (both multiples of 4): make the copy stream wait for the
+// step, then fill the buffer with all-ones bit patterns (NaN in fp32 and in bf16).
+hipError_t poison_after(void* buf, size_t bytes, hipEvent_t consumed, hipStream_t ps, bool split) {
+  hipError_t e;
+  if (split && (e = hipStreamWaitEvent(ps, consumed, 0)) != hipSuccess) return e;
+  uint32_t bits = 0xFFFFFFFFu;
+  float nan_all_ones;
+  memcpy(&nan_all_ones, &bits, 4);
+  return ra::launch_fill_lse((float*)buf, (int64_t)(bytes / 4), nan_all_ones, ps);
+}
+
 // Event set of one ring pass; destroyed on every exit path.
 struct Events {
   hipEvent_t e[2 + 2 * kMaxRing + 4 * RA_MAX_TIMED_STEPS] = {};
@@ -187,6 +208,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   const hipStream_t ps = copy ? (hipStream_t)copy : cs;
   const bool split = ps != cs;
   const bool timing = tm != nullptr;
+  const bool poison = poison_staging();
 
   Events ev;
   hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
@@ -250,6 +272,10 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (poison && k >= 1 &&
+        ((e = poison_after(kbuf[k & 1], shard_bytes, consumed[k], ps, split)) != hipSuccess ||
+         (e = poison_after(vbuf[k & 1], shard_bytes, consumed[k], ps, split)) != hipSuccess))
+      return hip_fail(e, "staging poison");
   }
   const int64_t n_out = (int64_t)p->b * p->L * p->h * p->d;
   if (!have_acc) {
@@ -467,6 +493,7 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   const hipStream_t cs = (hipStream_t)compute;
   const hipStream_t ps = copy ? (hipStream_t)copy : cs;
   const bool split = ps != cs;
+  const bool poison = poison_staging();
 
   Events ev;
   hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
@@ -533,6 +560,10 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (poison && k >= 1 &&
+        ((e = poison_after(kbuf[k & 1], shard_bytes, consumed[k], ps, split)) != hipSuccess ||
+         (e = poison_after(vbuf[k & 1], shard_bytes, consumed[k], ps, split)) != hipSuccess))
+      return hip_fail(e, "staging poison");
   }
   if (timing) {
     hipEvent_t done;
@@ -717,6 +748,7 @@ ra_status ra_ring_bwd_kv_stationary(const ra_problem* p, int32_t ks, const void*
   const hipStream_t cs = (hipStream_t)compute;
   const hipStream_t ps = copy ? (hipStream_t)copy : cs;
   const bool split = ps != cs;
+  const bool poison = poison_staging();
 
   Events ev;
   hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
@@ -767,6 +799,8 @@ ra_status ra_ring_bwd_kv_stationary(const ra_problem* p, int32_t ks, const void*
         return hip_fail(e, "backward step kernel launch");
     }
     if ((e = hipEventRecord(consumed[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (poison && k >= 1 && (e = poison_after(buf[k & 1], w.one, consumed[k], ps, split)) != hipSuccess)
+      return hip_fail(e, "staging poison");
   }
   return RA_OK;
 }
