@@ -15,7 +15,8 @@
  *
  * Conventions for every entry point:
  *   - Pointers named q, k, v, o, lse, ws, ... are DEVICE pointers owned by the caller,
- *     16-byte aligned.  The library never allocates or frees device memory.
+ *     16-byte aligned.  The library never allocates or frees device memory (the one fixed
+ *     array of ra_ring_fwd_noalloc is part of the loaded library, not an allocation).
  *   - Streams are hipStream_t values passed as ra_stream (NULL = the null stream).  Calls
  *     only enqueue work and return; they never synchronise (except ra_ring_fwd_timed).
  *   - Every argument is validated before anything is enqueued; on any error nothing is
@@ -29,7 +30,8 @@
  *   - LSE is the natural-log softmax denominator of each query row, in units of the scaled
  *     logit: LSE = m + ln(sum_j exp(s_j - m)), s_j = scale * q.k_j.  A row with no
  *     allowed key has LSE = -inf and O = 0.
- *   - Thread safety: the library holds no mutable global state; calls are reentrant.
+ *   - Thread safety: calls are reentrant; the only global state is the per-device scratch
+ *     array and events of ra_ring_fwd_noalloc, set up once under a lock (see there).
  *   - Debugging aid: with RA_POISON_STAGING=1 in the environment, the ring passes
  *     (ra_ring_fwd[_timed], ra_ring_bwd[_timed], ra_ring_bwd_kv_stationary) fill each staging
  *     buffer with NaN on the copy stream as soon as the step that read it has finished, so a
@@ -163,6 +165,27 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
                             const void* k_all, const void* v_all, void* o, float* lse, void* ws,
                             size_t ws_bytes, ra_stream compute, ra_stream copy,
                             ra_ring_timing* t);
+
+/* ---------------------------------------------------------------------------------------
+ * ra_ring_fwd_noalloc — ra_ring_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * pass, kernels and results as ra_ring_fwd, with its workspace (the KV staging double buffer
+ * and the fp32 output accumulator) held in a fixed device array of RA_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of a caller buffer; the caller passes inputs and outputs only.
+ * Runs on the calling thread's current device.  Each device holds its own array from the
+ * library's load until the process ends; the first call on a device looks up the array's
+ * address and creates the pass's events (no device memory is allocated then or later).
+ * Errors: as ra_ring_fwd, and RA_ERR_WORKSPACE (nothing enqueued) when
+ * ra_ring_fwd_workspace(p) exceeds RA_NOALLOC_SCRATCH_BYTES (for bf16 that is
+ * 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32, n_kv = 8, d = 128
+ * fits).  Every call on one device shares that device's array and events, and the array
+ * keeps the last call's contents (each pass overwrites everything it reads, so nothing
+ * needs clearing): calls whose work overlaps on one device (different streams, or threads
+ * not ordered by the caller) race and give wrong results, so order them, e.g. on one stream.
+ * ------------------------------------------------------------------------------------- */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ra_status ra_ring_fwd_noalloc(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                              const void* v_all, void* o, float* lse, ra_stream compute, ra_stream copy);
 
 /* ---------------------------------------------------------------------------------------
  * Backward (page 1, "The Backward Pass and Gradient Exchange"; page 4, "The Backward Pass:

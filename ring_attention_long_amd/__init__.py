@@ -35,7 +35,7 @@ import torch
 from . import _lib
 from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, RaUlyssesTiming, check
 
-__all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "allowed_pairs",
+__all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "ring_fwd_noalloc", "allowed_pairs",
            "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_workspace_bytes",
            "ring_bwd_kv_stationary", "ulysses_fwd", "ulysses_fwd_timed", "ulysses_workspace_bytes",
            "ulysses_bwd", "make_problem", "RaError", "library_path"]
@@ -240,6 +240,30 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
         "total_ms": tm.total_ms,
     }
     return o, lse, timing
+
+
+def ring_fwd_noalloc(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
+                     stream=None, copy_stream="auto", out=None, lse_out=None, docs=None):
+    """ring_fwd through ra_ring_fwd_noalloc: no workspace (the library's fixed scratch array of
+    the current device holds it).  Outputs are allocated here unless given."""
+    N, b, L, n_kv, d = k_all.shape
+    h = q.shape[2]
+    _need(q, "q", (b, L, h, d), q.dtype)
+    _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
+    _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
+                     dtype=q.dtype, scale=scale, docs=docs)
+    o = out if out is not None else torch.empty((b, L, h, d), device=q.device, dtype=q.dtype)
+    lse = lse_out if lse_out is not None else torch.empty((b, h, L), device=q.device, dtype=torch.float32)
+    _need(o, "o", (b, L, h, d), q.dtype)
+    _need(lse, "lse", (b, h, L), torch.float32)
+    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    with torch.cuda.device(q.device):
+        check(_lib.lib().ra_ring_fwd_noalloc(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
+                                             _ptr(o), _ptr(lse), _stream(stream),
+                                             ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
+              "ra_ring_fwd_noalloc")
+    return o, lse
 
 
 def ulysses_workspace_bytes(q_all, k_all, *, causal=False, layout="contiguous", scale=None) -> int:

@@ -18,6 +18,7 @@ RA_ERR_HIP = -4
 RA_LAYOUT = {"contiguous": 0, "striped": 1, "zigzag": 2}
 RA_F32, RA_BF16 = 0, 1
 RA_MAX_TIMED_STEPS = 64
+RA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class RaProblem(ctypes.Structure):
@@ -59,6 +60,7 @@ SIGNATURES = [
     ("ra_ring_fwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_ring_fwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V,
                                ctypes.POINTER(RaRingTiming)]),
+    ("ra_ring_fwd_noalloc", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V]),
     ("ra_bwd_preprocess", _I, [_P, _V, _V, _V, _V]),
     ("ra_step_bwd", _I, [_P, _I, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     ("ra_ring_bwd_workspace", _S, [_P]),

@@ -15,6 +15,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "ra_internal.h"
@@ -178,9 +179,18 @@ struct Events {
   }
 };
 
+// Events of one forward pass made ahead of time (the allocation-free entry point keeps one
+// set per device); without one, ring_fwd_impl creates its own for the call.
+struct RingEvents {
+  hipEvent_t entry = nullptr;
+  hipEvent_t staged[kMaxRing] = {};
+  hipEvent_t consumed[kMaxRing] = {};
+};
+
 ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                         const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
-                        ra_stream compute, ra_stream copy, ra_ring_timing* tm) {
+                        ra_stream compute, ra_stream copy, ra_ring_timing* tm,
+                        const RingEvents* pre = nullptr) {
   RA_TRY(check_problem(p));
   RA_TRY(check_shard(p, qs, "q_shard"));
   RA_TRY(check_ptr(q, "q", 16));
@@ -215,10 +225,18 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   hipEvent_t t_sb[RA_MAX_TIMED_STEPS], t_se[RA_MAX_TIMED_STEPS], t_cb[RA_MAX_TIMED_STEPS],
       t_ce[RA_MAX_TIMED_STEPS];
   hipError_t e;
-  if ((e = ev.make(&entry, timing)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-  for (int k = 0; k < N; ++k) {
-    if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-    if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if (pre) {
+    entry = pre->entry;
+    for (int k = 0; k < N; ++k) {
+      staged[k] = pre->staged[k];
+      consumed[k] = pre->consumed[k];
+    }
+  } else {
+    if ((e = ev.make(&entry, timing)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    for (int k = 0; k < N; ++k) {
+      if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+      if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
   }
   if (timing) {
     tm->n_steps = N;
@@ -585,6 +603,57 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   return RA_OK;
 }
 
+// ---- allocation-free forward pass --------------------------------------------------------
+// For callers that cannot allocate device memory: the staging double buffer and the fp32
+// accumulator of ra_ring_fwd live in this fixed device array instead of a caller workspace.
+// Host code never passes `scratch` itself to a kernel or a copy (on the host it only names the
+// symbol); it uses the device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current and kept in g_scratch.
+__device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchDevice {
+  void* ptr = nullptr;   // this device's address of `scratch`
+  RingEvents events;     // made once, reused by every call on the device
+  bool ready = false;
+};
+std::mutex g_scratch_mu;
+ScratchDevice g_scratch[kMaxDevices];
+
+// Set-up on the first call on the current device: the array's address and the events.
+ra_status scratch_for_current_device(const ScratchDevice** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDevice& s = g_scratch[dev];
+  if (!s.ready) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    RingEvents ev;
+    hipEvent_t* all[1 + 2 * kMaxRing];
+    int n = 0;
+    all[n++] = &ev.entry;
+    for (int k = 0; k < kMaxRing; ++k) {
+      all[n++] = &ev.staged[k];
+      all[n++] = &ev.consumed[k];
+    }
+    for (int i = 0; i < n; ++i) {
+      if ((e = hipEventCreateWithFlags(all[i], hipEventDisableTiming)) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(*all[j]);
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+    s.ptr = ptr;
+    s.events = ev;
+    s.ready = true;
+  }
+  *out = &s;
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -657,6 +726,26 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
                             size_t ws_bytes, ra_stream compute, ra_stream copy, ra_ring_timing* t) {
   if (!t) return fail(RA_ERR_INVALID_ARG, "timing output is NULL");
   return ring_fwd_impl(p, q_shard, q, k_all, v_all, o, lse, ws, ws_bytes, compute, copy, t);
+}
+
+ra_status ra_ring_fwd_noalloc(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
+                              const void* v_all, void* o, float* lse, ra_stream compute, ra_stream copy) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_shard(p, q_shard, "q_shard"));
+  RA_TRY(check_ptr(q, "q", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o, "o", 16));
+  RA_TRY(check_ptr(lse, "lse", 4));
+  const size_t need = ra_ring_fwd_workspace(p);
+  if (need > RA_NOALLOC_SCRATCH_BYTES)
+    return fail(RA_ERR_WORKSPACE, "this problem needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                need, (size_t)RA_NOALLOC_SCRATCH_BYTES);
+  if (p->N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", p->N, kMaxRing);
+  const ScratchDevice* s = nullptr;
+  RA_TRY(scratch_for_current_device(&s));
+  return ring_fwd_impl(p, q_shard, q, k_all, v_all, o, lse, s->ptr, RA_NOALLOC_SCRATCH_BYTES, compute, copy,
+                       nullptr, &s->events);
 }
 
 ra_status ra_bwd_preprocess(const ra_problem* p, const void* o, const void* dout, float* delta,

@@ -295,3 +295,23 @@ def test_document_inputs_are_validated():
         ra.document_ranges(np.array([0, 5, 5, 40], dtype=np.int32), N=4, L=10, shard=0)
     with pytest.raises(ra.RaError):
         ra.document_ranges(np.array([0, 39], dtype=np.int32), N=4, L=10, shard=0)
+
+
+def test_noalloc_scratch_limit_and_validation():
+    """ra_ring_fwd_noalloc: the scratch size in the header is the binding's; a problem whose
+    workspace exceeds it, a bad shard and a null pointer are refused before any HIP call."""
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    m = re.search(r"#define RA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.RA_NOALLOC_SCRATCH_BYTES
+    lib = _lib.lib()
+    big = _prob(L=8192, h=32, n_kv=8, d=128, N=2, dtype=_lib.RA_BF16)
+    assert lib.ra_ring_fwd_workspace(ctypes.byref(big)) > _lib.RA_NOALLOC_SCRATCH_BYTES
+    assert lib.ra_ring_fwd_noalloc(ctypes.byref(big), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        _lib.RA_ERR_WORKSPACE
+    assert b"scratch" in lib.ra_last_error()
+    p = _prob()
+    assert lib.ra_ring_fwd_noalloc(ctypes.byref(p), p.N, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        _lib.RA_ERR_INVALID_ARG
+    assert lib.ra_ring_fwd_noalloc(ctypes.byref(p), 0, FAKE, None, FAKE, FAKE, FAKE, None, None) == \
+        _lib.RA_ERR_INVALID_ARG
+    assert b"k_all is NULL" in lib.ra_last_error()
