@@ -7,5 +7,5 @@ from .ring_oracle import (  # noqa: F401
     LAYOUTS, allowed_mask, allowed_pairs, attend, attention_over_shards, brute_force_row, merge,
     document_of, key_grads, online_blocks, ring_order, shard_attention, shard_dq_rows, shard_grads,
     shard_tokens,
-    step_attention,
+    step_attention, usp_tokens,
 )

@@ -86,6 +86,18 @@ def shard_tokens(layout: str, N: int, L: int) -> list[np.ndarray]:
     return [np.concatenate([chunks[p], chunks[2 * N - 1 - p]]) for p in range(N)]
 
 
+def usp_tokens(layout: str, N_h: int, N_s: int, L: int) -> list[np.ndarray]:
+    """Global positions held by each of the N = N_h * N_s devices of the two-dimensional
+    (head x sequence) arrangement, before its first exchange (page 3, section 7: heads and
+    sequence are cut at the same time; section 8's table: during attention a device holds
+    S/N_s tokens of h/N_h heads).  The sequence is cut into N_s ring shards of N_h * L tokens
+    under `layout`, exactly as shard_tokens(layout, N_s, N_h * L); ring shard r is then split
+    into N_h consecutive pieces of L tokens, and device r * N_h + g holds piece g (all
+    heads).  Returns one array of L positions per device, in the device's local order."""
+    ring = shard_tokens(layout, N_s, N_h * L)
+    return [ring[j // N_h][(j % N_h) * L:(j % N_h + 1) * L].copy() for j in range(N_h * N_s)]
+
+
 def ring_order(N: int, shard: int) -> list[int]:
     """KV shard held at ring step k = 0..N-1 by device `shard`.
 

@@ -10,7 +10,9 @@ the per-step example) and page 1 ("Overlapping Arithmetic and Communication Rati
     I = (h / n_kv) * S / (N - 1) FLOPs per received byte;
   * all-to-all sequence parallelism (page 3, sections 4.2 and 7): per device and layer the
     two exchanges move (N-1)/N of its S/N slice of Q and O (h heads) and K and V (n_kv
-    heads), and the attention work is 4 b S^2 (h/N) d, the same as a ring device's.
+    heads), and the attention work is 4 b S^2 (h/N) d, the same as a ring device's;
+  * the two-dimensional arrangement (page 3, sections 7 and 8) receives "between the two,
+    by the split": the all-to-all among N_h devices on S/N_s tokens plus a ring over N_s.
 """
 from __future__ import annotations
 
@@ -55,6 +57,18 @@ def ulysses_bytes_per_device(b: int, S: int, N: int, h: int, n_kv: int, d: int, 
     """Bytes one device receives in the two all-to-all exchanges of one layer: (N-1)/N of an
     S/N slice of Q and O (h heads each) and of K and V (n_kv heads each)."""
     return (N - 1) / N * b * (S / N) * (2 * h + 2 * n_kv) * d * elem_bytes
+
+
+def usp_bytes_per_device(b: int, S: int, N_h: int, N_s: int, h: int, n_kv: int, d: int,
+                         elem_bytes: int) -> float:
+    """Bytes one device of the two-dimensional arrangement (N_h head groups x N_s sequence
+    shards; page 3, sections 7 and 8) receives per layer: the two all-to-all exchanges among
+    the N_h devices that share a ring shard of S/N_s tokens, plus the ring over the N_s
+    devices of its head group, which passes the K and V of n_kv/N_h heads.  N_h = 1 gives
+    the ring's figure and N_s = 1 the all-to-all's; other splits lie between the two."""
+    a2a = ulysses_bytes_per_device(b, S // N_s, N_h, h, n_kv, d, elem_bytes)
+    ring = (N_s - 1) / N_s * 2 * b * S * (n_kv / N_h) * d * elem_bytes
+    return a2a + ring
 
 
 def ulysses_flops_noncausal(b: int, S: int, N: int, h: int, d: int) -> int:

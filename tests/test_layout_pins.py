@@ -105,3 +105,31 @@ def test_page3_causal_utilisation_table(golden):
         N, L = int(N_s), 512
         W = [allowed_pairs("contiguous", N, L, i) for i in range(N)]
         assert 100 * np.mean(W) / max(W) == pytest.approx(pct, abs=tol)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_usp_tokens_reduce_to_the_ring_and_all_to_all_layouts(layout):
+    """The two-dimensional arrangement: N_h = 1 is the ring's sharding, N_s = 1 the all-to-all
+    path's contiguous one; every split is a bijection onto [0, S) whose N_h pieces of a ring
+    shard concatenate to that ring shard."""
+    from oracle import usp_tokens
+    L = 6
+    for N in (1, 2, 4, 6):
+        assert all(np.array_equal(a, b) for a, b in zip(usp_tokens(layout, 1, N, L), shard_tokens(layout, N, L)))
+        flat = usp_tokens(layout, N, 1, L)
+        assert all(np.array_equal(t, np.arange(g * L, (g + 1) * L)) for g, t in enumerate(flat))
+    for N_h, N_s in ((2, 2), (2, 3), (3, 2), (4, 2)):
+        toks = usp_tokens(layout, N_h, N_s, L)
+        S = N_h * N_s * L
+        assert np.array_equal(np.sort(np.concatenate(toks)), np.arange(S))
+        ring = shard_tokens(layout, N_s, N_h * L)
+        for r in range(N_s):
+            assert np.array_equal(np.concatenate(toks[r * N_h:(r + 1) * N_h]), ring[r])
+
+
+def test_usp_tokens_small_example():
+    """8 tokens, 2 head groups x 2 sequence shards, striped: the ring shards are the even and
+    the odd positions; each is split in two halves."""
+    from oracle import usp_tokens
+    toks = usp_tokens("striped", 2, 2, 2)
+    assert [t.tolist() for t in toks] == [[0, 2], [4, 6], [1, 3], [5, 7]]

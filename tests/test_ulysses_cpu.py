@@ -115,3 +115,22 @@ def test_ulysses_bwd_workspace_and_validation():
     assert lib.ra_ulysses_bwd_workspace(ctypes.byref(f32)) == 0 and call(0, prob=f32) == _lib.RA_ERR_UNSUPPORTED
     if _no_hip_device():
         assert call(1) == _lib.RA_ERR_HIP
+
+
+def test_usp_bytes_between_ring_and_all_to_all(golden):
+    """Page 3, section 8's table: the two-dimensional arrangement receives between the ring's
+    (N-1)/N 2 S n_kv d p and the all-to-all's (N-1)/N (S/N)(2h + 2 n_kv) d p, by the split;
+    its limits are those two figures (0.94 and 0.587 GB at the page's shapes)."""
+    g = golden("alltoall_accounting.json")
+    S, b, N, h, n_kv, d, p = (g[k] for k in ("S", "b", "N", "h", "n_kv", "d", "bytes_per_element"))
+    ring = accounting.usp_bytes_per_device(b, S, 1, N, h, n_kv, d, p)
+    a2a = accounting.usp_bytes_per_device(b, S, N, 1, h, n_kv, d, p)
+    assert ring == pytest.approx(accounting.ring_kv_bytes_per_pass(b, S, N, n_kv, d, p))
+    assert a2a == pytest.approx(accounting.ulysses_bytes_per_device(b, S, N, h, n_kv, d, p))
+    assert round(ring / 1e9, 2) == g["ring_gb_gqa"] and round(a2a / 1e9, 3) == g["ulysses_gb_gqa"]
+    for N_h, N_s in ((2, 4), (4, 2)):
+        mid = accounting.usp_bytes_per_device(b, S, N_h, N_s, h, n_kv, d, p)
+        assert a2a < mid < ring
+    # more head groups move more of the traffic into the (cheaper here) all-to-all
+    assert accounting.usp_bytes_per_device(b, S, 4, 2, h, n_kv, d, p) < \
+        accounting.usp_bytes_per_device(b, S, 2, 4, h, n_kv, d, p)
