@@ -71,6 +71,14 @@ ULYSSES_WORKLOADS = {
 ULYSSES_WORKLOADS["ulysses_bwd_striped_causal_8k"] = (
     "ulysses_bwd striped causal, S=65536 N=8 L=8192 h=32 n_kv=8 d=128 bf16, head group 0 (4 query "
     "heads, 1 KV head)", dict(b=1, L=8192, h=32, n_kv=8, d=128, N=8), "striped", True, 0, 1008)
+# heads and sequence cut together (page 3, sections 7 and 8): n_head_groups x N/n_head_groups
+# devices; the last two fields are the device's head group and ring rank
+USP_WORKLOADS = {
+    "usp2x4_striped_causal_32k": ("usp_fwd striped causal over 4 ring shards, S=262144, 8 devices of L=32768 as "
+                                  "2 head groups x 4 ring shards, h=32 n_kv=8 d=128 bf16, device (head group 0, "
+                                  "ring rank 0): 16 query heads, 2 KV heads, 65536 tokens",
+                                  dict(b=1, L=32768, h=32, n_kv=8, d=128, N=8), "striped", True, 2, 0, 0, 1009),
+}
 ULYSSES_METRIC = ("all-to-all sequence-parallel attention TFLOP/s (bf16, causal), one device's share, "
                   "and % of MI355X MFMA peak")
 # packed-document workloads (page 3, section 5): the same shapes with documents of lognormal
@@ -178,6 +186,16 @@ def exposure_band(exposed_ms, compute_ms):
     return "< 5 %" if r < 0.05 else ("5-15 %" if r <= 0.15 else "> 15 %")
 
 
+def receive_over_compute(receive_ms, compute_ms):
+    """Page 3, section 11 (the three-step check, step 3): the share of communication is the
+    per-step receive time over the per-step compute time, both medians of measurements, with
+    no overlap subtracted; under 5 % there is ample room to overlap, 5-15 % whether overlap
+    hides it depends on the implementation, above 15 % the transfer can no longer be ignored."""
+    r = float(np.median(receive_ms)) / float(np.median(compute_ms))
+    band = "< 5 %" if r < 0.05 else ("5-15 %" if r <= 0.15 else "> 15 %")
+    return {"ratio": round(r, 4), "band": band}
+
+
 def timed_passes(one_pass, steps, stream):
     """Run `steps` passes between HIP events on `stream`: mean ms per pass, and the median,
     min and max of the individual passes (an event between passes)."""
@@ -192,6 +210,57 @@ def timed_passes(one_pass, steps, stream):
     mean = ev[0].elapsed_time(ev[steps]) / steps
     return mean, {"median": round(float(np.median(per)), 4), "min": round(min(per), 4),
                   "max": round(max(per), 4)}
+
+
+def forward_passes(ra, q, k_all, v_all, ws, o, lse, *, shard, causal, layout, docs, steps, warmup):
+    """`warmup` untimed then `steps` timed forward ring passes (ra_ring_fwd_timed: HIP events
+    around every step kernel and staging copy on the streams they run on).  Returns the mean
+    ms per pass, the per-pass statistics and the per-step timings of the timed passes."""
+    import torch
+    timings = []
+
+    def one_pass():
+        timings.append(ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
+                                         workspace=ws, out=o, lse_out=lse, docs=docs)[2])
+
+    for i in range(warmup):
+        one_pass()
+        log(f"[bench] warmup {i + 1}/{warmup}")
+    torch.cuda.synchronize()
+    timings.clear()
+    ms, pass_stats = timed_passes(one_pass, steps, torch.cuda.current_stream())
+    return ms, pass_stats, timings
+
+
+def step_kernel_stats(timings, N, shard, step_flops):
+    """Mean duration of each live step's kernel over the timed passes, and the useful FLOPs of
+    those steps (step_flops(src) for the KV shard src a step holds)."""
+    step_ms, live_flops = [], 0
+    for k in range(N):
+        src = (shard - k) % N
+        if timings[0]["step_begin_ms"][k] >= 0:
+            step_ms.append(float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings])))
+            live_flops += step_flops(src)
+    return step_ms, live_flops
+
+
+def forward_summary(ra, accounting, q, k_all, v_all, ws, o, lse, *, cfg, shard, causal, layout, steps, warmup):
+    """A short record of one more forward workload on tensors already in HBM."""
+    b, L, h, d, N = (cfg[x] for x in ("b", "L", "h", "d", "N"))
+    ms, pass_stats, timings = forward_passes(ra, q, k_all, v_all, ws, o, lse, shard=shard, causal=causal,
+                                             layout=layout, docs=None, steps=steps, warmup=warmup)
+    pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+    value = accounting.flops_from_pairs(pairs, h, d) / (ms * 1e-3) / 1e12
+    step_ms, live_flops = step_kernel_stats(
+        timings, N, shard, lambda src: accounting.flops_from_pairs(
+            ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal, layout=layout), h, d))
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    achieved = live_flops / (sum(step_ms) * 1e-3) / 1e12
+    log(f"[bench] {layout} causal={causal}: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+    return {"value": round(value, 2), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100 * value / peak, 2),
+            "ms_per_pass": round(ms, 4), "pass_ms": pass_stats, "steps": steps, "warmup": warmup,
+            "step_kernel_avg_ms": round(float(np.mean(step_ms)), 4),
+            "roofline_frac": round(achieved / peak, 4)}
 
 
 def cpu_baseline_bwd(inp, cfg, layout, causal, shard, budget_s=20.0):
@@ -314,15 +383,28 @@ def oracle_timing():
 
 
 def run_backward(args):
+    result = measure_backward(args.workload, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        import synth
+        desc, cfg, layout, causal, shard, seed = BWD_WORKLOADS[args.workload]
+        inp = synth.shard_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16", with_dout=True)
+        result["cpu_baseline"] = cpu_baseline_bwd(inp, cfg, layout, causal, shard, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def measure_backward(workload, steps, warmup):
+    """Time `steps` backward ring passes (after `warmup`) of a BWD_WORKLOADS entry; returns
+    the bench record without the cpu_baseline."""
     import torch
 
     import ring_attention_long_amd as ra
     import synth
     from ring_attention_long_amd import accounting
 
-    desc, cfg, layout, causal, shard, seed = BWD_WORKLOADS[args.workload]
+    desc, cfg, layout, causal, shard, seed = BWD_WORKLOADS[workload]
     b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
-    log(f"[bench] workload {args.workload}: {desc}")
+    log(f"[bench] workload {workload}: {desc}")
     inp = synth.shard_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16", with_dout=True)
     dev = torch.device("cuda:0")
     g = lambda name: torch.from_numpy(inp[name]).to(dev, torch.bfloat16)  # noqa: E731
@@ -345,14 +427,14 @@ def run_backward(args):
         timings.append(ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal,
                                    layout=layout, workspace=ws, out=out, timed=True)[3])
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         one_pass()
-        log(f"[bench] warmup {i + 1}/{args.warmup}")
+        log(f"[bench] warmup {i + 1}/{warmup}")
     torch.cuda.synchronize()
     timings.clear()
-    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
+    ms, pass_stats = timed_passes(one_pass, steps, compute)
     value = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
+    log(f"[bench] {steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
 
     step_ms, step_flops = [], 0
     for k in range(N):
@@ -370,8 +452,8 @@ def run_backward(args):
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms, 4),
         "pass_ms": pass_stats,
         "higher_is_better": True,
@@ -391,10 +473,7 @@ def run_backward(args):
                      "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4),
                      "timed_over": f"the {len(timings)} timed passes"},
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline_bwd(inp, cfg, layout, causal, shard, args.cpu_budget)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def run_backward_stationary(args):
@@ -599,6 +678,76 @@ def run_ulysses(args):
     print(json.dumps(result), flush=True)
 
 
+def run_usp(args):
+    import torch
+
+    import ring_attention_long_amd as ra
+    import synth
+    from ring_attention_long_amd import accounting
+
+    desc, cfg, layout, causal, N_h, g, r, seed = USP_WORKLOADS[args.workload]
+    b, L, h, n_kv, d, N = (cfg[k] for k in ("b", "L", "h", "n_kv", "d", "N"))
+    N_s, S = N // N_h, N * L
+    log(f"[bench] workload {args.workload}: {desc}")
+    dev = torch.device("cuda:0")
+    mk = lambda name, heads: torch.from_numpy(np.stack([synth.normal((b, L, heads, d), seed=seed, name=name, shard=j)  # noqa: E731
+                                                        for j in range(N)])).to(dev, torch.bfloat16)
+    q_all, k_all, v_all = mk("q", h), mk("k", n_kv), mk("v", n_kv)
+    o_all = torch.zeros((N, b, L, h, d), device=dev, dtype=torch.bfloat16)
+    lse_all = torch.full((N, b, h, L), float("-inf"), device=dev, dtype=torch.float32)
+    ws = torch.empty(ra.usp_workspace_bytes(q_all, k_all, n_head_groups=N_h, causal=causal, layout=layout),
+                     device=dev, dtype=torch.uint8)
+    # the device's work: its ring shard's rows (N_h L tokens) against the sequence, h/N_h heads
+    pairs = ra.allowed_pairs(b=b, L=N_h * L, N=N_s, q_shard=r, causal=causal, layout=layout)
+    flops = accounting.flops_from_pairs(pairs, h // N_h, d)
+    parts = []
+
+    def one_pass():
+        parts.append(ra.usp_fwd(q_all, k_all, v_all, n_head_groups=N_h, head_group=g, ring_rank=r, causal=causal,
+                                layout=layout, workspace=ws, out=o_all, lse_out=lse_all, timed=True)[2])
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    parts.clear()
+    tm = {}
+    for i in range(args.steps):
+        one_pass()
+    tm = {k: float(np.median([t[k] for t in parts])) for k in parts[0]}
+    ms = tm["total_ms"]               # this device's work: its exchanges and its ring (not the others' gathers)
+    value = flops / (ms * 1e-3) / 1e12
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    achieved = flops / (tm["ring_ms"] * 1e-3) / 1e12
+    log(f"[bench] {args.steps} calls: device share {ms:.3f} ms, {value:.1f} TFLOP/s useful")
+    es = 2
+    result = {
+        "metric": "two-dimensional (head x sequence) attention TFLOP/s (bf16, causal), one device's share, "
+                  "and % of MI355X MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "pass_ms": {"median": round(ms, 4), "min": round(min(t["total_ms"] for t in parts), 4),
+                    "max": round(max(t["total_ms"] for t in parts), 4)},
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) bf16 Q/K/V from seeded numpy PCG64",
+        "config": {"workload": desc, "S": S, "N": N, "n_head_groups": N_h, "ring_shards": N_s, "L": L, "b": b,
+                   "h": h, "n_kv": n_kv, "d": d, "layout": layout, "causal": causal, "head_group": g,
+                   "ring_rank": r, "useful_tflop_per_pass": round(flops / 1e12, 4),
+                   "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": f"the ring over {N_s} ring shards (step kernels, merges, staging waits)",
+                     "launches": N_s, "avg_launch_ms": round(tm["ring_ms"] / N_s, 4),
+                     "timed_over": f"the {len(parts)} timed calls (HIP events, median)"},
+        "exchange": {"gather_ms": round(tm["gather_ms"], 4), "ring_ms": round(tm["ring_ms"], 4),
+                     "scatter_ms": round(tm["scatter_ms"], 4),
+                     "other_ring_shards_gather_ms": round(tm["others_gather_ms"], 4),
+                     "usp_bytes_per_device": int(accounting.usp_bytes_per_device(b, S, N_h, N_s, h, n_kv, d, es)),
+                     "ring_bytes_per_device": int(accounting.usp_bytes_per_device(b, S, 1, N, h, n_kv, d, es)),
+                     "alltoall_bytes_per_device": int(accounting.usp_bytes_per_device(b, S, N, 1, h, n_kv, d, es))},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def run_hbm_kernels(args):
     """The HBM-bound pieces alone, at the S = 262144, N = 8 one-device shapes (L = 32768,
     h = 32, n_kv = 8, d = 128): the standalone LSE merge (ra_merge_lse), the finalize
@@ -790,7 +939,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(WORKLOADS) + sorted(BWD_WORKLOADS) + sorted(BWD_STATIONARY_WORKLOADS)
-                    + sorted(ULYSSES_WORKLOADS))
+                    + sorted(ULYSSES_WORKLOADS) + sorted(USP_WORKLOADS))
     ap.add_argument("--oracle-timing", action="store_true",
                     help="CPU only: time the fp64 oracle on each configuration (full or a bounded "
                          "sample, extrapolated) and describe the host")
@@ -801,6 +950,8 @@ def main():
                     help="instead of a workload: the LSE merge, the finalize and a K/V shard copy "
                          "alone, with their HBM GB/s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip the non-causal and backward passes measured beside it")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="instead of the ring pass, run the library's plain fp32 copy kernel "
@@ -825,6 +976,8 @@ def main():
         return run_ulysses(args)
     if args.workload in BWD_STATIONARY_WORKLOADS:
         return run_backward_stationary(args)
+    if args.workload in USP_WORKLOADS:
+        return run_usp(args)
 
     import torch
 
@@ -858,32 +1011,16 @@ def main():
                                        kv_shard=kv_shard, causal=causal, layout=layout)
     pairs = pairs_of()
     flops = accounting.flops_from_pairs(pairs, h, d)
-    compute = torch.cuda.current_stream()
 
     # Every pass records HIP events around each step kernel and each staging copy on the
     # streams they run on (ra_ring_fwd_timed); the roofline's launch durations come from
     # the timed passes themselves.
-    timings = []
-
-    def one_pass():
-        timings.append(ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
-                                         workspace=ws, out=o, lse_out=lse, docs=docs)[2])
-
-    for i in range(args.warmup):
-        one_pass()
-        log(f"[bench] warmup {i + 1}/{args.warmup}")
-    torch.cuda.synchronize()
-    timings.clear()
-    ms, pass_stats = timed_passes(one_pass, args.steps, compute)
+    ms, pass_stats, timings = forward_passes(ra, q, k_all, v_all, ws, o, lse, shard=shard, causal=causal,
+                                             layout=layout, docs=docs, steps=args.steps, warmup=args.warmup)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
-
-    step_ms, live_flops = [], 0
-    for k in range(N):
-        src = (shard - k) % N
-        if timings[0]["step_begin_ms"][k] >= 0:
-            step_ms.append(float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings])))
-            live_flops += accounting.flops_from_pairs(pairs_of(src), h, d)
+    step_ms, live_flops = step_kernel_stats(timings, N, shard,
+                                            lambda src: accounting.flops_from_pairs(pairs_of(src), h, d))
     tm = sorted(timings, key=lambda t: t["total_ms"])[len(timings) // 2]   # the median pass
     kern_ms = sum(step_ms)
     achieved = live_flops / (kern_ms * 1e-3) / 1e12
@@ -903,6 +1040,7 @@ def main():
     kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
     copy_ms = [tm["copy_end_ms"][k] - tm["copy_begin_ms"][k] for k in range(1, N)
                if tm["copy_begin_ms"][k] >= 0]
+    xgmi_ms = kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3
 
     result = {
         "metric": METRIC,
@@ -936,8 +1074,34 @@ def main():
                     "overlap_fraction_per_step": [round(x, 4) for x in overlapped],
                     "exposed_ms_per_step": [round(x, 4) for x in exposed],
                     "exposed_over_compute_band": exposure_band(sum(exposed), kern_ms),
-                    "step_kernel_ms": [round(x, 4) for x in step_ms]},
+                    "step_kernel_ms": [round(x, 4) for x in step_ms],
+                    "receive_over_compute": {
+                        "definition": "page 3 section 11: median per-step receive time / median per-step "
+                                      "compute time, no overlap subtracted",
+                        "on_gpu_copy": receive_over_compute(copy_ms, step_ms) if copy_ms else None,
+                        "xgmi_link_model": dict(receive_over_compute([xgmi_ms], step_ms),
+                                                receive_ms=round(xgmi_ms, 4), link_GBps=XGMI_LINK_GBPS)}},
     }
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extras:
+        # the same run also measures the non-causal pass at the same shapes (on the same
+        # tensors: the step time does not depend on the values) and the backward pass
+        extras = {}
+        log("[bench] also: non-causal pass at the same shapes")
+        extras["noncausal_32k"] = dict(
+            forward_summary(ra, accounting, q, k_all, v_all, ws, o, lse, cfg=cfg, shard=shard, causal=False,
+                            layout="contiguous", steps=args.steps, warmup=args.warmup),
+            workload="ring_fwd non-causal, S=262144 N=8 L=32768 h=32 n_kv=8 d=128 bf16, shard 0 (same tensors)")
+        del q, k_all, v_all, ws, o, lse
+        torch.cuda.empty_cache()
+        log("[bench] also: backward pass")
+        bwd = measure_backward("bwd_striped_causal_8k", args.steps, args.warmup)
+        extras["bwd_striped_causal_8k"] = {
+            "workload": bwd["config"]["workload"], "metric": bwd["metric"], "value": bwd["value"],
+            "unit": "TFLOP/s", "pct_of_bf16_peak": bwd["config"]["pct_of_bf16_peak"],
+            "ms_per_pass": bwd["ms_per_step"], "pass_ms": bwd["pass_ms"], "steps": bwd["steps"],
+            "warmup": bwd["warmup"], "roofline_frac": bwd["roofline"]["frac"],
+            "step_avg_ms": bwd["roofline"]["avg_launch_ms"]}
+        result["also_measured"] = extras
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(inp, cfg, layout, causal, shard, args.cpu_budget,

@@ -304,6 +304,45 @@ ra_status ra_ulysses_bwd(const ra_problem* p, int32_t head_group, const void* q_
                          float* dq_all, float* dk_all, float* dv_all, void* ws, size_t ws_bytes,
                          ra_stream stream);
 
+/* ---- Heads and sequence cut together, one device's share (page 3, sections 7 and 8) ----
+ * The two-dimensional arrangement that combines both schemes: N = N_h * N_s devices
+ * (N_h = n_head_groups).  The sequence is cut into N_s ring shards of N_h L tokens under
+ * p->layout (as the ring cuts it into shards); ring shard r is split into N_h consecutive
+ * pieces of L tokens, and device r N_h + g holds piece g for every head (its local order).
+ * Device (g, r) trades pieces with the other devices of ring shard r in an all-to-all (first
+ * exchange) for the whole ring shard of head group g: query heads [g h/N_h, (g+1) h/N_h) and
+ * KV heads [g n_kv/N_h, (g+1) n_kv/N_h), S/N_s tokens of h/N_h heads as page 3's table puts
+ * it.  It then runs the ring of ra_ring_fwd over the N_s ring shards with the devices of head
+ * group g (KV staged on `copy` as there), and sends each piece's rows back (second exchange).
+ * Both dimensions must divide: N_h divides N, h and n_kv (RA_ERR_INVALID_ARG otherwise).
+ *
+ * ra_usp_fwd computes device (head_group, ring_rank)'s share on one GPU where the N devices'
+ * inputs are resident: q_all [N][b][L][h][d], k_all and v_all [N][b][L][n_kv][d] as above.  It
+ * writes query heads of head_group for devices ring_rank N_h .. ring_rank N_h + N_h - 1 of
+ * o_all [N][b][L][h][d] (dtype) and lse_all [N][b][h][L] (fp32), leaving everything else; one
+ * call per (head group, ring rank) fills the outputs, which equal plain attention of each
+ * device's queries over the whole sequence by global position.  The other ring shards' first
+ * exchanges (what the other devices of head group g gather for themselves, and the ring hands
+ * over) run first in the same call.  Workspace: ra_usp_fwd_workspace(p, n_head_groups)
+ * bytes (the gathered Q of the ring shard, K and V of every ring shard for the head group, an
+ * fp32 output, the LSE and the ring's staging buffers), 0 if invalid for this path.  No
+ * packed documents (RA_ERR_UNSUPPORTED).  ra_usp_fwd_timed also reports the parts' times
+ * (HIP events on `compute`, ms) and waits for the call to finish. */
+typedef struct ra_usp_timing {
+  float others_gather_ms; /* the other ring shards' first exchanges (not this device's work) */
+  float gather_ms;        /* this device's first exchange                                    */
+  float ring_ms;          /* the ring over the N_s ring shards                               */
+  float scatter_ms;       /* the second exchange                                             */
+  float total_ms;         /* gather + ring + scatter                                         */
+} ra_usp_timing;
+size_t ra_usp_fwd_workspace(const ra_problem* p, int32_t n_head_groups);
+ra_status ra_usp_fwd(const ra_problem* p, int32_t n_head_groups, int32_t head_group, int32_t ring_rank,
+                     const void* q_all, const void* k_all, const void* v_all, void* o_all, float* lse_all, void* ws,
+                     size_t ws_bytes, ra_stream compute, ra_stream copy);
+ra_status ra_usp_fwd_timed(const ra_problem* p, int32_t n_head_groups, int32_t head_group, int32_t ring_rank,
+                           const void* q_all, const void* k_all, const void* v_all, void* o_all, float* lse_all,
+                           void* ws, size_t ws_bytes, ra_stream compute, ra_stream copy, ra_usp_timing* t);
+
 /* Host-only (no GPU work): number of (query, key) pairs shard q_shard may attend to in KV
  * shard kv_shard (or the whole sequence when kv_shard = -1), summed over the batch.  Useful
  * FLOPs of the forward are 4 * d * h * pairs (page 3, section 2: two GEMMs, 2 FLOPs per

@@ -38,7 +38,7 @@ from ._lib import RA_BF16, RA_F32, RA_LAYOUT, RaError, RaProblem, RaRingTiming, 
 __all__ = ["step_fwd", "merge_lse", "finalize", "ring_fwd", "ring_fwd_timed", "ring_fwd_noalloc", "allowed_pairs",
            "bwd_preprocess", "step_bwd", "ring_bwd", "ring_bwd_workspace_bytes",
            "ring_bwd_kv_stationary", "ulysses_fwd", "ulysses_fwd_timed", "ulysses_workspace_bytes",
-           "ulysses_bwd", "make_problem", "RaError", "library_path"]
+           "ulysses_bwd", "usp_fwd", "usp_workspace_bytes", "make_problem", "RaError", "library_path"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 _copy_streams: dict[int, torch.cuda.Stream] = {}
@@ -357,6 +357,50 @@ def ulysses_bwd(q_all, k_all, v_all, o_all, dout_all, lse_all, *, head_group, ca
                                     _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
           "ra_ulysses_bwd")
     return dq, dk, dv
+
+
+def usp_workspace_bytes(q_all, k_all, *, n_head_groups, causal=False, layout="contiguous", scale=None) -> int:
+    N, b, L, h, d = q_all.shape
+    p = make_problem(b=b, L=L, h=h, n_kv=k_all.shape[3], d=d, N=N, causal=causal, layout=layout,
+                     dtype=q_all.dtype, scale=scale)
+    return int(_lib.lib().ra_usp_fwd_workspace(ctypes.byref(p), n_head_groups))
+
+
+def usp_fwd(q_all, k_all, v_all, *, n_head_groups, head_group, ring_rank, causal=False, layout="contiguous",
+            scale=None, stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, timed=False):
+    """Device (head_group, ring_rank)'s share of the two-dimensional arrangement (n_head_groups
+    head groups x N / n_head_groups ring shards): q_all [N, b, L, h, d], k_all, v_all
+    [N, b, L, n_kv, d], device r * n_head_groups + g holding piece g of ring shard r.  Writes
+    the head group's heads of the ring shard's devices into out [N, b, L, h, d] and lse_out
+    [N, b, h, L] (allocated if None: zeros and -inf elsewhere) and returns them (and, with
+    timed=True, the parts' times in ms; that call synchronises)."""
+    N, b, L, h, d = q_all.shape
+    n_kv = k_all.shape[3]
+    _need(q_all, "q_all", (N, b, L, h, d), q_all.dtype)
+    _need(k_all, "k_all", (N, b, L, n_kv, d), q_all.dtype)
+    _need(v_all, "v_all", (N, b, L, n_kv, d), q_all.dtype)
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout, dtype=q_all.dtype,
+                     scale=scale)
+    need = int(_lib.lib().ra_usp_fwd_workspace(ctypes.byref(p), n_head_groups))
+    if need == 0:
+        raise RaError(int(_lib.RA_ERR_INVALID_ARG), "ra_usp_fwd_workspace")
+    if workspace is None:
+        workspace = torch.empty(need, device=q_all.device, dtype=torch.uint8)
+    o = out if out is not None else torch.zeros((N, b, L, h, d), device=q_all.device, dtype=q_all.dtype)
+    lse = lse_out if lse_out is not None else torch.full((N, b, h, L), float("-inf"), device=q_all.device,
+                                                         dtype=torch.float32)
+    _need(o, "o_all", (N, b, L, h, d), q_all.dtype)
+    _need(lse, "lse_all", (N, b, h, L), torch.float32)
+    cs = copy_stream_for(q_all.device) if copy_stream == "auto" else copy_stream
+    args = (ctypes.byref(p), n_head_groups, head_group, ring_rank, _ptr(q_all), _ptr(k_all), _ptr(v_all), _ptr(o),
+            _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
+            ctypes.c_void_p(cs.cuda_stream) if cs is not None else None)
+    if not timed:
+        check(_lib.lib().ra_usp_fwd(*args), "ra_usp_fwd")
+        return o, lse
+    tm = _lib.RaUspTiming()
+    check(_lib.lib().ra_usp_fwd_timed(*args, ctypes.byref(tm)), "ra_usp_fwd_timed")
+    return o, lse, {k: getattr(tm, k) for k, _ in _lib.RaUspTiming._fields_}
 
 
 def bwd_preprocess(o, dout, *, stream=None):

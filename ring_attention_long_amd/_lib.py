@@ -47,6 +47,11 @@ class RaUlyssesTiming(ctypes.Structure):
                 ("scatter_ms", ctypes.c_float), ("total_ms", ctypes.c_float)]
 
 
+class RaUspTiming(ctypes.Structure):
+    _fields_ = [("others_gather_ms", ctypes.c_float), ("gather_ms", ctypes.c_float),
+                ("ring_ms", ctypes.c_float), ("scatter_ms", ctypes.c_float), ("total_ms", ctypes.c_float)]
+
+
 # (name, restype, argtypes) of every exported entry point, in include/ra.h order.
 _P = ctypes.POINTER(RaProblem)
 _V = ctypes.c_void_p
@@ -75,6 +80,10 @@ SIGNATURES = [
                                   ctypes.POINTER(RaUlyssesTiming)]),
     ("ra_ulysses_bwd_workspace", _S, [_P]),
     ("ra_ulysses_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V]),
+    ("ra_usp_fwd_workspace", _S, [_P, _I]),
+    ("ra_usp_fwd", _I, [_P, _I, _I, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
+    ("ra_usp_fwd_timed", _I, [_P, _I, _I, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V,
+                              ctypes.POINTER(RaUspTiming)]),
     ("ra_allowed_pairs", ctypes.c_int64, [_P, _I, _I]),
     ("ra_allowed_pairs_packed", ctypes.c_int64, [_P, _I, _I, _V, _V]),
     ("ra_document_ranges", _I, [_P, _I, _V, _I, _V, _V]),

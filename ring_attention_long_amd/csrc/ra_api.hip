@@ -179,6 +179,11 @@ struct Events {
   }
 };
 
+// The KV staging double buffer of a forward or backward ring pass: K and V of two shards.
+size_t staging_bytes(const ra_problem* p) {
+  return 4 * align_up((size_t)p->b * p->L * p->n_kv * p->d * elem_size(p), 256);
+}
+
 // Events of one forward pass made ahead of time (the allocation-free entry point keeps one
 // set per device); without one, ring_fwd_impl creates its own for the call.
 struct RingEvents {
@@ -190,16 +195,18 @@ struct RingEvents {
 ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                         const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
                         ra_stream compute, ra_stream copy, ra_ring_timing* tm,
-                        const RingEvents* pre = nullptr) {
+                        const RingEvents* pre = nullptr, float* o_acc_ext = nullptr) {
+  // o_acc_ext: leave the merged fp32 result there (no cast to p->dtype, o unused) and use
+  // the workspace for the staging buffers only.
   RA_TRY(check_problem(p));
   RA_TRY(check_shard(p, qs, "q_shard"));
   RA_TRY(check_ptr(q, "q", 16));
   RA_TRY(check_ptr(k_all, "k_all", 16));
   RA_TRY(check_ptr(v_all, "v_all", 16));
-  RA_TRY(check_ptr(o, "o", 16));
+  if (!o_acc_ext) RA_TRY(check_ptr(o, "o", 16));
   RA_TRY(check_ptr(lse, "lse", 4));
   RA_TRY(check_ptr(ws, "ws", 16));
-  const size_t need = ra_ring_fwd_workspace(p);
+  const size_t need = o_acc_ext ? staging_bytes(p) : ra_ring_fwd_workspace(p);
   if (ws_bytes < need)
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
   const int N = p->N;
@@ -212,7 +219,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   char* wsc = (char*)ws;
   char* kbuf[2] = {wsc, wsc + 2 * A};
   char* vbuf[2] = {wsc + A, wsc + 3 * A};
-  float* o_acc = p->dtype == RA_F32 ? (float*)o : (float*)(wsc + 4 * A);
+  float* o_acc = o_acc_ext ? o_acc_ext : p->dtype == RA_F32 ? (float*)o : (float*)(wsc + 4 * A);
   float* lse_acc = lse;
   const hipStream_t cs = (hipStream_t)compute;
   const hipStream_t ps = copy ? (hipStream_t)copy : cs;
@@ -302,7 +309,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     if ((e = ra::launch_fill_lse(lse_acc, (int64_t)p->b * p->h * p->L, -INFINITY, cs)) != hipSuccess)
       return hip_fail(e, "fill kernel launch");
   }
-  if (p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess)
+  if (!o_acc_ext && p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess)
     return hip_fail(e, "finalize kernel launch");
 
   if (timing) {
@@ -424,6 +431,137 @@ ra_status ulysses_fwd_impl(const ra_problem* p, int32_t group, const void* q_all
     (void)hipEventElapsedTime(&tm->attend_ms, t1, t2);
     (void)hipEventElapsedTime(&tm->scatter_ms, t2, t3);
     (void)hipEventElapsedTime(&tm->total_ms, t0, t3);
+  }
+  return RA_OK;
+}
+
+// ---- two-dimensional arrangement: head groups x sequence ring (page 3, sections 7, 8) ----
+// N = N_h * N_s devices.  The sequence is cut into N_s ring shards of N_h L tokens under
+// p->layout; ring shard r is split into N_h consecutive pieces of L tokens and device
+// r N_h + g holds piece g for every head.  Device (g, r) trades pieces with the other N_h - 1
+// devices of ring shard r (first exchange) for the whole ring shard of its head group (h/N_h
+// query heads, n_kv/N_h KV heads), runs the ring over the N_s ring shards with the devices of
+// its head group, and sends each piece's rows back (second exchange).
+ra_status check_usp(const ra_problem* p, int32_t n_hg) {
+  if (!p) return fail(RA_ERR_INVALID_ARG, "problem is NULL");
+  // the layout cuts ring shards of n_hg L tokens (checked on the ring problem), not pieces
+  ra_problem pieces = *p;
+  if (pieces.layout == RA_LAYOUT_ZIGZAG) pieces.layout = RA_LAYOUT_CONTIGUOUS;
+  RA_TRY(check_problem(&pieces));
+  if (p->doc_begin) return fail(RA_ERR_UNSUPPORTED, "packed documents are not supported by the two-dimensional path");
+  if (n_hg < 1 || p->N % n_hg)
+    return fail(RA_ERR_INVALID_ARG, "n_head_groups=%d must divide the device count N=%d", n_hg, p->N);
+  if (p->h % n_hg || p->n_kv % n_hg)
+    return fail(RA_ERR_INVALID_ARG, "the two-dimensional path splits heads over n_head_groups=%d: h=%d and n_kv=%d "
+                "must be multiples of it", n_hg, p->h, p->n_kv);
+  if (p->b > 65535) return fail(RA_ERR_UNSUPPORTED, "batch %d above 65535", p->b);
+  return RA_OK;
+}
+
+// The ring problem one device runs after the first exchange.
+ra_problem usp_ring_problem(const ra_problem* p, int32_t n_hg) {
+  ra_problem r = *p;
+  r.L = p->L * n_hg;
+  r.h = p->h / n_hg;
+  r.n_kv = p->n_kv / n_hg;
+  r.N = p->N / n_hg;
+  r.scale = effective_scale(p);
+  r.doc_begin = r.doc_end = nullptr;
+  return r;
+}
+
+struct UspWs {
+  size_t q, kv, o, lse, staging, total;
+};
+UspWs usp_ws(const ra_problem* rp) {
+  const size_t es = elem_size(rp);
+  UspWs w;
+  w.q = align_up((size_t)rp->b * rp->L * rp->h * rp->d * es, 256);
+  w.kv = align_up((size_t)rp->N * rp->b * rp->L * rp->n_kv * rp->d * es, 256);   // every ring shard's K (or V)
+  w.o = align_up((size_t)rp->b * rp->L * rp->h * rp->d * 4, 256);
+  w.lse = align_up((size_t)rp->b * rp->h * rp->L * 4, 256);
+  w.staging = staging_bytes(rp);
+  w.total = w.q + 2 * w.kv + w.o + w.lse + w.staging;
+  return w;
+}
+
+ra_status usp_fwd_impl(const ra_problem* p, int32_t n_hg, int32_t g, int32_t r, const void* q_all,
+                       const void* k_all, const void* v_all, void* o_all, float* lse_all, void* ws, size_t ws_bytes,
+                       ra_stream compute, ra_stream copy, ra_usp_timing* tm) {
+  RA_TRY(check_usp(p, n_hg));
+  const ra_problem rp = usp_ring_problem(p, n_hg);
+  RA_TRY(check_problem(&rp));
+  if (g < 0 || g >= n_hg) return fail(RA_ERR_INVALID_ARG, "head_group=%d outside [0, %d)", g, n_hg);
+  RA_TRY(check_shard(&rp, r, "ring_rank"));
+  RA_TRY(check_ptr(q_all, "q_all", 16));
+  RA_TRY(check_ptr(k_all, "k_all", 16));
+  RA_TRY(check_ptr(v_all, "v_all", 16));
+  RA_TRY(check_ptr(o_all, "o_all", 16));
+  RA_TRY(check_ptr(lse_all, "lse_all", 4));
+  RA_TRY(check_ptr(ws, "ws", 16));
+  const UspWs w = usp_ws(&rp);
+  if (ws_bytes < w.total) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+  if (rp.N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N_s=%d above %d", rp.N, kMaxRing);
+
+  char* base = (char*)ws;
+  char* q_g = base;
+  char* k_ring = base + w.q;
+  char* v_ring = k_ring + w.kv;
+  float* o_g = (float*)(v_ring + w.kv);
+  float* lse_g = (float*)((char*)o_g + w.o);
+  char* staging = (char*)lse_g + w.lse;
+  const hipStream_t s = (hipStream_t)compute;
+  const int es = (int)elem_size(p), Hg = rp.h, Kg = rp.n_kv, N_s = rp.N;
+  // bytes of one device's shard of q (all heads) and of k (all KV heads)
+  const size_t dev_q = (size_t)p->b * p->L * p->h * p->d * es, dev_kv = (size_t)p->b * p->L * p->n_kv * p->d * es;
+  const size_t ring_kv = (size_t)rp.b * rp.L * Kg * p->d * es;   // one ring shard's K of the head group
+  const char* qc = (const char*)q_all;
+  const char* kc = (const char*)k_all;
+  const char* vc = (const char*)v_all;
+
+  Events ev;
+  hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr, t4 = nullptr;
+  hipError_t e;
+  if (tm && ((e = ev.make(&t0, true)) != hipSuccess || (e = ev.make(&t1, true)) != hipSuccess ||
+             (e = ev.make(&t2, true)) != hipSuccess || (e = ev.make(&t3, true)) != hipSuccess ||
+             (e = ev.make(&t4, true)) != hipSuccess))
+    return hip_fail(e, "hipEventCreate");
+  auto gather_kv = [&](int rr) -> hipError_t {
+    hipError_t x = ra::launch_ulysses_gather(k_ring + (size_t)rr * ring_kv, kc + (size_t)rr * n_hg * dev_kv, p->b,
+                                             p->L, n_hg, RA_LAYOUT_CONTIGUOUS, p->n_kv, Kg, g * Kg, p->d, es, s);
+    if (x != hipSuccess) return x;
+    return ra::launch_ulysses_gather(v_ring + (size_t)rr * ring_kv, vc + (size_t)rr * n_hg * dev_kv, p->b, p->L,
+                                     n_hg, RA_LAYOUT_CONTIGUOUS, p->n_kv, Kg, g * Kg, p->d, es, s);
+  };
+  // The first exchanges of the other ring shards: what the other devices of head group g
+  // gather for themselves; on a real machine the ring below receives them from those devices.
+  if (tm && (e = hipEventRecord(t0, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  for (int rr = 0; rr < N_s; ++rr)
+    if (rr != r && (e = gather_kv(rr)) != hipSuccess) return hip_fail(e, "gather kernel launch");
+  // This device's first exchange: Q, K and V of head group g for the whole ring shard r.
+  if (tm && (e = hipEventRecord(t1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = ra::launch_ulysses_gather(q_g, qc + (size_t)r * n_hg * dev_q, p->b, p->L, n_hg, RA_LAYOUT_CONTIGUOUS, p->h,
+                                     Hg, g * Hg, p->d, es, s)) != hipSuccess ||
+      (e = gather_kv(r)) != hipSuccess)
+    return hip_fail(e, "gather kernel launch");
+  if (tm && (e = hipEventRecord(t2, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  // The ring over the N_s ring shards, the merged fp32 result left in o_g.
+  RA_TRY(ring_fwd_impl(&rp, r, q_g, k_ring, v_ring, nullptr, lse_g, staging, w.staging, compute, copy, nullptr,
+                       nullptr, o_g));
+  if (tm && (e = hipEventRecord(t3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  // Second exchange: rows [g' L, (g'+1) L) of the ring shard go back to device r N_h + g'.
+  if ((e = ra::launch_ulysses_scatter((char*)o_all + (size_t)r * n_hg * dev_q,
+                                      lse_all + (size_t)r * n_hg * p->b * p->h * p->L, o_g, lse_g, p->b, p->L, n_hg,
+                                      RA_LAYOUT_CONTIGUOUS, p->h, Hg, g * Hg, p->d, p->dtype, s)) != hipSuccess)
+    return hip_fail(e, "scatter kernel launch");
+  if (tm) {
+    if ((e = hipEventRecord(t4, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipEventSynchronize(t4)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    (void)hipEventElapsedTime(&tm->others_gather_ms, t0, t1);
+    (void)hipEventElapsedTime(&tm->gather_ms, t1, t2);
+    (void)hipEventElapsedTime(&tm->ring_ms, t2, t3);
+    (void)hipEventElapsedTime(&tm->scatter_ms, t3, t4);
+    tm->total_ms = tm->gather_ms + tm->ring_ms + tm->scatter_ms;
   }
   return RA_OK;
 }
@@ -922,6 +1060,28 @@ int64_t ra_allowed_pairs_packed(const ra_problem* p, int32_t q_shard, int32_t kv
       }
     }
   return total;
+}
+
+size_t ra_usp_fwd_workspace(const ra_problem* p, int32_t n_head_groups) {
+  if (check_usp(p, n_head_groups) != RA_OK) return 0;
+  const ra_problem rp = usp_ring_problem(p, n_head_groups);
+  if (check_problem(&rp) != RA_OK) return 0;
+  return usp_ws(&rp).total;
+}
+
+ra_status ra_usp_fwd(const ra_problem* p, int32_t n_head_groups, int32_t head_group, int32_t ring_rank,
+                     const void* q_all, const void* k_all, const void* v_all, void* o_all, float* lse_all, void* ws,
+                     size_t ws_bytes, ra_stream compute, ra_stream copy) {
+  return usp_fwd_impl(p, n_head_groups, head_group, ring_rank, q_all, k_all, v_all, o_all, lse_all, ws, ws_bytes,
+                      compute, copy, nullptr);
+}
+
+ra_status ra_usp_fwd_timed(const ra_problem* p, int32_t n_head_groups, int32_t head_group, int32_t ring_rank,
+                           const void* q_all, const void* k_all, const void* v_all, void* o_all, float* lse_all,
+                           void* ws, size_t ws_bytes, ra_stream compute, ra_stream copy, ra_usp_timing* t) {
+  if (!t) return fail(RA_ERR_INVALID_ARG, "timing output is NULL");
+  return usp_fwd_impl(p, n_head_groups, head_group, ring_rank, q_all, k_all, v_all, o_all, lse_all, ws, ws_bytes,
+                      compute, copy, t);
 }
 
 size_t ra_ulysses_bwd_workspace(const ra_problem* p) {

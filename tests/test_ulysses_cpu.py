@@ -134,3 +134,37 @@ def test_usp_bytes_between_ring_and_all_to_all(golden):
     # more head groups move more of the traffic into the (cheaper here) all-to-all
     assert accounting.usp_bytes_per_device(b, S, 4, 2, h, n_kv, d, p) < \
         accounting.usp_bytes_per_device(b, S, 2, 4, h, n_kv, d, p)
+
+
+def test_usp_workspace_and_validation():
+    """The two-dimensional path: workspace = the ring shard's gathered Q, K and V of every ring
+    shard (head group), an fp32 output, the LSE and the ring's two staging buffers; both
+    dimensions must divide; bad ranks, pointers and workspaces are refused before any launch."""
+    lib = _lib.lib()
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    p = _prob(L=100, h=8, n_kv=4, N=4, layout=2)                 # N_h = 2, N_s = 2: ring shards of 200 tokens
+    Lr, Hg, Kg, Ns = 200, 4, 2, 2
+    want = pad(Lr * Hg * 128 * 2) + 2 * pad(Ns * Lr * Kg * 128 * 2) + pad(Lr * Hg * 128 * 4) + pad(Hg * Lr * 4) \
+        + 4 * pad(Lr * Kg * 128 * 2)
+    assert lib.ra_usp_fwd_workspace(ctypes.byref(p), 2) == want
+    few_kv = _prob(L=100, h=8, n_kv=2, N=4)
+    for pp, n_hg, why in ((p, 3, b"divide"), (p, 8, b"divide"), (p, 0, b"divide"), (few_kv, 4, b"multiples")):
+        assert lib.ra_usp_fwd_workspace(ctypes.byref(pp), n_hg) == 0
+        assert lib.ra_usp_fwd(ctypes.byref(pp), n_hg, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None,
+                              None) == _lib.RA_ERR_INVALID_ARG
+        assert why in lib.ra_last_error()
+    odd = _prob(L=3, h=8, n_kv=4, N=4, layout=2)                  # zigzag ring shard of 3 tokens (N_h = 1)
+    assert lib.ra_usp_fwd_workspace(ctypes.byref(odd), 1) == 0
+    assert lib.ra_usp_fwd_workspace(ctypes.byref(odd), 2) > 0      # 6 tokens per ring shard: even
+    call = lambda g, r, q=FAKE, ws=want: lib.ra_usp_fwd(  # noqa: E731
+        ctypes.byref(p), 2, g, r, q, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None)
+    assert call(2, 0) == _lib.RA_ERR_INVALID_ARG and b"head_group" in lib.ra_last_error()
+    assert call(0, 2) == _lib.RA_ERR_INVALID_ARG and b"ring_rank" in lib.ra_last_error()
+    assert call(0, 0, q=None) == _lib.RA_ERR_INVALID_ARG and b"q_all is NULL" in lib.ra_last_error()
+    assert call(0, 0, ws=want - 1) == _lib.RA_ERR_WORKSPACE
+    assert lib.ra_usp_fwd_timed(ctypes.byref(p), 2, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, want, None, None,
+                                None) == _lib.RA_ERR_INVALID_ARG
+    pd = _prob(L=100, h=8, n_kv=4, N=4)
+    pd.doc_begin = pd.doc_end = FAKE.value
+    assert lib.ra_usp_fwd(ctypes.byref(pd), 2, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, want, None, None) == \
+        _lib.RA_ERR_UNSUPPORTED
