@@ -135,16 +135,22 @@ __device__ __forceinline__ dma_rsrc make_dma_rsrc(const void* base, unsigned num
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_to_lds(dma_rsrc rsrc, const void* lds_dst, unsigned voffset,
+// 32-bit LDS byte address of a __shared__ object: taken from the object itself (a link-time
+// constant), so that stage and slot offsets stay plain scalar integer arithmetic instead of
+// generic-pointer arithmetic with its null checks.
+#define RA_LDS_ADDR(obj) ((unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)(obj))
+
+// One 1 KB LDS-DMA load: 16 bytes per lane from the buffer at voffset + soffset into LDS at
+// lds_addr + 16 lane (lds_addr is wave-uniform).
+__device__ __forceinline__ void dma16_to_lds(dma_rsrc rsrc, unsigned lds_addr, unsigned voffset,
                                              unsigned soffset) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
   // s_nop: one wait state between writing M0 and an LDS-DMA load that reads it.  No memory
   // clobber: the destination is never read before the caller's wait and barrier, and the
   // compiler may keep scheduling LDS reads of other buffers around the load.
   __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    :
-                   : "s"(m), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
+                   : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(rsrc),
+                     "s"(__builtin_amdgcn_readfirstlane(soffset))
                    : "m0");
 }
 #pragma clang diagnostic pop

@@ -53,12 +53,12 @@ __device__ __forceinline__ unsigned dma_lane_offset(unsigned row_stride, int lan
   const int lrow = lane >> 4;
   return (unsigned)lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow + w)) * 16;
 }
-__device__ __forceinline__ void dma_tile(dma_rsrc rsrc, char* dst, unsigned lane_off, unsigned row0_off,
+__device__ __forceinline__ void dma_tile(dma_rsrc rsrc, unsigned dst, unsigned lane_off, unsigned row0_off,
                                          unsigned row_stride, int w) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int i = w + 4 * t;
-    dma16_to_lds(rsrc, dst + 1024 * i, lane_off, row0_off + (unsigned)(4 * i) * row_stride);
+    dma16_to_lds(rsrc, dst + 1024u * i, lane_off, row0_off + (unsigned)(4 * i) * row_stride);
   }
 }
 // Buffer descriptor covering rows 0..rows-1 (row_stride bytes apart, 256 B each) from base;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   // load i = wq + 4 (k % 4) of the 16 that fill a tile (see dma_tile).
   auto stage_dma_one = [&](const Cursor& c, int buf, int k) __attribute__((always_inline)) {
     const int i = wq + 4 * (k & 3);
-    char* dst = smem + buf * STAGE_BYTES + (k >> 2) * TILE_BYTES + 1024 * i;
+    const unsigned dst = RA_LDS_ADDR(smem) + (unsigned)(buf * STAGE_BYTES + (k >> 2) * TILE_BYTES + 1024 * i);
     dma16_to_lds(k < 4 ? q_rsrc : o_rsrc, dst, q_lane_off,
                  (unsigned)c.hq * ROW_BYTES + (unsigned)(c.tq0 + 4 * i) * q_stride);
   };
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = wave + 8 * t;            // i % 4 == wave % 4
-      dma16_to_lds(vr, smem + V_OFF + 1024 * i, v_lane_off, (unsigned)(u0 + 4 * i) * kv_stride);
+      dma16_to_lds(vr, RA_LDS_ADDR(smem) + (unsigned)(V_OFF + 1024 * i), v_lane_off, (unsigned)(u0 + 4 * i) * kv_stride);
     }
     u32x4* z = (u32x4*)(smem + 2 * STAGE_BYTES);   // stage 2 is read (with P = 0) before its first tile
     for (int i = tid; i < STAGE_BYTES / 16; i += KV_THREADS) z[i] = u32x4{};
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   const unsigned lane_off = dma_lane_offset(row_stride, lane, wave & 3);
   // tile `tile` of K or V into an LDS stage (this wave's four loads); tiles past the last
   // point beyond the buffer: zeros, no memory traffic, into a stage nobody reads again
-  auto tile_dma = [&](const dma_rsrc& r, char* dst, int tile) {
+  auto tile_dma = [&](const dma_rsrc& r, unsigned dst, int tile) {
     dma_tile(r, dst, lane_off, tile < n_tiles ? (unsigned)(tile * 64) * row_stride : 0x80000000u,
              row_stride, wave & 3);
   };
@@ -774,8 +774,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   // Accumulator layout: lane = query, register i of block jj = key
   // 64 j + 32 jj + 8 (i / 4) + 4 lg + (i % 4).
   auto vector_phase = [&](int j, int vs2, int ks3) __attribute__((always_inline)) {
-    if (grp == 0) tile_dma(v_rsrc, v_lds[vs2], j + 2);
-    else tile_dma(k_rsrc, k_lds[ks3], j + 3);
+    if (grp == 0) tile_dma(v_rsrc, RA_LDS_ADDR(v_lds) + (unsigned)(vs2 * TILE_BYTES), j + 2);
+    else tile_dma(k_rsrc, RA_LDS_ADDR(k_lds) + (unsigned)(ks3 * TILE_BYTES), j + 3);
     if (j >= wave_tiles || j < wave_first) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) ds[c] = bf16x8{};
@@ -810,11 +810,11 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
     for (int i = tid; i < TILE_BYTES / 16; i += DQ_THREADS) z[i] = u32x4{};
   }
   if (grp == 1) {
-    tile_dma(k_rsrc, k_lds[0], j_begin);
-    tile_dma(k_rsrc, k_lds[1], j_begin + 1);
+    tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[0]), j_begin);
+    tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[1]), j_begin + 1);
   } else {
-    tile_dma(v_rsrc, v_lds[0], j_begin);
-    tile_dma(v_rsrc, v_lds[1], j_begin + 1);
+    tile_dma(v_rsrc, RA_LDS_ADDR(v_lds[0]), j_begin);
+    tile_dma(v_rsrc, RA_LDS_ADDR(v_lds[1]), j_begin + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   // the stage of V(j-1) and has it by the end of 2j+4; group 1 loads K(j+3) in 2j+3 into the
   // stage of K(j-1) and has it by the end of 2j+5.
   if (grp == 1) {
-    tile_dma(k_rsrc, k_lds[2], j_begin + 2);
+    tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[2]), j_begin + 2);
     barrier_no_fence();
   }
   int ks = 0, vs = 0;                     // stages of tile j: counted from j_begin

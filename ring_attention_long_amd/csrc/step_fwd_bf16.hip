@@ -206,7 +206,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const unsigned lrow = lane >> 4;                       // row within a 1 KB load
   const unsigned k_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ ((4 * ws + lrow) & 15)) * 16;
   const unsigned v_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow)) * 16;
-  auto issue_tile_dma = [&](dma_rsrc rsrc, char* dst, unsigned off, int j) {
+  auto issue_tile_dma = [&](dma_rsrc rsrc, unsigned dst, unsigned off, int j) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = ws + 4 * t;
@@ -223,11 +223,11 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // again, so every phase issues exactly two loads and the waits can count them.
   const dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
   const unsigned my_dma_off = group ? k_dma_off : v_dma_off;
-  char* const my_lds = group ? &k_lds[0][0] : &v_lds[0][0];
+  const unsigned my_lds = group ? RA_LDS_ADDR(k_lds) : RA_LDS_ADDR(v_lds);
   auto issue_one = [&](int tile, int stage, int t) {
     const int i = ws + 4 * t;
     const unsigned soff = tile < n_tiles ? (unsigned)(tile * BN + 4 * i) * row_stride : 0x80000000u;
-    dma16_to_lds(my_rsrc, my_lds + stage * TILE_BYTES + 1024 * i, my_dma_off, soff);
+    dma16_to_lds(my_rsrc, my_lds + (unsigned)(stage * TILE_BYTES + 1024 * i), my_dma_off, soff);
   };
 
   // ---- the two phases of one wave ------------------------------------------------------
@@ -408,15 +408,15 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
   }
   if (group == 1) {
-    issue_tile_dma(k_rsrc, k_lds[0], k_dma_off, j_begin);   // rows past L arrive as zeros
-    issue_tile_dma(k_rsrc, k_lds[1], k_dma_off, j_begin + 1);
+    issue_tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[0]), k_dma_off, j_begin);   // rows past L arrive as zeros
+    issue_tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[1]), k_dma_off, j_begin + 1);
   } else {
-    issue_tile_dma(v_rsrc, v_lds[0], v_dma_off, j_begin);
+    issue_tile_dma(v_rsrc, RA_LDS_ADDR(v_lds[0]), v_dma_off, j_begin);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q, K(0), K(1), V(0) are in place
   __syncthreads();
   if (group == 1) {
-    issue_tile_dma(k_rsrc, k_lds[2], k_dma_off, j_begin + 2);
+    issue_tile_dma(k_rsrc, RA_LDS_ADDR(k_lds[2]), k_dma_off, j_begin + 2);
     barrier_no_fence();
   }
   auto step = [&](int j, auto stage_c) __attribute__((always_inline)) {
