@@ -123,10 +123,29 @@ ra_status ra_merge_lse(const ra_problem* p, float* o_acc, float* lse_acc, const 
  * ------------------------------------------------------------------------------------- */
 ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_stream stream);
 
-/* Bytes of device workspace ra_ring_fwd needs: two KV staging buffers (the double buffer of
- * page 1, "Practical Implementation Patterns") plus, unless dtype is fp32, an fp32 output
- * accumulator.  Returns 0 if p is invalid. */
+/* Bytes of device workspace for ra_ring_fwd: two KV staging buffers (the double buffer of
+ * page 1, "Practical Implementation Patterns"); unless dtype is fp32, an fp32 output
+ * accumulator [b][L][h][d]; and, for bf16 without packed documents and L <= 4096, a second
+ * fp32 accumulator [b][L][h][d] with its LSE [b][h][L] (each part 256-byte aligned).  With
+ * the second accumulator the steps of short shards may run the key range of a heavy query
+ * block as two workgroups, one merging into each accumulator, and the pass folds the two
+ * together at the end (page 2, "FlashAttention Integration": partials over disjoint key
+ * sets merge by their LSE); this evens out the causal imbalance between query blocks and
+ * fills the chip when a step has few blocks.  A workspace without the second accumulator is
+ * accepted too: the pass then runs every block whole (the same result up to the order of
+ * the fp32 sums).  Returns 0 if p is invalid. */
 size_t ra_ring_fwd_workspace(const ra_problem* p);
+
+/* ra_fwd_step_plan — how one bf16 forward step of a pass with the second accumulator
+ * distributes its query blocks over workgroups (inspection and tests; no GPU call).  Query
+ * block i holds rows [i R, (i+1) R) (R = *block_rows) of the query heads of one KV head that
+ * one workgroup runs; work item j (launch order; each item runs once per KV head and batch
+ * row) is block[j] whole (part[j] = -1) or the first (0) or second (1) half of its key tiles.
+ * Items are ordered by decreasing work.  n_cu: compute units to plan for.  Writes up to
+ * max_items entries of block and part and the item count to *n_items.  RA_ERR_UNSUPPORTED
+ * unless dtype is bf16. */
+ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shard, int32_t n_cu, int32_t* block,
+                           int32_t* part, int32_t max_items, int32_t* n_items, int32_t* block_rows);
 
 /* ---------------------------------------------------------------------------------------
  * ra_ring_fwd — the whole forward ring pass of device q_shard.
@@ -139,7 +158,8 @@ size_t ra_ring_fwd_workspace(const ra_problem* p);
  * shard in place.  Steps whose KV shard is entirely in the causal future are skipped
  * (their copy still runs).  `copy` may be NULL or equal to `compute` (copies then run in
  * order on `compute`).  All work has finished when work queued on `compute` after this
- * call runs.  ws must hold ra_ring_fwd_workspace(p) bytes.
+ * call runs.  ws must hold ra_ring_fwd_workspace(p) bytes, or those less the second
+ * accumulator (see there).
  * ------------------------------------------------------------------------------------- */
 ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
                       const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
@@ -176,9 +196,11 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
  * library's load until the process ends; the first call on a device looks up the array's
  * address and creates the pass's events (no device memory is allocated then or later).
  * Errors: as ra_ring_fwd, and RA_ERR_WORKSPACE (nothing enqueued) when
- * ra_ring_fwd_workspace(p) exceeds RA_NOALLOC_SCRATCH_BYTES (for bf16 that is
- * 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32, n_kv = 8, d = 128
- * fits).  Every call on one device shares that device's array and events, and the array
+ * ra_ring_fwd_workspace(p) without its second accumulator exceeds RA_NOALLOC_SCRATCH_BYTES
+ * (for bf16 that is 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32,
+ * n_kv = 8, d = 128 fits); the second accumulator is used when it fits as well (L = 2048 with
+ * h = 16, n_kv = 8), and the results equal ra_ring_fwd's with a workspace of
+ * RA_NOALLOC_SCRATCH_BYTES.  Every call on one device shares that device's array and events, and the array
  * keeps the last call's contents (each pass overwrites everything it reads, so nothing
  * needs clearing): calls whose work overlaps on one device (different streams, or threads
  * not ordered by the caller) race and give wrong results, so order them, e.g. on one stream.
@@ -267,8 +289,9 @@ ra_status ra_ring_bwd_kv_stationary(const ra_problem* p, int32_t kv_shard, const
  * group fills the whole outputs, which equal ra_ring_fwd's for every shard.  The
  * exchanges are copy kernels on `stream` (gather, then attention, then scatter).
  * Workspace: ra_ulysses_fwd_workspace(p) bytes (the gathered Q, K, V of the head group, an
- * fp32 output and the LSE of the whole sequence), 16-byte aligned; 0 if p is invalid for
- * this path.  RA_ERR_INVALID_ARG if h or n_kv is not a multiple of N; RA_ERR_UNSUPPORTED
+ * fp32 output and the LSE of the whole sequence, and the second accumulator of
+ * ra_ring_fwd_workspace when the whole-sequence problem keeps one; without it the attention
+ * runs unsplit), 16-byte aligned; 0 if p is invalid for this path.  RA_ERR_INVALID_ARG if h or n_kv is not a multiple of N; RA_ERR_UNSUPPORTED
  * with packed documents or where the whole-sequence problem (b, N L, h/N, n_kv/N, d) has
  * no kernel. */
 size_t ra_ulysses_fwd_workspace(const ra_problem* p);
@@ -325,7 +348,9 @@ ra_status ra_ulysses_bwd(const ra_problem* p, int32_t head_group, const void* q_
  * exchanges (what the other devices of head group g gather for themselves, and the ring hands
  * over) run first in the same call.  Workspace: ra_usp_fwd_workspace(p, n_head_groups)
  * bytes (the gathered Q of the ring shard, K and V of every ring shard for the head group, an
- * fp32 output, the LSE and the ring's staging buffers), 0 if invalid for this path.  No
+ * fp32 output, the LSE, the ring's staging buffers and the second accumulator of
+ * ra_ring_fwd_workspace when the ring problem keeps one; without it the ring runs unsplit),
+ * 0 if invalid for this path.  No
  * packed documents (RA_ERR_UNSUPPORTED).  ra_usp_fwd_timed also reports the parts' times
  * (HIP events on `compute`, ms) and waits for the call to finish. */
 typedef struct ra_usp_timing {

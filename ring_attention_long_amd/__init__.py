@@ -183,6 +183,20 @@ def ring_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=N
     return int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
 
 
+def fwd_step_plan(*, b, L, h, n_kv, d=128, N, q_shard, kv_shard, causal=False, layout="contiguous", n_cu=256):
+    """Work items of one bf16 forward ring step with the second accumulator (ra_fwd_step_plan):
+    returns ([(block, part), ...] in launch order, rows per block); part -1 = whole block."""
+    p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout, dtype=torch.bfloat16)
+    cap = 256
+    block = (ctypes.c_int32 * cap)()
+    part = (ctypes.c_int32 * cap)()
+    n = ctypes.c_int32(0)
+    rows = ctypes.c_int32(0)
+    check(_lib.lib().ra_fwd_step_plan(ctypes.byref(p), q_shard, kv_shard, n_cu, block, part, cap, ctypes.byref(n),
+                                      ctypes.byref(rows)), "ra_fwd_step_plan")
+    return [(block[i], part[i]) for i in range(min(n.value, cap))], rows.value
+
+
 def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, docs=None):
     N, b, L, n_kv, d = k_all.shape
     h = q.shape[2]

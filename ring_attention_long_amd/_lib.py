@@ -62,6 +62,8 @@ SIGNATURES = [
     ("ra_merge_lse", _I, [_P, _V, _V, _V, _V, _V]),
     ("ra_finalize", _I, [_P, _V, _V, _V]),
     ("ra_ring_fwd_workspace", _S, [_P]),
+    ("ra_fwd_step_plan", _I, [_P, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), _I, ctypes.POINTER(_I),
+                              ctypes.POINTER(_I)]),
     ("ra_ring_fwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_ring_fwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _S, _V, _V,
                                ctypes.POINTER(RaRingTiming)]),

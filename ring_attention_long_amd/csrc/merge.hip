@@ -1,5 +1,6 @@
-// Bandwidth-bound kernels around the ring: the (O, LSE) merge of two partial results and
-// the final cast of the fp32 accumulator to the output type.
+// Bandwidth-bound kernels around the ring: the (O, LSE) merge of two partial results, the
+// final cast of the fp32 accumulator to the output type, and the fold of a pass's second
+// accumulator (the split key ranges of short shards) into the first.
 //
 // Merge (page 2, "FlashAttention Integration"; page 3, section 3): the two partials are
 // normalised outputs over disjoint key sets with denominators exp(lse_acc) and
@@ -67,6 +68,53 @@ __global__ __launch_bounds__(256) void finalize_bf16_kernel(const float* __restr
   ((u32x4*)dst)[i] = __builtin_bit_cast(u32x4, r);
 }
 
+// Fold of a forward pass's second accumulator (see launch_fold_second): one thread per 8
+// consecutive floats of a row, the d/8 threads of a row in one wave (every lane reads the
+// row's LSE before the lane holding the row's first columns overwrites it).
+template <bool TO_BF16>
+__global__ __launch_bounds__(256) void fold_second_kernel(float* __restrict__ o, float* __restrict__ lse,
+                                                          const float* __restrict__ o2,
+                                                          const float* __restrict__ lse2,
+                                                          __bf16* __restrict__ out, int L, int h, int d8,
+                                                          int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t row = i / d8;                 // row = (bi * L + t) * h + hq
+  const int col8 = (int)(i - row * d8);
+  const int hq = (int)(row % h);
+  const int64_t bt = row / h;
+  const int t = (int)(bt % L);
+  const int64_t bi = bt / L;
+  const int64_t li = (bi * h + hq) * L + t;
+  const float l2 = lse2[li];
+  f32x4 a = ((const f32x4*)o)[2 * i];
+  f32x4 b = ((const f32x4*)o)[2 * i + 1];
+  if (l2 > -INFINITY) {                       // otherwise o2's row is undefined and not read
+    const MergeWeights m = merge_weights(lse[li], l2);
+    const f32x4 c = ((const f32x4*)o2)[2 * i];
+    const f32x4 e = ((const f32x4*)o2)[2 * i + 1];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      a[x] = merge_value(m, a[x], c[x]);
+      b[x] = merge_value(m, b[x], e[x]);
+    }
+    if (!TO_BF16) {
+      ((f32x4*)o)[2 * i] = a;
+      ((f32x4*)o)[2 * i + 1] = b;
+    }
+    if (col8 == 0) lse[li] = m.lse;
+  }
+  if (TO_BF16) {
+    __bf16 r[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      r[x] = (__bf16)a[x];       // round to nearest even
+      r[4 + x] = (__bf16)b[x];
+    }
+    ((u32x4*)out)[i] = __builtin_bit_cast(u32x4, r);
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src,
                                                        float* __restrict__ dst, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -101,6 +149,20 @@ hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n, hi
     hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(n / 4)), dim3(256), 0, s, o_acc,
                        (float*)o, n / 4);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_second(float* o, float* lse, const float* o2, const float* lse2, void* out, int b, int L,
+                              int h, int d, hipStream_t s) {
+  const int64_t n8 = (int64_t)b * L * h * d / 8;
+  if (n8 == 0) return hipSuccess;
+  if (d % 8) return hipErrorInvalidValue;
+  if (out)
+    hipLaunchKernelGGL(fold_second_kernel<true>, dim3(blocks_for(n8)), dim3(256), 0, s, o, lse, o2, lse2,
+                       (__bf16*)out, L, h, d / 8, n8);
+  else
+    hipLaunchKernelGGL(fold_second_kernel<false>, dim3(blocks_for(n8)), dim3(256), 0, s, o, lse, o2, lse2,
+                       (__bf16*)nullptr, L, h, d / 8, n8);
   return hipGetLastError();
 }
 

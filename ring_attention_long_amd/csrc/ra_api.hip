@@ -184,6 +184,26 @@ size_t staging_bytes(const ra_problem* p) {
   return 4 * align_up((size_t)p->b * p->L * p->n_kv * p->d * elem_size(p), 256);
 }
 
+// A forward pass keeps a second accumulator (bf16 path, short shards, no packed documents),
+// so that its steps may split the key ranges of their heaviest query blocks over two
+// workgroups (see plan_split).  Its bytes: fp32 [b][L][h][d] and LSE [b][h][L].
+bool fwd_split(const ra_problem* p) {
+  return p->dtype == RA_BF16 && !p->doc_begin && p->L <= ra::kSplitMaxL;
+}
+size_t second_o_bytes(const ra_problem* p) { return align_up((size_t)p->b * p->L * p->h * p->d * 4, 256); }
+size_t second_lse_bytes(const ra_problem* p) { return align_up((size_t)p->b * p->h * p->L * 4, 256); }
+size_t second_acc_bytes(const ra_problem* p) {
+  return fwd_split(p) ? second_o_bytes(p) + second_lse_bytes(p) : 0;
+}
+// ra_ring_fwd's workspace without the second accumulator: the KV double buffer and (not for
+// fp32) the fp32 accumulator.
+size_t ring_fwd_base_workspace(const ra_problem* p) {
+  const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
+  size_t n = 4 * align_up(shard_bytes, 256);
+  if (p->dtype != RA_F32) n += align_up((size_t)p->b * p->L * p->h * p->d * 4, 256);
+  return n;
+}
+
 // Events of one forward pass made ahead of time (the allocation-free entry point keeps one
 // set per device); without one, ring_fwd_impl creates its own for the call.
 struct RingEvents {
@@ -195,9 +215,11 @@ struct RingEvents {
 ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                         const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
                         ra_stream compute, ra_stream copy, ra_ring_timing* tm,
-                        const RingEvents* pre = nullptr, float* o_acc_ext = nullptr) {
+                        const RingEvents* pre = nullptr, float* o_acc_ext = nullptr, float* o2_ext = nullptr,
+                        float* lse2_ext = nullptr) {
   // o_acc_ext: leave the merged fp32 result there (no cast to p->dtype, o unused) and use
-  // the workspace for the staging buffers only.
+  // the workspace for the staging buffers only; the second accumulator (when the problem
+  // keeps one) is then (o2_ext, lse2_ext).
   RA_TRY(check_problem(p));
   RA_TRY(check_shard(p, qs, "q_shard"));
   RA_TRY(check_ptr(q, "q", 16));
@@ -206,9 +228,22 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   if (!o_acc_ext) RA_TRY(check_ptr(o, "o", 16));
   RA_TRY(check_ptr(lse, "lse", 4));
   RA_TRY(check_ptr(ws, "ws", 16));
-  const size_t need = o_acc_ext ? staging_bytes(p) : ra_ring_fwd_workspace(p);
+  const size_t need = o_acc_ext ? staging_bytes(p) : ring_fwd_base_workspace(p);
   if (ws_bytes < need)
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  // the second accumulator: the caller's (o_acc_ext), or after the rest when the workspace
+  // has room for it
+  bool second = fwd_split(p) && (o_acc_ext ? (o2_ext && lse2_ext) : ws_bytes >= need + second_acc_bytes(p));
+  if (second) {   // ... and only if some step splits a query block (else the plain finalize)
+    bool any_split = false;
+    for (int k = 0; k < p->N && !any_split; ++k) {
+      const int src = ((qs - k) % p->N + p->N) % p->N;
+      if (!step_is_live(p, qs, src)) continue;
+      const ra::StepArgs a = step_args(p, qs, src, nullptr, nullptr, nullptr, nullptr, nullptr);
+      any_split = ra::step_splits_bf16(a);
+    }
+    second = any_split;
+  }
   const int N = p->N;
   if (tm && N > RA_MAX_TIMED_STEPS)
     return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
@@ -221,6 +256,17 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   char* vbuf[2] = {wsc + A, wsc + 3 * A};
   float* o_acc = o_acc_ext ? o_acc_ext : p->dtype == RA_F32 ? (float*)o : (float*)(wsc + 4 * A);
   float* lse_acc = lse;
+  float* o2 = nullptr;
+  float* lse2 = nullptr;
+  if (second) {
+    if (o_acc_ext) {
+      o2 = o2_ext;
+      lse2 = lse2_ext;
+    } else {   // after the staging buffers and the (bf16 path) accumulator
+      o2 = (float*)(wsc + 4 * A + align_up((size_t)p->b * p->L * p->h * p->d * 4, 256));
+      lse2 = (float*)((char*)o2 + second_o_bytes(p));
+    }
+  }
   const hipStream_t cs = (hipStream_t)compute;
   const hipStream_t ps = copy ? (hipStream_t)copy : cs;
   const bool split = ps != cs;
@@ -290,7 +336,9 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     live[k] = step_is_live(p, qs, src);
     if (live[k]) {
       if (timing && (e = hipEventRecord(t_sb[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, o_acc, lse_acc);
+      ra::StepArgs a = step_args(p, qs, src, q, kp, vp, o_acc, lse_acc);
+      a.o2 = o2;
+      a.lse2 = lse2;
       if ((e = launch_step(p, a, have_acc ? ra::MODE_MERGE : ra::MODE_PART, cs)) != hipSuccess)
         return hip_fail(e, "step kernel launch");
       have_acc = true;
@@ -309,8 +357,14 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     if ((e = ra::launch_fill_lse(lse_acc, (int64_t)p->b * p->h * p->L, -INFINITY, cs)) != hipSuccess)
       return hip_fail(e, "fill kernel launch");
   }
-  if (!o_acc_ext && p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess)
+  if (second && have_acc) {
+    // fold the second accumulator in: into the bf16 output, or in place for o_acc_ext
+    if ((e = ra::launch_fold_second(o_acc, lse_acc, o2, lse2, o_acc_ext ? nullptr : o, p->b, p->L, p->h, p->d,
+                                    cs)) != hipSuccess)
+      return hip_fail(e, "fold kernel launch");
+  } else if (!o_acc_ext && p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess) {
     return hip_fail(e, "finalize kernel launch");
+  }
 
   if (timing) {
     hipEvent_t done;
@@ -362,7 +416,7 @@ ra_problem ulysses_local(const ra_problem* p) {
 }
 
 struct UlyssesWs {
-  size_t q, kv, o, lse, total;
+  size_t q, kv, o, lse, second, total;
 };
 UlyssesWs ulysses_ws(const ra_problem* p) {
   const size_t S = (size_t)p->N * p->L, es = elem_size(p);
@@ -371,7 +425,9 @@ UlyssesWs ulysses_ws(const ra_problem* p) {
   w.kv = align_up((size_t)p->b * S * (p->n_kv / p->N) * p->d * es, 256);
   w.o = align_up((size_t)p->b * S * (p->h / p->N) * p->d * 4, 256);
   w.lse = align_up((size_t)p->b * (p->h / p->N) * S * 4, 256);
-  w.total = w.q + 2 * w.kv + w.o + w.lse;
+  const ra_problem lp = ulysses_local(p);
+  w.second = second_acc_bytes(&lp);
+  w.total = w.q + 2 * w.kv + w.o + w.lse + w.second;
   return w;
 }
 
@@ -389,8 +445,11 @@ ra_status ulysses_fwd_impl(const ra_problem* p, int32_t group, const void* q_all
   RA_TRY(check_ptr(lse_all, "lse_all", 4));
   RA_TRY(check_ptr(ws, "ws", 16));
   const UlyssesWs w = ulysses_ws(p);
-  if (ws_bytes < w.total)
-    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+  if (ws_bytes < w.total - w.second)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total - w.second);
+  // room for the second accumulator, and a query block that the step splits
+  const bool second = w.second && ws_bytes >= w.total &&
+                      ra::step_splits_bf16(step_args(&lp, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr));
 
   char* base = (char*)ws;
   void* q_g = base;
@@ -418,8 +477,15 @@ ra_status ulysses_fwd_impl(const ra_problem* p, int32_t group, const void* q_all
           hipSuccess)
     return hip_fail(e, "gather kernel launch");
   if (tm && (e = hipEventRecord(t1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  const ra::StepArgs a = step_args(&lp, 0, 0, q_g, k_g, v_g, o_g, lse_g);
+  ra::StepArgs a = step_args(&lp, 0, 0, q_g, k_g, v_g, o_g, lse_g);
+  if (second) {
+    a.o2 = (float*)(base + w.q + 2 * w.kv + w.o + w.lse);
+    a.lse2 = (float*)((char*)a.o2 + second_o_bytes(&lp));
+  }
   if ((e = launch_step(&lp, a, ra::MODE_PART, s)) != hipSuccess) return hip_fail(e, "step kernel launch");
+  if (second && (e = ra::launch_fold_second(o_g, lse_g, a.o2, a.lse2, nullptr, lp.b, lp.L, lp.h, lp.d, s)) !=
+                      hipSuccess)
+    return hip_fail(e, "fold kernel launch");
   if (tm && (e = hipEventRecord(t2, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if ((e = ra::launch_ulysses_scatter(o_all, lse_all, o_g, lse_g, p->b, p->L, p->N, p->layout, p->h, Hg, group * Hg,
                                       p->d, p->dtype, s)) != hipSuccess)
@@ -471,7 +537,7 @@ ra_problem usp_ring_problem(const ra_problem* p, int32_t n_hg) {
 }
 
 struct UspWs {
-  size_t q, kv, o, lse, staging, total;
+  size_t q, kv, o, lse, staging, second, total;
 };
 UspWs usp_ws(const ra_problem* rp) {
   const size_t es = elem_size(rp);
@@ -481,7 +547,8 @@ UspWs usp_ws(const ra_problem* rp) {
   w.o = align_up((size_t)rp->b * rp->L * rp->h * rp->d * 4, 256);
   w.lse = align_up((size_t)rp->b * rp->h * rp->L * 4, 256);
   w.staging = staging_bytes(rp);
-  w.total = w.q + 2 * w.kv + w.o + w.lse + w.staging;
+  w.second = second_acc_bytes(rp);
+  w.total = w.q + 2 * w.kv + w.o + w.lse + w.staging + w.second;
   return w;
 }
 
@@ -500,7 +567,9 @@ ra_status usp_fwd_impl(const ra_problem* p, int32_t n_hg, int32_t g, int32_t r, 
   RA_TRY(check_ptr(lse_all, "lse_all", 4));
   RA_TRY(check_ptr(ws, "ws", 16));
   const UspWs w = usp_ws(&rp);
-  if (ws_bytes < w.total) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+  if (ws_bytes < w.total - w.second)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total - w.second);
+  const bool second = w.second && ws_bytes >= w.total;   // room for the second accumulator
   if (rp.N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N_s=%d above %d", rp.N, kMaxRing);
 
   char* base = (char*)ws;
@@ -546,8 +615,10 @@ ra_status usp_fwd_impl(const ra_problem* p, int32_t n_hg, int32_t g, int32_t r, 
     return hip_fail(e, "gather kernel launch");
   if (tm && (e = hipEventRecord(t2, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   // The ring over the N_s ring shards, the merged fp32 result left in o_g.
+  float* o2 = second ? (float*)(staging + w.staging) : nullptr;
+  float* lse2 = second ? (float*)((char*)o2 + second_o_bytes(&rp)) : nullptr;
   RA_TRY(ring_fwd_impl(&rp, r, q_g, k_ring, v_ring, nullptr, lse_g, staging, w.staging, compute, copy, nullptr,
-                       nullptr, o_g));
+                       nullptr, o_g, o2, lse2));
   if (tm && (e = hipEventRecord(t3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   // Second exchange: rows [g' L, (g'+1) L) of the ring shard go back to device r N_h + g'.
   if ((e = ra::launch_ulysses_scatter((char*)o_all + (size_t)r * n_hg * dev_q,
@@ -845,12 +916,35 @@ ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_strea
   return e == hipSuccess ? RA_OK : hip_fail(e, "finalize kernel launch");
 }
 
+ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shard, int32_t n_cu, int32_t* block,
+                           int32_t* part, int32_t max_items, int32_t* n_items, int32_t* block_rows) {
+  RA_TRY(check_problem(p));
+  RA_TRY(check_shard(p, q_shard, "q_shard"));
+  RA_TRY(check_shard(p, kv_shard, "kv_shard"));
+  if (!n_items || !block_rows || (max_items > 0 && (!block || !part)))
+    return fail(RA_ERR_INVALID_ARG, "output pointer is NULL");
+  if (p->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the step plan describes the bf16 kernel");
+  if (n_cu < 1) return fail(RA_ERR_INVALID_ARG, "n_cu=%d must be positive", n_cu);
+  const ra::StepArgs a = step_args(p, q_shard, kv_shard, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const ra::StepGeometry g = ra::step_geometry_bf16(a);
+  ra::SplitPlan pl{};
+  pl.split_from = g.n_qb;
+  if (fwd_split(p)) pl = ra::plan_split(a, g, n_cu);
+  const int n = pl.split_from + 2 * (g.n_qb - pl.split_from);
+  *n_items = n;
+  *block_rows = g.rows_wg;
+  for (int i = 0; i < n && i < max_items; ++i) {
+    int qb, pt;
+    ra::split_item(pl, g.n_qb, i, qb, pt);
+    block[i] = qb;
+    part[i] = qb >= pl.split_from ? pt : -1;
+  }
+  return RA_OK;
+}
+
 size_t ra_ring_fwd_workspace(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
-  const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
-  size_t n = 4 * align_up(shard_bytes, 256);
-  if (p->dtype != RA_F32) n += align_up((size_t)p->b * p->L * p->h * p->d * 4, 256);
-  return n;
+  return ring_fwd_base_workspace(p) + second_acc_bytes(p);
 }
 
 ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,
@@ -875,7 +969,7 @@ ra_status ra_ring_fwd_noalloc(const ra_problem* p, int32_t q_shard, const void* 
   RA_TRY(check_ptr(v_all, "v_all", 16));
   RA_TRY(check_ptr(o, "o", 16));
   RA_TRY(check_ptr(lse, "lse", 4));
-  const size_t need = ra_ring_fwd_workspace(p);
+  const size_t need = ring_fwd_base_workspace(p);   // with the second accumulator only if it fits too
   if (need > RA_NOALLOC_SCRATCH_BYTES)
     return fail(RA_ERR_WORKSPACE, "this problem needs %zu bytes of scratch; the allocation-free entry point holds %zu",
                 need, (size_t)RA_NOALLOC_SCRATCH_BYTES);

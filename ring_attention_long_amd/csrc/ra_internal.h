@@ -216,6 +216,14 @@ struct StepArgs {
   float scale;         // softmax scale on q.k
   const int32_t* doc_begin;   // [b][L] packed-document bounds of each query row, or null
   const int32_t* doc_end;
+  // Second accumulator of a forward pass, [b][L][h][d] and [b][h][L] fp32 (bf16 step kernel
+  // only; null: none).  With it the step kernel may run the key range of its heaviest query
+  // blocks as two work items, the second one writing (MODE_PART) or merging (MODE_MERGE) its
+  // partial here; MODE_PART also sets lse2 to -inf on every row no second item covers, so
+  // after the first step of a pass every row of (o2, lse2) is a valid partial or empty.
+  // Rows with lse2 = -inf may hold anything in o2.
+  float* o2 = nullptr;
+  float* lse2 = nullptr;
 };
 
 hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t s);
@@ -225,6 +233,80 @@ hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
 hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n_elems,
                            hipStream_t s);
 hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s);
+// Fold the second accumulator (o2, lse2) of a forward pass into (o, lse), row by row (rows
+// with lse2 = -inf keep (o, lse) and never read o2).  With out null, o is updated in place in
+// fp32; otherwise the folded rows (and the untouched ones) are written to out in bf16 and o is
+// only read.  lse is updated in place either way.
+hipError_t launch_fold_second(float* o, float* lse, const float* o2, const float* lse2, void* out, int b, int L,
+                              int h, int d, hipStream_t s);
+
+// Work items of a bf16 forward step whose heaviest query blocks are split over two
+// workgroups: blocks [split_from, n_qb) run as two items each, part 0 on the first half of
+// the block's key tiles (rounded up) and part 1 on the rest.  Item i (launch order) is an
+// unsplit block when bit i of `order` is set: the k-th such item is block split_from - 1 - k;
+// otherwise the m-th part item is part m % 2 of block n_qb - 1 - m / 2.  Any bit pattern with
+// split_from ones among the first split_from + 2 (n_qb - split_from) bits maps the items one
+// to one onto the (block, part) pairs; the host picks one that launches the heaviest first.
+// With split_from = n_qb nothing is split and item i is block n_qb - 1 - i.
+struct SplitPlan {
+  uint32_t order[4];   // up to 128 items
+  int split_from;
+};
+constexpr int kSplitMaxBlocks = 64;
+__host__ __device__ inline void split_item(const SplitPlan& pl, int n_qb, int item, int& qb, int& part) {
+  part = 0;
+  if (pl.split_from >= n_qb) {
+    qb = n_qb - 1 - item;
+    return;
+  }
+  const int word = item >> 5;
+  const uint32_t w = word == 0 ? pl.order[0] : word == 1 ? pl.order[1] : word == 2 ? pl.order[2] : pl.order[3];
+  int before = __builtin_popcount(w & ((1u << (item & 31)) - 1u));
+  if (word > 0) before += __builtin_popcount(pl.order[0]);
+  if (word > 1) before += __builtin_popcount(pl.order[1]);
+  if (word > 2) before += __builtin_popcount(pl.order[2]);
+  if ((w >> (item & 31)) & 1u) {
+    qb = pl.split_from - 1 - before;
+  } else {
+    const int m = item - before;
+    qb = n_qb - 1 - (m >> 1);
+    part = m & 1;
+  }
+}
+// The plan of one step (host), for a pass with a second accumulator: geometry as
+// launch_step_bf16 uses it, n_cu compute units.
+struct StepGeometry {
+  int Hw, PB, n_qb, inner, rows_wg;
+};
+StepGeometry step_geometry_bf16(const StepArgs& a);
+SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu);
+// Whether launch_step_bf16 would split any query block of this step (given a second
+// accumulator) on the current device.
+bool step_splits_bf16(const StepArgs& a);
+
+// Largest shard length for which a forward pass keeps a second accumulator, so that its steps
+// can split the key ranges of their heaviest query blocks (below it a step has too few
+// workgroups to fill the chip, or the causal imbalance between query blocks is not evened
+// out by running several blocks per compute unit).
+constexpr int kSplitMaxL = 4096;
+
+// (O, LSE) of two partials over disjoint key sets, merged (page 2, "FlashAttention
+// Integration": each partial is rescaled by its share of the combined denominator).  One
+// definition for every kernel that merges a second accumulator, so that all paths round the
+// same way: explicit FMA, no contraction left to the compiler.
+struct MergeWeights {
+  float f1, f2, lse;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float l1, float l2) {
+  const float M = fmaxf(l1, l2);
+  const float w1 = __builtin_amdgcn_exp2f((l1 - M) * 1.4426950408889634f);
+  const float w2 = __builtin_amdgcn_exp2f((l2 - M) * 1.4426950408889634f);
+  const float tot = w1 + w2;
+  return MergeWeights{w1 / tot, w2 / tot, M + __logf(tot)};
+}
+__device__ __forceinline__ float merge_value(const MergeWeights& m, float o1, float o2) {
+  return __builtin_fmaf(m.f1, o1, m.f2 * o2);
+}
 // Head-group exchange of the all-to-all sequence-parallel scheme, one device's side.
 // Gather: rows [b][S][Hg][d] (element bytes es) of heads head0 .. head0+Hg-1, in global
 // position order, from the N shards src_all [N][b][L][H][d] in their own layout order.

@@ -52,6 +52,9 @@
 //    position), with the KV head as the fastest-varying index so that neighbouring
 //    workgroups, dispatched round-robin over the 8 XCDs, put each KV head's tiles into
 //    one XCD's L2.
+#include <atomic>
+#include <type_traits>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -102,7 +105,7 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 template <int MODE>
 __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, int heads_per_wg,
-                                                                  int n_qb, int inner_count) {
+                                                                  int n_qb, int inner_count, SplitPlan plan) {
   __shared__ __attribute__((aligned(1024))) char k_lds[3][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds[3][TILE_BYTES];
 
@@ -118,7 +121,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const int Hw = heads_per_wg;          // heads per workgroup (4, 2 or 1)
   const int PB = WAVES / Hw;            // 32-row query blocks per workgroup
   const int inner = blockIdx.x % inner_count;
-  const int qb = n_qb - 1 - blockIdx.x / inner_count;   // heaviest query block first
+  const int item = blockIdx.x / inner_count;
+  int qb, part;                         // heaviest query block first
+  split_item(plan, n_qb, item, qb, part);
+  const bool split_blk = qb >= plan.split_from;
   const int g = inner % a.n_kv;
   const int bi = (inner / a.n_kv) % a.b;
   const int hs = inner / (a.n_kv * a.b);
@@ -167,8 +173,20 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   }
   j_begin = __builtin_amdgcn_readfirstlane(j_begin);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+  if (split_blk) {                      // this item's half of the block's key tiles
+    const int j_mid = j_begin + (n_tiles - j_begin + 1) / 2;
+    if (part == 0) n_tiles = j_mid;
+    else j_begin = j_mid;
+    wave_first = max(wave_first, j_begin);
+    wave_tiles = min(wave_tiles, n_tiles);
+  }
   // no row of the workgroup sees a key of this shard: merging would leave (O, LSE) as it is
   if (MODE == MODE_MERGE && n_tiles <= j_begin) return;
+  // the accumulator this item writes, and (first step only) the second accumulator's LSE
+  // where no second item covers the rows: chosen here, so only these stay live in the loop
+  float* const o_dst = part ? a.o2 : a.o;
+  float* const l_dst = part ? a.lse2 : a.lse;
+  float* const l2_empty = (MODE == MODE_PART && !split_blk) ? a.lse2 : nullptr;
 
   // ---- Q^T operand, resident for the whole kernel -------------------------------------
   // Rows past the shard end read row L-1 instead: they are never stored, and their key
@@ -448,9 +466,13 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const bool any = l_tot > 0.f;
   const float lse_new = any ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
   const float inv = any ? 1.f / l_tot : 0.f;
-  float* orow = a.o + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
-  float* lse_p = a.lse + ((int64_t)bi * a.h + hq) * L + t;
+  const int64_t lse_idx = ((int64_t)bi * a.h + hq) * L + t;
+  float* orow = o_dst + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
+  float* lse_p = l_dst + lse_idx;
   if (MODE == MODE_PART) {
+    // rows of an unsplit block have no second partial in this step: mark it empty (a later
+    // step may split the block and merge into it)
+    if (l2_empty && lg == 0) l2_empty[lse_idx] = -INFINITY;
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
 #pragma unroll
@@ -468,37 +490,138 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     const float wb = __builtin_amdgcn_exp2f((lse_new - M) * LOG2E);
     const float tot = wa + wb;
     const float fa = wa / tot, fb = wb * inv / tot;
+    auto merge_rows = [&](auto may_be_empty) __attribute__((always_inline)) {
+      // an empty row of the second accumulator is not read: its O is undefined
+      const bool have_old = !decltype(may_be_empty)::value || lse_old > -INFINITY;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+      for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        f32x4* dst = (f32x4*)(orow + 32 * e + 8 * ib);
-        const f32x4 old = *dst;
-        f32x4 v;
+        for (int ib = 0; ib < 4; ++ib) {
+          f32x4* dst = (f32x4*)(orow + 32 * e + 8 * ib);
+          const f32x4 old = have_old ? *dst : f32x4{};
+          f32x4 v;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = fa * old[x] + fb * acc[e][4 * ib + x];
-        *dst = v;
-      }
+          for (int x = 0; x < 4; ++x) v[x] = fa * old[x] + fb * acc[e][4 * ib + x];
+          *dst = v;
+        }
+    };
+    if (part) merge_rows(std::true_type{});
+    else merge_rows(std::false_type{});   // the first accumulator: every row was written in the first step
     if (lg == 0) *lse_p = M + __logf(tot);
   }
 }
 
 }  // namespace
 
-hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
+namespace {
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace
+
+StepGeometry step_geometry_bf16(const StepArgs& a) {
+  StepGeometry g;
   const int G = a.h / a.n_kv;
-  const int Hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
-  const int PB = WAVES / Hw;
-  const int n_qb = (a.L + QW * PB - 1) / (QW * PB);
-  const int inner = a.n_kv * a.b * (G / Hw);
-  const int64_t grid = (int64_t)n_qb * inner;
+  g.Hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
+  g.PB = WAVES / g.Hw;
+  g.rows_wg = QW * g.PB;
+  g.n_qb = (a.L + g.rows_wg - 1) / g.rows_wg;
+  g.inner = a.n_kv * a.b * (G / g.Hw);
+  return g;
+}
+
+// Which query blocks of a step run as two work items, and the launch order.
+//
+// One workgroup per compute unit fits (its LDS).  When a step has fewer query blocks than the
+// chip has units for them (short shards: n_qb blocks per KV head and batch row), units sit
+// idle and the longest block sets the step time; splitting a block's key range over two
+// workgroups halves its length, the second half merging into a second accumulator (no two
+// workgroups write one row) that the pass folds into the first at the end.  Measured on
+// MI355X: that pays only while it puts idle units to work.  Balancing a grid that already
+// fills the chip does not: the units whose blocks finish early let the clock of the busy ones
+// rise (the chip is power-limited under full load), and every extra workgroup adds its fixed
+// cost.  So the split is taken only when n_qb is below the units per (KV head, batch row),
+// with at most one item per unit; among those plans it takes the one with the shortest
+// longest item (a block's work: its key tiles plus a fixed cost; blocks s and up are split,
+// the tile counts grow with the block index), the fewest splits on a tie, and only if the
+// longest item shrinks by a tenth.  The host knows every block's tile count from the scalar
+// key limit (not with packed documents, whose bounds live on the device).  Items go out
+// heaviest first (ties: unsplit blocks first).
+SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
+  SplitPlan pl{};
+  const int n_qb = g.n_qb;
+  pl.split_from = n_qb;
+  if (a.doc_begin || n_qb < 1 || n_qb > kSplitMaxBlocks || n_cu < 1) return pl;
+  const int units = n_cu / g.inner;     // units per copy of the item list
+  if (n_qb >= units) return pl;         // the grid fills the chip already
+  constexpr int FIXED = 3;              // per-workgroup cost in tile times (Q load, pipeline fill, epilogue)
+  int w[kSplitMaxBlocks];
+  for (int qb = 0; qb < n_qb; ++qb) {
+    const int last = min((qb + 1) * g.rows_wg, a.L) - 1;
+    w[qb] = (kv_limit(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard, last) + BN - 1) / BN;
+  }
+  int pre_max[kSplitMaxBlocks + 1], suf_max[kSplitMaxBlocks + 1];
+  pre_max[0] = 0;
+  for (int qb = 0; qb < n_qb; ++qb) pre_max[qb + 1] = max(pre_max[qb], w[qb] + FIXED);
+  suf_max[n_qb] = 0;
+  for (int qb = n_qb - 1; qb >= 0; --qb) suf_max[qb] = max(suf_max[qb + 1], (w[qb] + 1) / 2 + FIXED);
+  const int none = pre_max[n_qb];
+  int best = n_qb, best_len = none;
+  for (int s = n_qb - 1; s >= max(0, 2 * n_qb - units); --s) {   // s + 2 (n_qb - s) items <= units
+    const int len = max(pre_max[s], suf_max[s]);
+    if (len < best_len) {
+      best_len = len;
+      best = s;
+    }
+  }
+  if (best == n_qb || 10 * best_len > 9 * none) return pl;
+  // merge the unsplit blocks (best-1 .. 0) and the parts (2 per block, n_qb-1 .. best), both
+  // already in nonincreasing cost, into one nonincreasing order
+  int u = best - 1, m = 0, item = 0;
+  const int n_parts = 2 * (n_qb - best);
+  while (u >= 0 || m < n_parts) {
+    const int cu = u >= 0 ? w[u] + FIXED : -1;
+    const int cp = m < n_parts ? (w[n_qb - 1 - m / 2] + 1) / 2 + FIXED : -1;
+    if (cu >= cp) {
+      pl.order[item >> 5] |= 1u << (item & 31);
+      --u;
+    } else {
+      ++m;
+    }
+    ++item;
+  }
+  pl.split_from = best;
+  return pl;
+}
+
+bool step_splits_bf16(const StepArgs& a) {
+  const StepGeometry g = step_geometry_bf16(a);
+  return plan_split(a, g, cu_count()).split_from < g.n_qb;
+}
+
+hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
+  const StepGeometry g = step_geometry_bf16(a);
+  SplitPlan plan{};
+  plan.split_from = g.n_qb;
+  if (a.o2 && a.lse2) plan = plan_split(a, g, cu_count());
+  const int n_items = plan.split_from + 2 * (g.n_qb - plan.split_from);
+  const int64_t grid = (int64_t)n_items * g.inner;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (mode == MODE_PART)
     hipLaunchKernelGGL(step_fwd_bf16_kernel<MODE_PART>, dim3((unsigned)grid), dim3(THREADS), 0,
-                       stream, a, Hw, n_qb, inner);
+                       stream, a, g.Hw, g.n_qb, g.inner, plan);
   else
     hipLaunchKernelGGL(step_fwd_bf16_kernel<MODE_MERGE>, dim3((unsigned)grid), dim3(THREADS), 0,
-                       stream, a, Hw, n_qb, inner);
+                       stream, a, g.Hw, g.n_qb, g.inner, plan);
   return hipGetLastError();
 }
 

@@ -12,6 +12,10 @@
 #include "ra.h"
 
 static long n_checks = 0, n_fail = 0;
+// The second accumulator that ra_ring_fwd_workspace includes for short bf16 shards; a
+// workspace without it is accepted.
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t second_acc(size_t b, size_t L, size_t h, size_t d) { return al256(b * L * h * d * 4) + al256(b * h * L * 4); }
 static void expect(bool ok, const char* what) {
   ++n_checks;
   if (!ok) {
@@ -66,11 +70,49 @@ int main() {
   expect(ra_merge_lse(&p, Ff, nullptr, Ff, Ff, nullptr) == RA_ERR_INVALID_ARG, "merge null lse");
   expect(ra_finalize(&p, Ff, nullptr, nullptr) == RA_ERR_INVALID_ARG, "finalize null o");
   const size_t ws = ra_ring_fwd_workspace(&p);
-  expect(ws > 0, "ring_fwd_workspace");
-  expect(ra_ring_fwd(&p, 0, F, F, F, F, Ff, F, ws - 1, nullptr, nullptr) == RA_ERR_WORKSPACE, "ring_fwd workspace");
+  expect(ws > second_acc(p.b, p.L, p.h, p.d), "ring_fwd_workspace");
+  const size_t ws_min = ws - second_acc(p.b, p.L, p.h, p.d);
+  expect(ra_ring_fwd(&p, 0, F, F, F, F, Ff, F, ws_min - 1, nullptr, nullptr) == RA_ERR_WORKSPACE, "ring_fwd workspace");
   ra_ring_timing tm;
-  expect(ra_ring_fwd_timed(&p, 0, F, F, F, F, Ff, F, ws - 1, nullptr, nullptr, &tm) == RA_ERR_WORKSPACE,
+  expect(ra_ring_fwd_timed(&p, 0, F, F, F, F, Ff, F, ws_min - 1, nullptr, nullptr, &tm) == RA_ERR_WORKSPACE,
          "ring_fwd_timed workspace");
+  // the step plan: validation, then valid plans (host only) that cover every block once
+  {
+    int32_t blk[256], part[256], n = 0, rows = 0;
+    expect(ra_fwd_step_plan(nullptr, 0, 0, 256, blk, part, 256, &n, &rows) < 0, "plan null problem");
+    expect(ra_fwd_step_plan(&p, 4, 0, 256, blk, part, 256, &n, &rows) == RA_ERR_INVALID_ARG, "plan shard");
+    expect(ra_fwd_step_plan(&p, 0, 0, 0, blk, part, 256, &n, &rows) == RA_ERR_INVALID_ARG, "plan n_cu");
+    expect(ra_fwd_step_plan(&p, 0, 0, 256, nullptr, part, 256, &n, &rows) == RA_ERR_INVALID_ARG, "plan null block");
+    ra_problem f = p;
+    f.dtype = RA_F32;
+    f.d = 64;
+    expect(ra_fwd_step_plan(&f, 0, 0, 256, blk, part, 256, &n, &rows) == RA_ERR_UNSUPPORTED, "plan fp32");
+    for (int L : {64, 1000, 2048, 4096, 4098, 8192})
+      for (int causal = 0; causal < 2; ++causal)
+        for (int cu : {1, 80, 256, 100000}) {
+          ra_problem q = p;
+          q.L = L;
+          q.h = 32;
+          q.n_kv = 8;
+          q.causal = causal;
+          q.layout = causal ? RA_LAYOUT_ZIGZAG : RA_LAYOUT_CONTIGUOUS;
+          const bool ok = ra_fwd_step_plan(&q, 1, 3, cu, blk, part, 256, &n, &rows) == RA_OK;
+          expect(ok && rows > 0 && n > 0 && n <= 256, "plan valid");
+          if (!ok || n > 256 || rows <= 0) continue;
+          const int n_qb = (L + rows - 1) / rows;
+          std::vector<int> seen(n_qb, 0);
+          bool cover = true;
+          for (int i = 0; i < n; ++i) {
+            if (blk[i] < 0 || blk[i] >= n_qb || part[i] < -1 || part[i] > 1) {
+              cover = false;
+              continue;
+            }
+            seen[blk[i]] += part[i] < 0 ? 3 : (part[i] == 0 ? 1 : 2);
+          }
+          for (int v : seen) cover = cover && v == 3;
+          expect(cover, "plan covers every block once");
+        }
+  }
   expect(ra_ring_fwd_timed(&p, 0, F, F, F, F, Ff, F, ws, nullptr, nullptr, nullptr) == RA_ERR_INVALID_ARG,
          "ring_fwd_timed null timing");
   expect(ra_ring_fwd_noalloc(&p, 4, F, F, F, F, Ff, nullptr, nullptr) == RA_ERR_INVALID_ARG, "noalloc shard");
@@ -104,8 +146,9 @@ int main() {
   ra_problem u2 = p;
   u2.N = 2;
   const size_t uws = ra_ulysses_fwd_workspace(&u2);
-  expect(uws > 0, "ulysses workspace");
-  expect(ra_ulysses_fwd_timed(&u2, 0, F, F, F, F, Ff, F, uws - 1, nullptr, &ut) == RA_ERR_WORKSPACE,
+  const size_t u_second = second_acc(u2.b, (size_t)u2.N * u2.L, u2.h / u2.N, u2.d);   // the whole-sequence problem
+  expect(uws > u_second, "ulysses workspace");
+  expect(ra_ulysses_fwd_timed(&u2, 0, F, F, F, F, Ff, F, uws - u_second - 1, nullptr, &ut) == RA_ERR_WORKSPACE,
          "ulysses_fwd_timed workspace");
   expect(ra_ulysses_bwd(&p, 4, F, F, F, F, F, Ff, Ff, Ff, Ff, F, 1u << 30, nullptr) == RA_ERR_INVALID_ARG,
          "ulysses_bwd group");

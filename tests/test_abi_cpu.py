@@ -93,10 +93,13 @@ def test_ring_fwd_rejects_small_workspace():
     lib = _lib.lib()
     p = _prob()
     need = lib.ra_ring_fwd_workspace(ctypes.byref(p))
-    st = lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None, None)
+    # a short bf16 shard: the workspace ends with the optional second accumulator
+    # (fp32 [b][L][h][d] and LSE [b][h][L]); less than the rest is refused
+    second = 128 * 4 * 128 * 4 + 4 * 128 * 4
+    st = lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1, None, None)
     assert st == _lib.RA_ERR_WORKSPACE
     tm = _lib.RaRingTiming()
-    st = lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+    st = lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1,
                                None, None, ctypes.byref(tm))
     assert st == _lib.RA_ERR_WORKSPACE
     assert lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
@@ -147,14 +150,18 @@ def test_hip_failure_is_reported_as_ra_err_hip():
 
 def test_workspace_size_is_two_kv_buffers_plus_fp32_accumulator():
     """Page 4, memory analysis: a device holds its own and one incoming KV block; here the
-    two staging buffers (K and V each) plus the fp32 output accumulator of bf16 problems."""
+    two staging buffers (K and V each) plus the fp32 output accumulator of bf16 problems, and
+    for short bf16 shards (L <= 4096) the second accumulator with its LSE."""
     lib = _lib.lib()
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for dtype, esz in ((1, 2), (0, 4)):
-        p = _prob(dtype=dtype, L=1000, b=2)
-        shard = 2 * 1000 * 2 * 128 * esz
-        pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        want = 4 * pad(shard) + (pad(2 * 1000 * 4 * 128 * 4) if dtype == 1 else 0)
-        assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == want
+        for L in (1000, 5000):
+            p = _prob(dtype=dtype, L=L, b=2)
+            shard = 2 * L * 2 * 128 * esz
+            want = 4 * pad(shard) + (pad(2 * L * 4 * 128 * 4) if dtype == 1 else 0)
+            if dtype == 1 and L <= 4096:
+                want += pad(2 * L * 4 * 128 * 4) + pad(2 * 4 * L * 4)
+            assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == want, (dtype, L)
     assert lib.ra_ring_fwd_workspace(ctypes.byref(_prob(h=3))) == 0
 
 

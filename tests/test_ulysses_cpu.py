@@ -45,6 +45,8 @@ def test_ulysses_workspace_size():
         S = 400
         want = (pad(2 * S * 2 * 128 * es) + 2 * pad(2 * S * 1 * 128 * es) + pad(2 * S * 2 * 128 * 4)
                 + pad(2 * 2 * S * 4))
+        if dtype == 1:     # the second accumulator (bf16, whole sequence <= 4096 tokens)
+            want += pad(2 * S * 2 * 128 * 4) + pad(2 * 2 * S * 4)
         assert lib.ra_ulysses_fwd_workspace(ctypes.byref(p)) == want
 
 
@@ -76,11 +78,12 @@ def test_ulysses_rejects_bad_arguments():
     assert call(-1) == _lib.RA_ERR_INVALID_ARG
     assert call(0, q=None) == _lib.RA_ERR_INVALID_ARG and b"q_all is NULL" in lib.ra_last_error()
     assert call(0, q=ctypes.c_void_p(0x10008)) == _lib.RA_ERR_INVALID_ARG
-    assert call(0, ws=need - 1) == _lib.RA_ERR_WORKSPACE
+    second = 512 * 2 * 128 * 4 + 2 * 512 * 4     # the optional second accumulator (S = 512, 2 heads)
+    assert call(0, ws=need - second - 1) == _lib.RA_ERR_WORKSPACE
     tm = _lib.RaUlyssesTiming()
     assert lib.ra_ulysses_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None,
                                     None) == _lib.RA_ERR_INVALID_ARG
-    assert lib.ra_ulysses_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None,
+    assert lib.ra_ulysses_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1, None,
                                     ctypes.byref(tm)) == _lib.RA_ERR_WORKSPACE
     # packed documents are not part of this path
     pd = _prob(h=8, n_kv=4, N=4)
@@ -145,7 +148,7 @@ def test_usp_workspace_and_validation():
     p = _prob(L=100, h=8, n_kv=4, N=4, layout=2)                 # N_h = 2, N_s = 2: ring shards of 200 tokens
     Lr, Hg, Kg, Ns = 200, 4, 2, 2
     want = pad(Lr * Hg * 128 * 2) + 2 * pad(Ns * Lr * Kg * 128 * 2) + pad(Lr * Hg * 128 * 4) + pad(Hg * Lr * 4) \
-        + 4 * pad(Lr * Kg * 128 * 2)
+        + 4 * pad(Lr * Kg * 128 * 2) + pad(Lr * Hg * 128 * 4) + pad(Hg * Lr * 4)   # last two: second accumulator
     assert lib.ra_usp_fwd_workspace(ctypes.byref(p), 2) == want
     few_kv = _prob(L=100, h=8, n_kv=2, N=4)
     for pp, n_hg, why in ((p, 3, b"divide"), (p, 8, b"divide"), (p, 0, b"divide"), (few_kv, 4, b"multiples")):
@@ -161,7 +164,7 @@ def test_usp_workspace_and_validation():
     assert call(2, 0) == _lib.RA_ERR_INVALID_ARG and b"head_group" in lib.ra_last_error()
     assert call(0, 2) == _lib.RA_ERR_INVALID_ARG and b"ring_rank" in lib.ra_last_error()
     assert call(0, 0, q=None) == _lib.RA_ERR_INVALID_ARG and b"q_all is NULL" in lib.ra_last_error()
-    assert call(0, 0, ws=want - 1) == _lib.RA_ERR_WORKSPACE
+    assert call(0, 0, ws=want - pad(Lr * Hg * 128 * 4) - pad(Hg * Lr * 4) - 1) == _lib.RA_ERR_WORKSPACE
     assert lib.ra_usp_fwd_timed(ctypes.byref(p), 2, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, want, None, None,
                                 None) == _lib.RA_ERR_INVALID_ARG
     pd = _prob(L=100, h=8, n_kv=4, N=4)

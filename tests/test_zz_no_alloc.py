@@ -1,7 +1,8 @@
-"""The allocation-free forward pass (ra_ring_fwd_noalloc) against ra_ring_fwd: the same kernels
-on the same inputs, so outputs must be bit-identical, on two calls in a row (the second smaller,
-so it runs over what the first left in the shared scratch array), in bf16 and fp32; a problem
-whose workspace exceeds the array is refused without writing anything."""
+"""The allocation-free forward pass (ra_ring_fwd_noalloc) against ra_ring_fwd given a workspace
+of the array's size: the same kernels on the same inputs (with the second accumulator exactly
+when it fits in the array), so outputs must be bit-identical, on calls in a row (each smaller,
+so it runs over what the one before left in the shared scratch array), in bf16 and fp32; a
+problem whose workspace exceeds the array is refused without writing anything."""
 import ctypes
 
 import numpy as np
@@ -21,19 +22,28 @@ def _inputs(cfg, dtype, seed, shard):
 
 
 def test_noalloc_matches_ring_fwd_two_calls():
-    cases = [  # (config, dtype, layout, shard): the second call is smaller than the first
+    cases = [  # (config, dtype, layout, shard): each call is smaller than the one before
+        # 48 MiB without the second accumulator, 80 MiB with it: runs unsplit
         (dict(b=1, L=2048, h=32, n_kv=8, d=128, N=4), "bf16", "striped", 1),
+        # 48 MiB with the second accumulator: the split path
+        (dict(b=1, L=2048, h=16, n_kv=8, d=128, N=4), "bf16", "striped", 2),
         (dict(b=2, L=330, h=8, n_kv=2, d=128, N=3), "bf16", "zigzag", 2),
         (dict(b=1, L=256, h=2, n_kv=1, d=64, N=4), "f32", "contiguous", 3),
     ]
+    scratch = _lib.RA_NOALLOC_SCRATCH_BYTES
+    ws = torch.empty(scratch, device="cuda", dtype=torch.uint8)
     for n, (cfg, dtype, layout, shard) in enumerate(cases):
         p = ra.make_problem(**cfg, causal=True, layout=layout,
                             dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
         need = _lib.lib().ra_ring_fwd_workspace(ctypes.byref(p))
-        assert 0 < need <= _lib.RA_NOALLOC_SCRATCH_BYTES
+        assert need > 0
+        if n == 0:
+            assert need > scratch      # the second accumulator does not fit
+        elif n == 1:
+            assert need <= scratch
         announce("ring_fwd_noalloc call", n, cfg, dtype, layout, "shard", shard, "workspace", need)
         inp, (q, k_all, v_all) = _inputs(cfg, dtype, 900 + n, shard)
-        o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout)
+        o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout, workspace=ws)
         o, lse = ra.ring_fwd_noalloc(q, k_all, v_all, q_shard=shard, causal=True, layout=layout)
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
