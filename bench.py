@@ -860,6 +860,55 @@ def run_sweep(args):
         hidden = [r["L"] for r in rows if r[key]["exposed_ms_max"] is not None
                   and r[key]["exposed_ms_max"] <= 0.01 * r[key]["step_ms_mean"]]
         out["sweep"][f"L_min_copy_hidden_on_gpu_{key}"] = min(hidden) if hidden else None
+    # (1b) short shards: the same pass captured in a HIP graph and replayed (the cross-stream
+    #      waits become graph edges), every replay checked against the eager result
+    graph_rows = []
+    for L in (1024, 2048, 4096):
+        q, k, v = inputs(L)
+        for layout, causal in (("striped", True), ("contiguous", False)):
+            ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=causal, layout=layout), device=dev,
+                             dtype=torch.uint8)
+            o = torch.empty_like(q)
+            lse = torch.empty((b, h, L), device=dev)
+
+            def one():
+                ra.ring_fwd(q, k, v, q_shard=0, causal=causal, layout=layout, workspace=ws, out=o, lse_out=lse)
+            one()
+            torch.cuda.synchronize()
+            ref = (o.clone(), lse.clone())
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                one()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                one()
+            torch.cuda.synchronize()
+            same = True
+            for _ in range(3):
+                graph.replay()
+                torch.cuda.synchronize()
+                same = same and torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+                one()                     # eager work between replays
+                torch.cuda.synchronize()
+
+            def med(fn, n=20):
+                ts = []
+                for _ in range(n):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                return float(np.median(ts))
+            eager, replay = med(one), med(graph.replay)
+            graph_rows.append({"L": L, "layout": layout, "causal": causal, "eager_ms": round(eager, 4),
+                               "graph_replay_ms": round(replay, 4), "replays_equal_eager": bool(same)})
+            log(f"[sweep] graph L={L} {layout}: eager {eager:.4f} ms, replay {replay:.4f} ms, equal {same}")
+        del q, k, v
+    out["sweep"]["graph_replay"] = graph_rows
     # (2) every shard of each causal layout at L = 32768 (load balance across devices)
     L = 32768
     q, k, v = inputs(L)
