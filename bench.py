@@ -518,7 +518,7 @@ def run_backward_stationary(args):
     ms, pass_stats = timed_passes(one_pass, args.steps, compute)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
-    # the key/value-rotating schedule of device ks on the same box, for comparison
+    # the key/value-rotating schedule of device ks in the same process, for comparison
     rq = q_all[ks].contiguous()
     rout = (torch.empty((b, L, h, d), device=dev, dtype=torch.float32),
             torch.empty((N, b, L, n_kv, d), device=dev, dtype=torch.float32),

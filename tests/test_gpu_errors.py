@@ -45,9 +45,11 @@ def test_rejected_calls_write_nothing():
 
     announce("errors: ra_ring_fwd with a workspace one byte short")
     need = lib.ra_ring_fwd_workspace(ctypes.byref(p))
+    # without the optional second accumulator of short shards (fp32 [b][L][h][d] and LSE)
+    need_min = need - (b * L * h * d * 4 + b * h * L * 4)
     ws = torch.empty(need, device="cuda", dtype=torch.uint8)
     o16 = _filled((b, L, h, d), torch.bfloat16)
-    assert lib.ra_ring_fwd(ctypes.byref(p), 0, _p(q), _p(k_all), _p(v_all), _p(o16), _p(lse), _p(ws), need - 1,
+    assert lib.ra_ring_fwd(ctypes.byref(p), 0, _p(q), _p(k_all), _p(v_all), _p(o16), _p(lse), _p(ws), need_min - 1,
                            s, None) == _lib.RA_ERR_WORKSPACE
     assert _unchanged(o16, lse)
 
