@@ -53,6 +53,10 @@ CASES = [
     # 1 (256-row blocks), odd ring size
     (dict(b=1, L=1536, h=4, n_kv=4, d=128, N=3), "contiguous", True, 2),
     (dict(b=1, L=640, h=8, n_kv=2, d=128, N=4), "contiguous", False, 1),
+    # three batch rows, one query head per KV head
+    (dict(b=3, L=640, h=4, n_kv=4, d=128, N=3), "striped", True, 1),
+    # two batch rows, 2 query heads per KV head, ragged zigzag shard
+    (dict(b=2, L=500, h=8, n_kv=4, d=128, N=4), "zigzag", True, 0),
 ]
 
 
