@@ -67,12 +67,17 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;            // head dimension
-constexpr int BN = 64;            // keys per tile
+constexpr int BN = 64;            // keys per tile (a multiple of 32)
+constexpr int NB = BN / 32;       // 32-key blocks per tile: score accumulators
+constexpr int NCH = BN / 16;      // 16-key chunks per tile: P operands of P V
+constexpr int SLOTS = BN / 4;     // matrix-phase slots of two products (NCH x 4 = NB x 8)
+constexpr int LOADS_W = BN / 16;  // 1 KB DMA loads per wave and tile (BN / 4 over 4 waves)
+constexpr int LOADS_HALF = LOADS_W / 2;   // issued in the softmax phase; the rest in the next matrix phase
 constexpr int QW = 32;            // query rows per wave
 constexpr int WAVES = 8;          // two per SIMD
 constexpr int THREADS = 64 * WAVES;
 constexpr int ROW_BYTES = D * 2;  // one key's K or V row: 256 B, sixteen 16-byte chunks
-constexpr int TILE_BYTES = BN * ROW_BYTES;   // 16 KB; written by 16 DMA loads of 1 KB
+constexpr int TILE_BYTES = BN * ROW_BYTES;   // written by BN / 4 DMA loads of 1 KB
 constexpr float TAU = 8.0f;       // lazy-rescale threshold, log2 units
 constexpr int PREFETCH = 2;       // matrix-phase operand slots read ahead
 
@@ -201,18 +206,20 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   f32x16 acc[D / 32];
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) acc[e] = f32x16{};
-  f32x16 sc[2];
-  bf16x8 pb[4] = {bf16x8{}, bf16x8{}, bf16x8{}, bf16x8{}};
+  f32x16 sc[NB];
+  bf16x8 pb[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) pb[c] = bf16x8{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale * LOG2E;
 
   // ---- tile staging: global -> LDS by DMA (buffer_load ... lds, 16 B per lane) -----------
-  // A K or V tile is 64 rows of 256 B; DMA load i (1 KB) fills rows 4i..4i+3, lane l
+  // A K or V tile is BN rows of 256 B; DMA load i (1 KB) fills rows 4i..4i+3, lane l
   // writing slot l: row 4i + l/16, slot position l%16.  Each lane picks which global
   // 16-byte chunk lands in its slot, which gives the swizzles the readers need:
   //   K: chunk c of row r sits at position c ^ (r & 15)   (16 rows, same chunk: 16 banks)
   //   V: chunk c of row r sits at position c ^ 4 (r & 3)  (transposed reads, see below)
-  // Group 1 issues the loads, wave w taking loads i = w, w+4, w+8, w+12, so the row bits
+  // Wave w of a group issues loads i = w, w+4, w+8, ... of a tile, so the row bits
   // that enter the swizzle are fixed per lane and the lane's byte offset is one register.
   // The buffer descriptor covers exactly rows 0..L-1 of this (batch, KV head), so rows
   // past the shard end fail the hardware range check and arrive as zeros (always masked).
@@ -226,19 +233,19 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const unsigned v_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ (4 * lrow)) * 16;
   auto issue_tile_dma = [&](dma_rsrc rsrc, unsigned dst, unsigned off, int j) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < LOADS_W; ++t) {
       const int i = ws + 4 * t;
       dma16_to_lds(rsrc, dst + 1024 * i, off, (unsigned)(j * BN + 4 * i) * row_stride);
     }
   };
-  // In the main loop each wave issues loads 0 and 1 of its share of a tile at the start of
-  // its softmax phase and loads 2 and 3 at the start of its next matrix phase (an LDS-DMA
+  // In the main loop each wave issues the first half of its share of a tile at the start of
+  // its softmax phase and the second half at the start of its next matrix phase (an LDS-DMA
   // load costs the issuing wave ~45-55 cycles in either phase; the split balances them:
   // -2 % cycles per tile against all four in the softmax phase).  (Measured against this:
   // the loads between the exponential chains, 11 % slower; all four in the matrix phase,
   // 4 % slower.)  Group 0 stages V tiles, group 1 K tiles.  Loads of tiles past the wave's
   // last one point beyond the buffer (zeros, no memory traffic) into a stage nobody reads
-  // again, so every phase issues exactly two loads and the waits can count them.
+  // again, so every phase issues exactly LOADS_HALF loads and the waits can count them.
   const dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
   const unsigned my_dma_off = group ? k_dma_off : v_dma_off;
   const unsigned my_lds = group ? RA_LDS_ADDR(k_lds) : RA_LDS_ADDR(v_lds);
@@ -298,27 +305,28 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     constexpr int dma_stage_g0 = stage, dma_stage_g1 = (stage + 2) % 3;
     const char* vt = v_lds[(stage + 2) % 3];            // V(j-1)
     const char* kt = k_lds[stage];                      // K(j)
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) sc[jj] = f32x16{};
     bf16x8 va[PREFETCH + 1], ka[PREFETCH + 1];
 #pragma unroll
     for (int x = 0; x < PREFETCH; ++x) {
       va[x] = v_operand(vt, x >> 2, x & 3);
-      ka[x] = k_operand(kt, x >> 1, x & 1);
+      ka[x] = k_operand(kt, x / NB, x % NB);
     }
     // Scheduling fences keep the program order: slot x first issues the reads of slot
     // x + PREFETCH, then its two products, whose operands were read PREFETCH slots
     // earlier, so the LDS latency hides behind 2 PREFETCH products.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      if (x + PREFETCH < 16) {
+    for (int x = 0; x < SLOTS; ++x) {
+      if (x + PREFETCH < SLOTS) {
         va[(x + PREFETCH) % (PREFETCH + 1)] = v_operand(vt, (x + PREFETCH) >> 2, (x + PREFETCH) & 3);
-        ka[(x + PREFETCH) % (PREFETCH + 1)] = k_operand(kt, (x + PREFETCH) >> 1, (x + PREFETCH) & 1);
+        ka[(x + PREFETCH) % (PREFETCH + 1)] = k_operand(kt, (x + PREFETCH) / NB, (x + PREFETCH) % NB);
       }
       acc[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % (PREFETCH + 1)], pb[x >> 2], acc[x & 3], 0, 0, 0);
-      sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (PREFETCH + 1)], qop[x >> 1], sc[x & 1], 0, 0, 0);
-      if (x < 2 && dma_now) issue_one(dma_tile_idx, group ? dma_stage_g1 : dma_stage_g0, 2 + x);
+      sc[x % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x % (PREFETCH + 1)], qop[x / NB], sc[x % NB], 0, 0, 0);
+      if (x < LOADS_W - LOADS_HALF && dma_now)
+        issue_one(dma_tile_idx, group ? dma_stage_g1 : dma_stage_g0, LOADS_HALF + x);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -327,16 +335,19 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // lane's share of the row sum, taken in fp32 from the unrounded weights (the LSE keeps
   // fp32 accuracy).  The scores in sc are left intact.
   auto exponentiate = [&](float neg_m) __attribute__((always_inline)) {
-    float r[4];
+    float r[NCH];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c >> 1][8 * (c & 1) + x], c2, neg_m));
         pb[c][x] = (__bf16)p;
         r[c] = x == 0 ? p : r[c] + p;     // each chain starts at its first weight
       }
-    return (r[0] + r[1]) + (r[2] + r[3]);
+    float sum = (r[0] + r[1]) + (r[2] + r[3]);
+#pragma unroll
+    for (int c = 4; c < NCH; c += 2) sum += r[c] + r[c + 1];
+    return sum;
   };
   // Softmax phase of step j: mask, P = exp2(S c2 - m), row sum.  Fast path: exponentiate
   // against the running maximum as it stands, without computing this tile's maximum; it
@@ -350,24 +361,28 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     const int dma_tile_idx = group ? j + 3 : j + 1;
     const int dma_stage = group ? stage : (stage == 2 ? 0 : stage + 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) issue_one(dma_tile_idx, dma_stage, t);   // the other two: next matrix phase
+    for (int t = 0; t < LOADS_HALF; ++t) issue_one(dma_tile_idx, dma_stage, t);   // the rest: next matrix phase
     if (j >= wave_tiles || j < wave_first) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pb[c] = bf16x8{};
+      for (int c = 0; c < NCH; ++c) pb[c] = bf16x8{};
       return;
     }
     if (j < full_begin || j >= full_end) {
       // keep this a real (scalar) branch: only diagonal, boundary and ragged tiles pay for
       // the mask
       __asm__ volatile("" ::: "memory");
-      const int thr = lim - (j * BN + 4 * lg);       // first masked key offset of this row
-      const int thr_lo = lo - (j * BN + 4 * lg);     // first allowed key offset of this row
+      // allowed key offsets of this row: [thr_lo, thr), thr_lo <= thr; one unsigned compare
+      // per score, fenced in groups of four so that the compiler keeps each compare next to
+      // its select instead of holding all the lane masks in scalar registers
+      const int thr_lo = lo - (j * BN + 4 * lg);
+      const unsigned width = (unsigned)(lim - lo);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < NB; ++jj)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int x = 32 * jj + 8 * (i >> 2) + (i & 3);
-          if (x >= thr || x < thr_lo) sc[jj][i] = -INFINITY;
+          if (!((unsigned)(x - thr_lo) < width)) sc[jj][i] = -INFINITY;
+          if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
     }
     bool full_path = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
@@ -379,15 +394,17 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     if (full_path) {
       float mx;
       {
-        float x0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
-        float x1 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);
+        float xm[NB];
 #pragma unroll
-        for (int i = 3; i < 15; i += 2) {
-          x0 = fmaxf(fmaxf(x0, sc[0][i]), sc[0][i + 1]);
-          x1 = fmaxf(fmaxf(x1, sc[1][i]), sc[1][i + 1]);
+        for (int jj = 0; jj < NB; ++jj) {
+          xm[jj] = fmaxf(fmaxf(sc[jj][0], sc[jj][1]), sc[jj][2]);
+#pragma unroll
+          for (int i = 3; i < 15; i += 2) xm[jj] = fmaxf(fmaxf(xm[jj], sc[jj][i]), sc[jj][i + 1]);
         }
-        x0 = fmaxf(fmaxf(x0, sc[0][15]), x1);
+        float x0 = fmaxf(fmaxf(xm[0], sc[0][15]), xm[1]);
         x0 = fmaxf(x0, sc[1][15]);
+#pragma unroll
+        for (int jj = 2; jj < NB; ++jj) x0 = fmaxf(fmaxf(x0, xm[jj]), sc[jj][15]);
         mx = lane_pair_max(x0) * c2;
       }
       if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
@@ -416,8 +433,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // (last read in interval 2j); first read in interval 2j+5.  Group 1 loads K(j+3) in
   // halves in its softmax phase j (interval 2j+3) and matrix phase j+1 (interval 2j+4),
   // into the stage of K(j) (last read in interval 2j+2); first read in interval 2j+7.  Each
-  // wave waits at the end of its softmax phase j+1 (vmcnt(2): only the two loads that phase
-  // just issued may still be in flight), before the barrier that opens the first interval
+  // wave waits at the end of its softmax phase j+1 (vmcnt(LOADS_HALF): only the loads that
+  // phase just issued may still be in flight), before the barrier that opens the first interval
   // reading the tile.  The prologue loads the first two K tiles and the first V tile
   // completely and starts the third K tile, which group 1's first wait covers; the first
   // matrix phase issues no loads.
@@ -443,9 +460,9 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     __builtin_amdgcn_s_setprio(0);
     barrier_no_fence();
     softmax_phase(j, decltype(stage_c)::value);
-    // vmcnt(2): everything but the two loads this softmax phase just issued has landed,
+    // vmcnt(LOADS_HALF): everything but the loads this softmax phase just issued has landed,
     // i.e. the tile split over the previous softmax phase and this step's matrix phase
-    __builtin_amdgcn_s_waitcnt(0x0F72);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_HALF);
     barrier_no_fence();
   };
   // unrolled by the three stages so that every LDS address in the matrix phase is a
