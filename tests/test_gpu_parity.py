@@ -137,6 +137,23 @@ def test_bf16_ring_equals_steps_merged_by_hand():
     check_bf16(o, lse_acc, O, LSE, "steps+merge")
 
 
+# ------------------------------------------------------------------ long shards: 96-key tiles
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layout,causal", [("striped", True), ("zigzag", True), ("contiguous", False)])
+def test_bf16_long_tiles_ragged_sampled(layout, causal):
+    """Shards of L >= 16384 run 96-key tiles: L = 16448 leaves a ragged last tile (171 tiles and
+    32 keys), checked on ~300 sampled rows of every head against the oracle."""
+    cfg = dict(b=1, L=16448, h=8, n_kv=2, d=128, N=2)
+    shard = 1
+    inp = make_inputs(**cfg, q_shard=shard, seed=61, dtype="bf16")
+    rows = full_size_rows(cfg["L"], 62)
+    announce("bf16 ring_fwd long tiles", layout, "causal", causal, cfg, "rows", rows.size)
+    o, lse = _ring(inp, "bf16", N=2, shard=shard, layout=layout, causal=causal)
+    O, LSE = oracle_ring_rows(inp, N=2, shard=shard, layout=layout, causal=causal, rows=rows)
+    ri = torch.from_numpy(rows).to(o.device)
+    check_bf16(o[:, ri], lse[:, :, ri], O, LSE, f"long tiles {layout} {causal}")
+
+
 # ------------------------------------------------------------------ merge and finalize
 def test_merge_lse_matches_oracle_including_empty_rows():
     rng = np.random.default_rng(5)
