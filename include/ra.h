@@ -156,8 +156,9 @@ ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shar
  * on `compute` (the ring's receive from the previous device, emulated on one GPU; page 1,
  * "The Ring Attention Protocol and Overlapped Communication").  Step 0 reads the local
  * shard in place.  Steps whose KV shard is entirely in the causal future are skipped
- * (their copy still runs).  `copy` may be NULL or equal to `compute` (copies then run in
- * order on `compute`).  All work has finished when work queued on `compute` after this
+ * (their copy still runs).  With bf16 the last live step writes o itself, rounded to
+ * nearest even (no separate finalize pass).  `copy` may be NULL or equal to `compute`
+ * (copies then run in order on `compute`).  All work has finished when work queued on `compute` after this
  * call runs.  ws must hold ra_ring_fwd_workspace(p) bytes, or those less the second
  * accumulator (see there).
  * ------------------------------------------------------------------------------------- */

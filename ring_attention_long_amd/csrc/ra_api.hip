@@ -301,6 +301,12 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     }
   }
   bool live[kMaxRing];
+  // The last live step of a bf16 pass without the second accumulator writes the output
+  // itself (merged rows cast to bf16), so no separate finalize pass reads the accumulator.
+  int k_final = -1;
+  if (!o_acc_ext && p->dtype == RA_BF16 && !second)
+    for (int k = 0; k < N; ++k)
+      if (step_is_live(p, qs, ((qs - k) % N + N) % N)) k_final = k;
 
   // The copy stream must not read k_all / v_all before work the caller queued on `compute`.
   if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -339,6 +345,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       ra::StepArgs a = step_args(p, qs, src, q, kp, vp, o_acc, lse_acc);
       a.o2 = o2;
       a.lse2 = lse2;
+      if (k == k_final) a.o_out = (__bf16*)o;
       if ((e = launch_step(p, a, have_acc ? ra::MODE_MERGE : ra::MODE_PART, cs)) != hipSuccess)
         return hip_fail(e, "step kernel launch");
       have_acc = true;
@@ -362,7 +369,8 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     if ((e = ra::launch_fold_second(o_acc, lse_acc, o2, lse2, o_acc_ext ? nullptr : o, p->b, p->L, p->h, p->d,
                                     cs)) != hipSuccess)
       return hip_fail(e, "fold kernel launch");
-  } else if (!o_acc_ext && p->dtype != RA_F32 && (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess) {
+  } else if (!o_acc_ext && p->dtype != RA_F32 && k_final < 0 &&
+             (e = ra::launch_finalize(o_acc, o, p->dtype, n_out, cs)) != hipSuccess) {
     return hip_fail(e, "finalize kernel launch");
   }
 

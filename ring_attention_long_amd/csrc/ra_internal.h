@@ -224,6 +224,11 @@ struct StepArgs {
   // Rows with lse2 = -inf may hold anything in o2.
   float* o2 = nullptr;
   float* lse2 = nullptr;
+  // Last step of a forward pass (bf16 step kernel, MODE_PART or MODE_MERGE, no second
+  // accumulator): the merged rows, and the accumulator rows this step does not change, are
+  // written here as bf16 [b][L][h][d] (rounded to nearest even) instead of to `o`; lse still
+  // receives the final LSE.  Null: write `o`.
+  __bf16* o_out = nullptr;
 };
 
 hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t s);

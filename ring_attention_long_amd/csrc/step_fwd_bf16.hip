@@ -65,6 +65,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;            // head dimension
@@ -194,13 +195,29 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
     wave_first = max(wave_first, j_begin);
     wave_tiles = min(wave_tiles, n_tiles);
   }
-  // no row of the workgroup sees a key of this shard: merging would leave (O, LSE) as it is
-  if (MODE == MODE_MERGE && n_tiles <= j_begin) return;
   // the accumulator this item writes, and (first step only) the second accumulator's LSE
   // where no second item covers the rows: chosen here, so only these stay live in the loop
   float* const o_dst = part ? a.o2 : a.o;
   float* const l_dst = part ? a.lse2 : a.lse;
   float* const l2_empty = (MODE == MODE_PART && !split_blk) ? a.lse2 : nullptr;
+  // This lane's half of row t, head hq: elements 32 e + 8 ib + 4 lg + x.  On the last step
+  // of a pass (o_out set) the rows go to the output instead of the accumulator, rounded to
+  // nearest even, and rows this step leaves alone are copied over, cast.
+  auto row_offset = [&]() { return (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg; };
+  auto cast_row = [&](int64_t off, int e, int ib, const f32x4& v) __attribute__((always_inline)) {
+    *(bf16x4*)(a.o_out + off + 32 * e + 8 * ib) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  };
+  // no row of the workgroup sees a key of this shard: merging would leave (O, LSE) as it is
+  if (MODE == MODE_MERGE && n_tiles <= j_begin) {
+    if (a.o_out && t < L) {
+      const int64_t off = row_offset();
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) cast_row(off, e, ib, *(const f32x4*)(o_dst + off + 32 * e + 8 * ib));
+    }
+    return;
+  }
 
   // ---- Q^T operand, resident for the whole kernel -------------------------------------
   // Rows past the shard end read row L-1 instead: they are never stored, and their key
@@ -291,7 +308,6 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
                (unsigned)((j16 & 1) * 8);
   }
   auto v_operand = [&](const char* vt, int c, int e) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const char* base = vt + v_off[e] + 16 * c * ROW_BYTES;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (__attribute__((address_space(3))) bf16x4*)(base));
@@ -493,8 +509,9 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const float lse_new = any ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
   const float inv = any ? 1.f / l_tot : 0.f;
   const int64_t lse_idx = ((int64_t)bi * a.h + hq) * L + t;
-  float* orow = o_dst + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
+  const int64_t row_off = row_offset();   // (formed here: not held through the loop)
   float* lse_p = l_dst + lse_idx;
+  // the row's final values are formed in acc, then stored once
   if (MODE == MODE_PART) {
     // rows of an unsplit block have no second partial in this step: mark it empty (a later
     // step may split the block and merge into it)
@@ -502,14 +519,19 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        f32x4 v = {acc[e][4 * ib] * inv, acc[e][4 * ib + 1] * inv, acc[e][4 * ib + 2] * inv,
-                   acc[e][4 * ib + 3] * inv};
-        *(f32x4*)(orow + 32 * e + 8 * ib) = v;
-      }
+      for (int i = 0; i < 16; ++i) acc[e][i] *= inv;
     if (lg == 0) *lse_p = lse_new;
+  } else if (!any) {   // nothing allowed in this step: the accumulator is unchanged
+    if (!a.o_out) return;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const f32x4 old = *(const f32x4*)(o_dst + row_off + 32 * e + 8 * ib);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[e][4 * ib + x] = old[x];
+      }
   } else {
-    if (!any) return;   // nothing allowed in this step: the accumulator is unchanged
     const float lse_old = *lse_p;
     const float M = fmaxf(lse_old, lse_new);
     const float wa = __builtin_amdgcn_exp2f((lse_old - M) * LOG2E);
@@ -523,18 +545,23 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
       for (int e = 0; e < D / 32; ++e)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
-          f32x4* dst = (f32x4*)(orow + 32 * e + 8 * ib);
-          const f32x4 old = have_old ? *dst : f32x4{};
-          f32x4 v;
+          const f32x4 old = have_old ? *(const f32x4*)(o_dst + row_off + 32 * e + 8 * ib) : f32x4{};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = fa * old[x] + fb * acc[e][4 * ib + x];
-          *dst = v;
+          for (int x = 0; x < 4; ++x) acc[e][4 * ib + x] = __builtin_fmaf(fb, acc[e][4 * ib + x], fa * old[x]);
         }
     };
     if (part) merge_rows(std::true_type{});
     else merge_rows(std::false_type{});   // the first accumulator: every row was written in the first step
     if (lg == 0) *lse_p = M + __logf(tot);
   }
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const f32x4 v = {acc[e][4 * ib], acc[e][4 * ib + 1], acc[e][4 * ib + 2], acc[e][4 * ib + 3]};
+      if (a.o_out) cast_row(row_off, e, ib, v);
+      else *(f32x4*)(o_dst + row_off + 32 * e + 8 * ib) = v;
+    }
 }
 
 }  // namespace
@@ -638,6 +665,7 @@ hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
   const StepGeometry g = step_geometry_bf16(a);
   SplitPlan plan{};
   plan.split_from = g.n_qb;
+  if (a.o_out && a.o2) return hipErrorInvalidValue;   // a split pass ends with the fold instead
   if (a.o2 && a.lse2) plan = plan_split(a, g, cu_count());
   const int n_items = plan.split_from + 2 * (g.n_qb - plan.split_from);
   const int64_t grid = (int64_t)n_items * g.inner;
