@@ -140,15 +140,18 @@ def cpu_baseline(inp, cfg, layout, causal, shard, budget_s=20.0, docs=None):
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_fwd_bf16_striped_causal_32k_hbm_bytes.md")
 
 
-def measured_traffic():
-    """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def measured_traffic(ring_steps):
+    """HBM bytes per launch of the dominant step kernel (launches running the ring steps listed
+    in `ring_steps`, e.g. [4, 3]) from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken or they describe other launches."""
     import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
         fields = dict(re.findall(r"^\s+([a-z_0-9]+): (\S+)$", text, flags=re.M))
         src = os.path.join(ROOT, fields["kernel_source"])
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        if fields.get("ring_steps_per_launch", "1") != ",".join(str(n) for n in ring_steps):
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -212,16 +215,17 @@ def timed_passes(one_pass, steps, stream):
                   "max": round(max(per), 4)}
 
 
-def forward_passes(ra, q, k_all, v_all, ws, o, lse, *, shard, causal, layout, docs, steps, warmup):
+def forward_passes(ra, q, k_all, v_all, ws, o, lse, *, shard, causal, layout, docs, steps, warmup, spl=0):
     """`warmup` untimed then `steps` timed forward ring passes (ra_ring_fwd_timed: HIP events
-    around every step kernel and staging copy on the streams they run on).  Returns the mean
-    ms per pass, the per-pass statistics and the per-step timings of the timed passes."""
+    around every kernel launch and staging copy on the streams they run on; spl: ring steps
+    per launch, 0 the library's choice).  Returns the mean ms per pass, the per-pass
+    statistics and the timings of the timed passes."""
     import torch
     timings = []
 
     def one_pass():
         timings.append(ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout,
-                                         workspace=ws, out=o, lse_out=lse, docs=docs)[2])
+                                         workspace=ws, out=o, lse_out=lse, docs=docs, steps_per_launch=spl)[2])
 
     for i in range(warmup):
         one_pass()
@@ -232,16 +236,18 @@ def forward_passes(ra, q, k_all, v_all, ws, o, lse, *, shard, causal, layout, do
     return ms, pass_stats, timings
 
 
-def step_kernel_stats(timings, N, shard, step_flops):
-    """Mean duration of each live step's kernel over the timed passes, and the useful FLOPs of
-    those steps (step_flops(src) for the KV shard src a step holds)."""
-    step_ms, live_flops = [], 0
+def launch_stats(timings, N, shard, step_flops):
+    """The kernel launches of a pass, from the timed passes: a launch running ring steps
+    k .. k + n - 1 is timed at step k.  Returns [(k, n, mean ms, useful FLOPs of its steps)],
+    step_flops(src) giving the FLOPs of the step holding KV shard src."""
+    out = []
     for k in range(N):
-        src = (shard - k) % N
-        if timings[0]["step_begin_ms"][k] >= 0:
-            step_ms.append(float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings])))
-            live_flops += step_flops(src)
-    return step_ms, live_flops
+        n = timings[0]["launch_steps"][k]
+        if n <= 0:
+            continue
+        ms = float(np.mean([t["step_end_ms"][k] - t["step_begin_ms"][k] for t in timings]))
+        out.append((k, n, ms, sum(step_flops((shard - j) % N) for j in range(k, k + n))))
+    return out
 
 
 def forward_summary(ra, accounting, q, k_all, v_all, ws, o, lse, *, cfg, shard, causal, layout, steps, warmup):
@@ -251,15 +257,16 @@ def forward_summary(ra, accounting, q, k_all, v_all, ws, o, lse, *, cfg, shard, 
                                              layout=layout, docs=None, steps=steps, warmup=warmup)
     pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
     value = accounting.flops_from_pairs(pairs, h, d) / (ms * 1e-3) / 1e12
-    step_ms, live_flops = step_kernel_stats(
+    launches = launch_stats(
         timings, N, shard, lambda src: accounting.flops_from_pairs(
             ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, kv_shard=src, causal=causal, layout=layout), h, d))
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
-    achieved = live_flops / (sum(step_ms) * 1e-3) / 1e12
+    rest = [x for x in launches if x[0] > 0] or launches  # the launches after step 0
+    achieved = sum(x[3] for x in rest) / (sum(x[2] for x in rest) * 1e-3) / 1e12
     log(f"[bench] {layout} causal={causal}: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
     return {"value": round(value, 2), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100 * value / peak, 2),
             "ms_per_pass": round(ms, 4), "pass_ms": pass_stats, "steps": steps, "warmup": warmup,
-            "step_kernel_avg_ms": round(float(np.mean(step_ms)), 4),
+            "launch_ms": [round(x[2], 4) for x in launches], "launch_steps": [x[1] for x in launches],
             "roofline_frac": round(achieved / peak, 4)}
 
 
@@ -807,15 +814,29 @@ def run_sweep(args):
         v = torch.randn((N, b, L, n_kv, d), device=dev, generator=gen).to(torch.bfloat16)
         return q, k, v
 
-    def timed(q, k, v, shard, layout, causal, copy_stream="auto", reps=3):
-        ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=causal, layout=layout), device=dev,
-                         dtype=torch.uint8)
+    def timed(q, k, v, shard, layout, causal, copy_stream="auto", reps=3, spl=1):
+        # spl: ring steps per launch; 1 (one launch per step) for the per-step analyses
+        ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=causal, layout=layout, steps_per_launch=spl),
+                         device=dev, dtype=torch.uint8)
         for _ in range(2):
             ra.ring_fwd(q, k, v, q_shard=shard, causal=causal, layout=layout, workspace=ws,
-                        copy_stream=copy_stream)
+                        copy_stream=copy_stream, steps_per_launch=spl)
         runs = [ra.ring_fwd_timed(q, k, v, q_shard=shard, causal=causal, layout=layout,
-                                  workspace=ws, copy_stream=copy_stream)[2] for _ in range(reps)]
+                                  workspace=ws, copy_stream=copy_stream, steps_per_launch=spl)[2]
+                for _ in range(reps)]
         return sorted(runs, key=lambda t: t["total_ms"])[reps // 2]
+
+    def batched(tm, L, shard, layout, causal):
+        """A pass with the library's batching of ring steps into launches."""
+        starts = [k for k in range(N) if tm["launch_steps"][k] > 0]
+        exposed = [max(0.0, max(tm["copy_end_ms"][k:k + tm["launch_steps"][k]]) - tm["step_end_ms"][prev])
+                   for prev, k in zip(starts, starts[1:])]
+        pairs = ra.allowed_pairs(b=b, L=L, N=N, q_shard=shard, causal=causal, layout=layout)
+        fl = accounting.flops_from_pairs(pairs, h, d)
+        return {"pass_ms": round(tm["total_ms"], 4), "tflops": round(fl / tm["total_ms"] / 1e9, 1),
+                "launch_ring_steps": [tm["launch_steps"][k] for k in starts],
+                "launch_ms": [round(tm["step_end_ms"][k] - tm["step_begin_ms"][k], 4) for k in starts],
+                "exposed_ms_max": round(max(exposed), 4) if exposed else None}
 
     def summarise(tm, L, shard, layout, causal):
         steps, copies, overlapped, exposed = [], [], [], []
@@ -850,6 +871,7 @@ def run_sweep(args):
         for layout, causal, key in (("striped", True, "striped_causal"),
                                     ("contiguous", False, "noncausal")):
             row[key] = summarise(timed(q, k, v, 0, layout, causal), L, 0, layout, causal)
+            row[key + "_batched"] = batched(timed(q, k, v, 0, layout, causal, spl=0), L, 0, layout, causal)
         rows.append(row)
         log(f"[sweep] L={L}: {row}")
         del q, k, v
@@ -904,7 +926,8 @@ def run_sweep(args):
                     ts.append(e0.elapsed_time(e1))
                 return float(np.median(ts))
             eager, replay = med(one), med(graph.replay)
-            graph_rows.append({"L": L, "layout": layout, "causal": causal, "eager_ms": round(eager, 4),
+            graph_rows.append({"L": L, "layout": layout, "causal": causal, "steps_per_launch": "library's choice",
+                               "eager_ms": round(eager, 4),
                                "graph_replay_ms": round(replay, 4), "replays_equal_eager": bool(same)})
             log(f"[sweep] graph L={L} {layout}: eager {eager:.4f} ms, replay {replay:.4f} ms, equal {same}")
         del q, k, v
@@ -959,21 +982,23 @@ def run_sweep(args):
         for layout in ("striped", "contiguous"):
             begin, end = ra.document_ranges(bounds, N=N, L=L, shard=0, layout=layout)
             docs = (torch.from_numpy(begin[None]).to(dev), torch.from_numpy(end[None]).to(dev))
-            ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=True, layout=layout), device=dev,
-                             dtype=torch.uint8)
-            for _ in range(2):
-                ra.ring_fwd(q, k, v, q_shard=0, causal=True, layout=layout, workspace=ws, docs=docs)
-            tm = sorted((ra.ring_fwd_timed(q, k, v, q_shard=0, causal=True, layout=layout,
-                                           workspace=ws, docs=docs)[2] for _ in range(3)),
-                        key=lambda t: t["total_ms"])[1]
             pairs = ra.allowed_pairs_packed(begin[None], end[None], N=N, q_shard=0, causal=True,
                                             layout=layout)
             fl = accounting.flops_from_pairs(pairs, h, d)
-            steps = [tm["step_end_ms"][kk] - tm["step_begin_ms"][kk] for kk in range(N)
-                     if tm["step_begin_ms"][kk] >= 0]
-            row[layout] = {"useful_tflop": round(fl / 1e12, 4), "pass_ms": round(tm["total_ms"], 4),
-                           "tflops": round(fl / tm["total_ms"] / 1e9, 1),
-                           "step_ms_mean": round(float(np.mean(steps)), 4)}
+            for spl, key in ((1, layout), (0, layout + "_batched")):
+                ws = torch.empty(ra.ring_workspace_bytes(q, k, causal=True, layout=layout, steps_per_launch=spl),
+                                 device=dev, dtype=torch.uint8)
+                for _ in range(2):
+                    ra.ring_fwd(q, k, v, q_shard=0, causal=True, layout=layout, workspace=ws, docs=docs,
+                                steps_per_launch=spl)
+                tm = sorted((ra.ring_fwd_timed(q, k, v, q_shard=0, causal=True, layout=layout, workspace=ws,
+                                               docs=docs, steps_per_launch=spl)[2] for _ in range(3)),
+                            key=lambda t: t["total_ms"])[1]
+                launches = [tm["step_end_ms"][kk] - tm["step_begin_ms"][kk] for kk in range(N)
+                            if tm["launch_steps"][kk] > 0]
+                row[key] = {"useful_tflop": round(fl / 1e12, 4), "pass_ms": round(tm["total_ms"], 4),
+                            "tflops": round(fl / tm["total_ms"] / 1e9, 1),
+                            "launch_ms": [round(x, 4) for x in launches]}
         packed.append(row)
         log(f"[sweep] packed {row}")
     out["sweep"]["packed_L32768_shard0"] = packed
@@ -1068,27 +1093,35 @@ def main():
                                              layout=layout, docs=docs, steps=args.steps, warmup=args.warmup)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} passes: {ms:.3f} ms/pass, {value:.1f} TFLOP/s useful")
-    step_ms, live_flops = step_kernel_stats(timings, N, shard,
-                                            lambda src: accounting.flops_from_pairs(pairs_of(src), h, d))
+    launches = launch_stats(timings, N, shard, lambda src: accounting.flops_from_pairs(pairs_of(src), h, d))
     tm = sorted(timings, key=lambda t: t["total_ms"])[len(timings) // 2]   # the median pass
-    kern_ms = sum(step_ms)
-    achieved = live_flops / (kern_ms * 1e-3) / 1e12
+    kern_ms = sum(x[2] for x in launches)
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
-    # per staged step k: share of its copy that ran under step kernels, and the time (if
-    # any) the copy ran on past the end of step k-1's kernel
+    # the roofline of the dominant kernel: the launches after step 0 (one kernel, batched or
+    # per step) over their mean duration, or step 0's when it takes longer in all
+    rest = [x for x in launches if x[0] > 0]
+    first = [x for x in launches if x[0] == 0]
+    dom = rest if sum(x[2] for x in rest) >= sum(x[2] for x in first) else first
+    dom_ms = sum(x[2] for x in dom)
+    achieved = sum(x[3] for x in dom) / (dom_ms * 1e-3) / 1e12
+    # per staged shard k: share of its copy that ran under kernels; per launch after the
+    # first: the time (if any) the copies of its shards ran on past the previous launch's end
     intervals = [(tm["step_begin_ms"][k], tm["step_end_ms"][k]) for k in range(N)
-                 if tm["step_begin_ms"][k] >= 0]
+                 if tm["launch_steps"][k] > 0]
     overlapped, exposed = [], []
     for k in range(1, N):
         cb, ce = tm["copy_begin_ms"][k], tm["copy_end_ms"][k]
-        se = tm["step_end_ms"][k - 1]
-        if cb < 0 or tm["step_begin_ms"][k - 1] < 0 or ce <= cb:
-            continue
-        overlapped.append(overlap_fraction(cb, ce, intervals))
-        exposed.append(max(0.0, ce - se))
+        if cb >= 0 and ce > cb:
+            overlapped.append(overlap_fraction(cb, ce, intervals))
+    starts = [k for k in range(N) if tm["launch_steps"][k] > 0]
+    for prev, k in zip(starts, starts[1:]):
+        last_copy = max(tm["copy_end_ms"][k:k + tm["launch_steps"][k]])
+        exposed.append(max(0.0, last_copy - tm["step_end_ms"][prev]))
     kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
     copy_ms = [tm["copy_end_ms"][k] - tm["copy_begin_ms"][k] for k in range(1, N)
                if tm["copy_begin_ms"][k] >= 0]
+    # compute per ring step: a launch's duration spread over the steps it ran
+    per_step_ms = [x[2] / x[1] for x in launches for _ in range(x[1])]
     xgmi_ms = kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3
 
     result = {
@@ -1112,23 +1145,27 @@ def main():
                    "pct_of_bf16_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic() if args.workload == DEFAULT_WORKLOAD else None,
-                     "kernel": "step_fwd_bf16_kernel<MODE_MERGE/MODE_PART>",
-                     "launches": len(step_ms),
-                     "avg_launch_ms": round(kern_ms / max(1, len(step_ms)), 4),
+                     "traffic": measured_traffic([x[1] for x in dom]) if args.workload == DEFAULT_WORKLOAD else None,
+                     "kernel": "step_fwd_bf16_kernel, " + ", ".join(
+                         f"ring steps {x[0]}..{x[0] + x[1] - 1}" if x[1] > 1 else f"ring step {x[0]}" for x in dom),
+                     "launches": len(dom),
+                     "avg_launch_ms": round(dom_ms / len(dom), 4),
+                     "useful_tflop_per_launch": round(sum(x[3] for x in dom) / len(dom) / 1e12, 4),
+                     "all_launches": {"ms": [round(x[2], 4) for x in launches], "ring_steps": [x[1] for x in launches],
+                                      "achieved": round(sum(x[3] for x in launches) / (kern_ms * 1e-3) / 1e12, 2)},
                      "timed_over": f"the {len(timings)} timed passes"},
         "staging": {"kv_bytes_per_step": kv_bytes,
                     "copy_ms": [round(x, 4) for x in copy_ms],
                     "copy_GBps": [round(2 * kv_bytes / (x * 1e-3) / 1e9, 1) for x in copy_ms if x > 0],
-                    "overlap_fraction_per_step": [round(x, 4) for x in overlapped],
-                    "exposed_ms_per_step": [round(x, 4) for x in exposed],
+                    "overlap_fraction_per_copy": [round(x, 4) for x in overlapped],
+                    "exposed_ms_per_launch": [round(x, 4) for x in exposed],
                     "exposed_over_compute_band": exposure_band(sum(exposed), kern_ms),
-                    "step_kernel_ms": [round(x, 4) for x in step_ms],
                     "receive_over_compute": {
                         "definition": "page 3 section 11: median per-step receive time / median per-step "
-                                      "compute time, no overlap subtracted",
-                        "on_gpu_copy": receive_over_compute(copy_ms, step_ms) if copy_ms else None,
-                        "xgmi_link_model": dict(receive_over_compute([xgmi_ms], step_ms),
+                                      "compute time (a launch's duration over the ring steps it ran), no "
+                                      "overlap subtracted",
+                        "on_gpu_copy": receive_over_compute(copy_ms, per_step_ms) if copy_ms else None,
+                        "xgmi_link_model": dict(receive_over_compute([xgmi_ms], per_step_ms),
                                                 receive_ms=round(xgmi_ms, 4), link_GBps=XGMI_LINK_GBPS)}},
     }
     if args.workload == DEFAULT_WORKLOAD and not args.no_extras:

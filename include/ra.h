@@ -89,6 +89,22 @@ typedef struct ra_problem {
    * values give wrong masks, never out-of-bounds accesses.  Both or neither. */
   const int32_t* doc_begin;
   const int32_t* doc_end;
+  /* Ring steps per kernel launch of a bf16 forward pass (ra_ring_fwd, ra_ring_fwd_timed,
+   * ra_ring_fwd_noalloc; other entry points ignore it).  Page 1 ("Blockwise Attention and
+   * Online Softmax Formulations") carries the online-softmax state (m, l, O) from one KV
+   * block to the next; page 2 ("FlashAttention Integration") merges per-step partials by
+   * their LSE instead.  Both give the same result; this chooses where the state lives.
+   *   1: one launch per ring step, merged into (O, LSE) in HBM after each; the KV shard of
+   *      the next step is staged into the idle half of a double buffer while a step runs.
+   *   m >= 2: step 0 (the local shard) alone, then the other steps m at a time, each launch
+   *      walking its KV shards in ring order with the state on chip and merging once; every
+   *      remote shard is staged into a slot of its own (ra_ring_fwd_workspace grows to
+   *      2 (N - 1) K/V slots), each launch waiting only for the copies of its own shards.
+   *   0: the library's choice for N >= 3 when the workspace holds the slots: up to 4 steps
+   *      per launch, all N - 1 remote steps with packed documents; else 1.
+   * On a real ring a device forwards each shard as it arrives, so a launch of m steps after
+   * step 0 finds its shards staged when m transfers take no longer than step 0's compute. */
+  int32_t steps_per_launch;
 } ra_problem;
 
 typedef void* ra_stream; /* a hipStream_t */
@@ -151,12 +167,14 @@ ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shar
  * ra_ring_fwd — the whole forward ring pass of device q_shard.
  * Step k = 0..N-1 attends q to KV shard (q_shard - k) mod N and merges the partial into the
  * running (O, LSE); the final o [b][L][h][d] (p->dtype) and lse [b][h][L] (fp32) equal
- * plain softmax attention of q over the whole sequence.  The KV shard of step k+1 is
- * copied into the idle half of a double buffer on the `copy` stream while step k computes
- * on `compute` (the ring's receive from the previous device, emulated on one GPU; page 1,
- * "The Ring Attention Protocol and Overlapped Communication").  Step 0 reads the local
- * shard in place.  Steps whose KV shard is entirely in the causal future are skipped
- * (their copy still runs).  With bf16 the last live step writes o itself, rounded to
+ * plain softmax attention of q over the whole sequence.  The KV shards of the remote steps
+ * are copied on the `copy` stream while earlier steps compute on `compute` (the ring's
+ * receive from the previous device, emulated on one GPU; page 1, "The Ring Attention
+ * Protocol and Overlapped Communication"): into the idle half of a double buffer, one step
+ * ahead, with one launch per step, or each into a slot of its own when steps are batched
+ * into launches (ra_problem.steps_per_launch).  Step 0 reads the local shard in place.
+ * Steps whose KV shard is entirely in the causal future are skipped (their copy still
+ * runs).  With bf16 the last live step writes o itself, rounded to
  * nearest even (no separate finalize pass).  `copy` may be NULL or equal to `compute`
  * (copies then run in order on `compute`).  All work has finished when work queued on `compute` after this
  * call runs.  ws must hold ra_ring_fwd_workspace(p) bytes, or those less the second
@@ -166,8 +184,10 @@ ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const
                       const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
                       ra_stream compute, ra_stream copy);
 
-/* Per-step timings reported by ra_ring_fwd_timed, in milliseconds from an event recorded
- * on `compute` at entry; -1 where a step was skipped or no copy ran. */
+/* Per-step timings reported by ra_ring_fwd_timed (and ra_ring_bwd), in milliseconds from an
+ * event recorded on `compute` at entry.  A launch that runs ring steps k .. k + n - 1 is
+ * timed at step k (step_begin_ms, step_end_ms) with launch_steps[k] = n; the other steps'
+ * entries are -1 and 0, as are those of skipped steps; copy times are -1 where no copy ran. */
 #define RA_MAX_TIMED_STEPS 64
 typedef struct ra_ring_timing {
   int32_t n_steps;
@@ -176,6 +196,7 @@ typedef struct ra_ring_timing {
   float copy_begin_ms[RA_MAX_TIMED_STEPS]; /* copy that stages the KV of step k */
   float copy_end_ms[RA_MAX_TIMED_STEPS];
   float total_ms;
+  int32_t launch_steps[RA_MAX_TIMED_STEPS];
 } ra_ring_timing;
 
 /* ra_ring_fwd_timed — ra_ring_fwd with timing events around every step kernel (on

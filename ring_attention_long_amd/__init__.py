@@ -49,9 +49,11 @@ def library_path() -> str:
 
 
 def make_problem(*, b, L, h, n_kv, d, N, causal=False, layout="contiguous",
-                 dtype=torch.bfloat16, scale=None, docs=None) -> RaProblem:
+                 dtype=torch.bfloat16, scale=None, docs=None, steps_per_launch=0) -> RaProblem:
     """The C-ABI problem descriptor.  docs: None, or (doc_begin, doc_end), int32 GPU tensors
-    [b, L] holding each query row's packed-document bounds (see document_ranges)."""
+    [b, L] holding each query row's packed-document bounds (see document_ranges).
+    steps_per_launch: ring steps per launch of a bf16 forward pass (0: the library's choice,
+    1: one launch per step; see ra_problem in include/ra.h)."""
     if layout not in RA_LAYOUT:
         raise ValueError(f"layout must be one of {sorted(RA_LAYOUT)}")
     if dtype not in _DTYPES:
@@ -63,7 +65,7 @@ def make_problem(*, b, L, h, n_kv, d, N, causal=False, layout="contiguous",
         _need(end, "doc_end", (b, L), torch.int32)
         db, de = begin.data_ptr(), end.data_ptr()
     return RaProblem(b, L, h, n_kv, d, N, int(bool(causal)), RA_LAYOUT[layout], _DTYPES[dtype],
-                     0.0 if scale is None else float(scale), db, de)
+                     0.0 if scale is None else float(scale), db, de, int(steps_per_launch))
 
 
 def document_ranges(bounds, *, N, L, shard, layout="contiguous"):
@@ -176,10 +178,10 @@ def copy_stream_for(device) -> torch.cuda.Stream:
     return _copy_streams[idx]
 
 
-def ring_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None) -> int:
+def ring_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None, steps_per_launch=0) -> int:
     N, b, L, n_kv, d = k_all.shape
     p = make_problem(b=b, L=L, h=q.shape[2], n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale)
+                     dtype=q.dtype, scale=scale, steps_per_launch=steps_per_launch)
     return int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
 
 
@@ -197,14 +199,14 @@ def fwd_step_plan(*, b, L, h, n_kv, d=128, N, q_shard, kv_shard, causal=False, l
     return [(block[i], part[i]) for i in range(min(n.value, cap))], rows.value
 
 
-def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, docs=None):
+def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, docs=None, steps_per_launch=0):
     N, b, L, n_kv, d = k_all.shape
     h = q.shape[2]
     _need(q, "q", (b, L, h, d), q.dtype)
     _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
     _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale, docs=docs)
+                     dtype=q.dtype, scale=scale, docs=docs, steps_per_launch=steps_per_launch)
     need = int(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
     if need == 0:
         raise RaError(int(_lib.RA_ERR_INVALID_ARG), "ra_ring_fwd_workspace")
@@ -219,13 +221,14 @@ def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, 
 
 
 def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
-             stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, docs=None):
+             stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, docs=None,
+             steps_per_launch=0):
     """Forward ring pass of device q_shard: q [b, L, h, d] against all N KV shards
     k_all, v_all [N, b, L, n_kv, d] in ring order.  Returns (o [b, L, h, d] in q's dtype,
     lse [b, h, L] fp32).  copy_stream="auto" stages KV on a side stream; None stages on
     the compute stream."""
     p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
-                                docs)
+                                docs, steps_per_launch)
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
     check(_lib.lib().ra_ring_fwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream),
@@ -235,11 +238,11 @@ def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", sca
 
 
 def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
-                   stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None,
+                   stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, steps_per_launch=0,
                    docs=None):
     """ring_fwd plus timings (ms from entry): returns (o, lse, dict).  Synchronises."""
     p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
-                                docs)
+                                docs, steps_per_launch)
     cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
     tm = RaRingTiming()
     check(_lib.lib().ra_ring_fwd_timed(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all),
@@ -251,13 +254,13 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
     timing = {
         "step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
         "copy_begin_ms": list(tm.copy_begin_ms[:n]), "copy_end_ms": list(tm.copy_end_ms[:n]),
-        "total_ms": tm.total_ms,
+        "total_ms": tm.total_ms, "launch_steps": list(tm.launch_steps[:n]),
     }
     return o, lse, timing
 
 
 def ring_fwd_noalloc(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
-                     stream=None, copy_stream="auto", out=None, lse_out=None, docs=None):
+                     stream=None, copy_stream="auto", out=None, lse_out=None, docs=None, steps_per_launch=0):
     """ring_fwd through ra_ring_fwd_noalloc: no workspace (the library's fixed scratch array of
     the current device holds it).  Outputs are allocated here unless given."""
     N, b, L, n_kv, d = k_all.shape
@@ -266,7 +269,7 @@ def ring_fwd_noalloc(q, k_all, v_all, *, q_shard, causal=False, layout="contiguo
     _need(k_all, "k_all", (N, b, L, n_kv, d), q.dtype)
     _need(v_all, "v_all", (N, b, L, n_kv, d), q.dtype)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
-                     dtype=q.dtype, scale=scale, docs=docs)
+                     dtype=q.dtype, scale=scale, docs=docs, steps_per_launch=steps_per_launch)
     o = out if out is not None else torch.empty((b, L, h, d), device=q.device, dtype=q.dtype)
     lse = lse_out if lse_out is not None else torch.empty((b, h, L), device=q.device, dtype=torch.float32)
     _need(o, "o", (b, L, h, d), q.dtype)
@@ -510,7 +513,7 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
     n = tm.n_steps
     return dq, dk, dv, {"step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
                         "copy_begin_ms": list(tm.copy_begin_ms[:n]), "copy_end_ms": list(tm.copy_end_ms[:n]),
-                        "total_ms": tm.total_ms}
+                        "total_ms": tm.total_ms, "launch_steps": list(tm.launch_steps[:n])}
 
 
 def ring_bwd_kv_stationary(k, v, q_all, dout_all, lse_all, delta_all, *, kv_shard, causal=False,

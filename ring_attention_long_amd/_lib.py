@@ -28,6 +28,7 @@ class RaProblem(ctypes.Structure):
         ("causal", ctypes.c_int32), ("layout", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("doc_begin", ctypes.c_void_p), ("doc_end", ctypes.c_void_p),
+        ("steps_per_launch", ctypes.c_int32),
     ]
 
 
@@ -39,6 +40,7 @@ class RaRingTiming(ctypes.Structure):
         ("copy_begin_ms", ctypes.c_float * RA_MAX_TIMED_STEPS),
         ("copy_end_ms", ctypes.c_float * RA_MAX_TIMED_STEPS),
         ("total_ms", ctypes.c_float),
+        ("launch_steps", ctypes.c_int32 * RA_MAX_TIMED_STEPS),
     ]
 
 

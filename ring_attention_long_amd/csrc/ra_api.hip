@@ -63,6 +63,8 @@ ra_status check_shape(const ra_problem* p) {
   if (p->layout == RA_LAYOUT_ZIGZAG && (p->L % 2))
     return fail(RA_ERR_INVALID_ARG, "zigzag layout needs an even L (got %d)", p->L);
   if (isnan(p->scale) || isinf(p->scale)) return fail(RA_ERR_INVALID_ARG, "scale is not finite");
+  if (p->steps_per_launch < 0)
+    return fail(RA_ERR_INVALID_ARG, "steps_per_launch must be >= 0 (got %d)", p->steps_per_launch);
   const int64_t seq = (int64_t)p->N * p->L;
   const int64_t q_elems = (int64_t)p->b * p->L * p->h * p->d;
   if (seq > (int64_t)1 << 31 || q_elems > (int64_t)1 << 40)
@@ -204,6 +206,31 @@ size_t ring_fwd_base_workspace(const ra_problem* p) {
   return n;
 }
 
+// Ring steps per launch of a forward pass (ra_problem.steps_per_launch; bf16 only): with
+// m >= 2 the steps after the first run m at a time, each workgroup walking those KV shards
+// in ring order with its softmax state in registers and merging once, instead of paying its
+// Q load, the fp32 accumulator's read-modify-write and a launch for every step; the staging
+// then gives every remote shard a slot of its own instead of the double buffer.
+// The library's choice (0), from measurement on MI355X (h = 32, n_kv = 8, N = 8, L = 1024 ..
+// 32768): at most kDefaultStepsPerLaunch steps per launch, or all N - 1 remote steps with
+// packed documents.  With a causal mask the query blocks of a launch do unequal work per
+// shard, so the workgroups sharing an XCD's L2 drift apart over the shards and stop sharing
+// K/V tiles: seven steps per launch fetched 2.5-3x the bytes of four at L = 8192 and 16384
+// striped (10.0 against 3.6 GB per pass) and no less time; four also leave fewer copies to
+// wait for before a launch at short shards.  Packed documents bound each block's keys per
+// shard, and there all remote steps in one launch took 4 % less time than four.
+constexpr int kDefaultStepsPerLaunch = 4;
+int fwd_steps_per_launch(const ra_problem* p) {
+  if (p->dtype != RA_BF16 || p->N < 3) return 1;
+  int m = p->steps_per_launch;
+  if (m == 0) m = p->doc_begin ? p->N - 1 : kDefaultStepsPerLaunch;
+  return m < p->N - 1 ? m : p->N - 1;
+}
+size_t batch_workspace(const ra_problem* p) {
+  const size_t A = align_up((size_t)p->b * p->L * p->n_kv * p->d * elem_size(p), 256);
+  return 2 * (size_t)(p->N - 1) * A + align_up((size_t)p->b * p->L * p->h * p->d * 4, 256);
+}
+
 // Events of one forward pass made ahead of time (the allocation-free entry point keeps one
 // set per device); without one, ring_fwd_impl creates its own for the call.
 struct RingEvents {
@@ -211,6 +238,151 @@ struct RingEvents {
   hipEvent_t staged[kMaxRing] = {};
   hipEvent_t consumed[kMaxRing] = {};
 };
+
+// The forward pass in batched launches (see fwd_steps_per_launch): step 0 on the local shard
+// while the copy stream stages the N - 1 remote shards in ring order, each into its own slot;
+// then the remaining steps, m at a time, each launch after the copies of its shards.  The
+// last launch with a live step writes the bf16 output.  Arguments as ring_fwd_impl's, checked;
+// tm: per-launch and per-copy timings (N <= RA_MAX_TIMED_STEPS), or null.
+ra_status ring_fwd_batched(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
+                           const void* v_all, void* o, float* lse, void* ws, hipStream_t cs, hipStream_t ps,
+                           const RingEvents* pre, int m, ra_ring_timing* tm) {
+  const int N = p->N;
+  const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
+  const size_t A = align_up(shard_bytes, 256);
+  char* wsc = (char*)ws;
+  char* kslot = wsc;                              // slot k - 1 holds the K of ring step k
+  char* vslot = wsc + (size_t)(N - 1) * A;
+  float* o_acc = (float*)(wsc + 2 * (size_t)(N - 1) * A);
+  const bool split = ps != cs;
+  const bool poison = poison_staging();
+  const bool timing = tm != nullptr;
+  Events ev;
+  hipEvent_t entry, staged[kMaxRing], consumed[kMaxRing];
+  hipEvent_t t_sb[RA_MAX_TIMED_STEPS], t_se[RA_MAX_TIMED_STEPS], t_cb[RA_MAX_TIMED_STEPS],
+      t_ce[RA_MAX_TIMED_STEPS];
+  hipError_t e;
+  if (pre) {
+    entry = pre->entry;
+    for (int k = 0; k < N; ++k) {
+      staged[k] = pre->staged[k];
+      consumed[k] = pre->consumed[k];
+    }
+  } else {
+    if ((e = ev.make(&entry, timing)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    for (int k = 0; k < N; ++k) {
+      if ((e = ev.make(&staged[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+      if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+  }
+  if (timing) {
+    tm->n_steps = N;
+    for (int k = 0; k < N; ++k) {
+      tm->step_begin_ms[k] = tm->step_end_ms[k] = tm->copy_begin_ms[k] = tm->copy_end_ms[k] = -1.f;
+      tm->launch_steps[k] = 0;
+      if ((e = ev.make(&t_sb[k], true)) != hipSuccess || (e = ev.make(&t_se[k], true)) != hipSuccess ||
+          (e = ev.make(&t_cb[k], true)) != hipSuccess || (e = ev.make(&t_ce[k], true)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+    }
+  }
+  // launches: [0], then [k0, k1) groups of live steps; the last live group writes o
+  int g_first[kMaxRing], g_end[kMaxRing], n_groups = 0;
+  g_first[0] = 0;
+  g_end[0] = 1;
+  n_groups = 1;
+  for (int k = 1; k < N; k += m) {
+    const int k1 = k + m < N ? k + m : N;
+    bool live = false;
+    for (int j = k; j < k1; ++j) live = live || step_is_live(p, qs, ((qs - j) % N + N) % N);
+    if (!live) continue;
+    g_first[n_groups] = k;
+    g_end[n_groups] = k1;
+    ++n_groups;
+  }
+  // The copy stream must not read k_all / v_all before work the caller queued on `compute`.
+  if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (split && (e = hipStreamWaitEvent(ps, entry, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  const char* kc = (const char*)k_all;
+  const char* vc = (const char*)v_all;
+  // the copies of every remote shard, in ring order, queued right after step 0's launch (which
+  // reads the local shard in place) so that the compute stream does not wait for the host
+  auto stage_all = [&]() -> ra_status {
+    for (int k = 1; k < N; ++k) {
+      const int src = ((qs - k) % N + N) % N;
+      if (timing && (e = hipEventRecord(t_cb[k], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipMemcpyAsync(kslot + (size_t)(k - 1) * A, kc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(K)");
+      if ((e = hipMemcpyAsync(vslot + (size_t)(k - 1) * A, vc + (size_t)src * shard_bytes, shard_bytes,
+                              hipMemcpyDeviceToDevice, ps)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(V)");
+      if (timing && (e = hipEventRecord(t_ce[k], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipEventRecord(staged[k], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    return RA_OK;
+  };
+  for (int gi = 0; gi < n_groups; ++gi) {
+    const int k0 = g_first[gi], k1 = g_end[gi];
+    const bool last = gi == n_groups - 1;
+    ra::StepArgs a;
+    if (k0 > 0 && split && (e = hipStreamWaitEvent(cs, staged[k1 - 1], 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");   // copies run in ring order: the last covers the others
+    if (timing && (e = hipEventRecord(t_sb[k0], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (k0 == 0) {
+      a = step_args(p, qs, qs, q, kc + (size_t)qs * shard_bytes, vc + (size_t)qs * shard_bytes, o_acc, lse);
+      if (last) a.o_out = (__bf16*)o;
+      if ((e = ra::launch_step_bf16(a, ra::MODE_PART, cs)) != hipSuccess) return hip_fail(e, "step kernel launch");
+    } else {
+      a = step_args(p, qs, qs, q, nullptr, nullptr, o_acc, lse);
+      if (last) a.o_out = (__bf16*)o;
+      ra::ShardBatch sb;
+      sb.k = kslot + (size_t)(k0 - 1) * A;
+      sb.v = vslot + (size_t)(k0 - 1) * A;
+      sb.stride = (int64_t)A;
+      sb.k_first = k0;
+      sb.n = k1 - k0;
+      if ((e = ra::launch_steps_bf16(a, sb, ra::MODE_MERGE, cs)) != hipSuccess)
+        return hip_fail(e, "step kernel launch");
+      if (poison) {
+        if ((e = hipEventRecord(consumed[k0], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        for (int k = k0; k < k1; ++k)
+          if ((e = poison_after(kslot + (size_t)(k - 1) * A, shard_bytes, consumed[k0], ps, split)) != hipSuccess ||
+              (e = poison_after(vslot + (size_t)(k - 1) * A, shard_bytes, consumed[k0], ps, split)) != hipSuccess)
+            return hip_fail(e, "staging poison");
+      }
+    }
+    if (timing) {
+      if ((e = hipEventRecord(t_se[k0], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      tm->launch_steps[k0] = k1 - k0;
+    }
+    if (k0 == 0) RA_TRY(stage_all());
+  }
+  // Work the caller queues on `compute` after this call must not overtake the copy stream,
+  // which still writes the workspace when the last live group ends before the last copy (or
+  // when poisoning): join it back.
+  if (split) {
+    if ((e = hipEventRecord(consumed[0], ps)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(cs, consumed[0], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  if (timing) {
+    hipEvent_t done;
+    if ((e = ev.make(&done, true)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventRecord(done, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipEventSynchronize(done)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    (void)hipEventElapsedTime(&tm->total_ms, entry, done);
+    for (int k = 0; k < N; ++k) {
+      if (tm->launch_steps[k] > 0) {
+        (void)hipEventElapsedTime(&tm->step_begin_ms[k], entry, t_sb[k]);
+        (void)hipEventElapsedTime(&tm->step_end_ms[k], entry, t_se[k]);
+      }
+      if (k >= 1) {
+        (void)hipEventElapsedTime(&tm->copy_begin_ms[k], entry, t_cb[k]);
+        (void)hipEventElapsedTime(&tm->copy_end_ms[k], entry, t_ce[k]);
+      }
+    }
+  }
+  return RA_OK;
+}
 
 ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                         const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
@@ -231,6 +403,17 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   const size_t need = o_acc_ext ? staging_bytes(p) : ring_fwd_base_workspace(p);
   if (ws_bytes < need)
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const int m = o_acc_ext ? 1 : fwd_steps_per_launch(p);
+  if (m >= 2) {
+    if (tm && p->N > RA_MAX_TIMED_STEPS)
+      return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
+    if (ws_bytes >= batch_workspace(p))
+      return ring_fwd_batched(p, qs, q, k_all, v_all, o, lse, ws, (hipStream_t)compute,
+                              copy ? (hipStream_t)copy : (hipStream_t)compute, pre, m, tm);
+    if (p->steps_per_launch != 0)   // asked for explicitly: the workspace must hold the slots
+      return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed for %d steps per launch", ws_bytes,
+                  batch_workspace(p), m);
+  }
   // the second accumulator: the caller's (o_acc_ext), or after the rest when the workspace
   // has room for it
   bool second = fwd_split(p) && (o_acc_ext ? (o2_ext && lse2_ext) : ws_bytes >= need + second_acc_bytes(p));
@@ -295,6 +478,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     tm->n_steps = N;
     for (int k = 0; k < N; ++k) {
       tm->step_begin_ms[k] = tm->step_end_ms[k] = tm->copy_begin_ms[k] = tm->copy_end_ms[k] = -1.f;
+      tm->launch_steps[k] = 0;
       if ((e = ev.make(&t_sb[k], true)) != hipSuccess || (e = ev.make(&t_se[k], true)) != hipSuccess ||
           (e = ev.make(&t_cb[k], true)) != hipSuccess || (e = ev.make(&t_ce[k], true)) != hipSuccess)
         return hip_fail(e, "hipEventCreate");
@@ -384,6 +568,7 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       if (live[k]) {
         (void)hipEventElapsedTime(&tm->step_begin_ms[k], entry, t_sb[k]);
         (void)hipEventElapsedTime(&tm->step_end_ms[k], entry, t_se[k]);
+        tm->launch_steps[k] = 1;
       }
       if (k >= 1) {
         (void)hipEventElapsedTime(&tm->copy_begin_ms[k], entry, t_cb[k]);
@@ -745,6 +930,7 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     tm->n_steps = N;
     for (int k = 0; k < N; ++k) {
       tm->step_begin_ms[k] = tm->step_end_ms[k] = tm->copy_begin_ms[k] = tm->copy_end_ms[k] = -1.f;
+      tm->launch_steps[k] = 0;
       if ((e = ev.make(&t_sb[k], true)) != hipSuccess || (e = ev.make(&t_se[k], true)) != hipSuccess ||
           (e = ev.make(&t_cb[k], true)) != hipSuccess || (e = ev.make(&t_ce[k], true)) != hipSuccess)
         return hip_fail(e, "hipEventCreate");
@@ -810,6 +996,7 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       if (live[k]) {
         (void)hipEventElapsedTime(&tm->step_begin_ms[k], entry, t_sb[k]);
         (void)hipEventElapsedTime(&tm->step_end_ms[k], entry, t_se[k]);
+        tm->launch_steps[k] = 1;
       }
       if (k >= 1) {
         (void)hipEventElapsedTime(&tm->copy_begin_ms[k], entry, t_cb[k]);
@@ -952,7 +1139,7 @@ ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shar
 
 size_t ra_ring_fwd_workspace(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
-  return ring_fwd_base_workspace(p) + second_acc_bytes(p);
+  return fwd_steps_per_launch(p) >= 2 ? batch_workspace(p) : ring_fwd_base_workspace(p) + second_acc_bytes(p);
 }
 
 ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,

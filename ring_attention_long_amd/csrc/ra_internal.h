@@ -231,7 +231,20 @@ struct StepArgs {
   __bf16* o_out = nullptr;
 };
 
+// Several consecutive ring steps in one launch of the bf16 step kernel: steps k_first ..
+// k_first + n - 1 of the pass of a.q_shard, i.e. KV shards (q_shard - k) mod N, whose K and V
+// sit at k + i stride and v + i stride bytes (i = k - k_first), each laid out as StepArgs::k
+// and ::v.  a.k, a.v and a.kv_shard are not used.
+struct ShardBatch {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t stride = 0;
+  int k_first = 0;
+  int n = 0;
+};
+constexpr int kMaxBatch = 128;
 hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t s);
+hipError_t launch_steps_bf16(const StepArgs& a, const ShardBatch& sb, int mode, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, int mode, hipStream_t s);
 hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
                         const float* lse_part, int b, int L, int h, int d, hipStream_t s);

@@ -111,9 +111,13 @@ __device__ __forceinline__ void barrier_no_fence() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int MODE, int BN>
+// BATCH: the workgroup walks the KV shards of `sb` one after the other (several ring steps in
+// one launch), carrying its online-softmax state (m, l, O) from one shard's keys to the next,
+// and merges or writes once at the end.  Otherwise the one KV shard of `a`.
+template <int MODE, int BN, bool BATCH>
 __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, int heads_per_wg,
-                                                                  int n_qb, int inner_count, SplitPlan plan) {
+                                                                  int n_qb, int inner_count, SplitPlan plan,
+                                                                  ShardBatch sb) {
   static_assert(BN % 32 == 0 && BN >= 64, "tiles of whole 32-key blocks, at least two");
   constexpr int NB = BN / 32;       // 32-key blocks per tile: score accumulators
   constexpr int NCH = BN / 16;      // 16-key chunks per tile: P operands of P V
@@ -149,51 +153,83 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   const int t = t0 + lq;                // this lane's query row
 
   const __bf16* qp = (const __bf16*)a.q;
-  const __bf16* kp = (const __bf16*)a.k;
-  const __bf16* vp = (const __bf16*)a.v;
   const int64_t kv_base = ((int64_t)bi * L * a.n_kv + g) * D;
+  const int n_shards = BATCH ? sb.n : 1;
 
-  // ---- key ranges and tile ranges ----------------------------------------------------
-  // Row t may attend to the keys [lo, hi) of this KV shard (a prefix when documents are
+  // ---- key ranges and tile ranges of a KV shard ----------------------------------------
+  // Row t may attend to the keys [lo, hi) of the KV shard (a prefix when documents are
   // not packed).  Both bounds are nondecreasing in t, so a wave's tile range comes from its
   // first and last valid rows: tiles before wave_first or from wave_tiles on are skipped,
   // tiles in [full_begin, full_end) need no mask, the rest are masked.
   const bool packed = a.doc_begin != nullptr;
+  int kv_shard = a.kv_shard;
   auto range = [&](int row) {
     int64_t db = 0, de = 0;
     if (packed) {
       db = a.doc_begin[(int64_t)bi * L + row];
       de = a.doc_end[(int64_t)bi * L + row];
     }
-    return key_range(a.causal, a.layout, a.N, L, a.q_shard, a.kv_shard, row, packed, db, de);
+    return key_range(a.causal, a.layout, a.N, L, a.q_shard, kv_shard, row, packed, db, de);
   };
-  const KeyRange rr = t < L ? range(t) : KeyRange{0, 0};
-  const int lim = rr.hi, lo = rr.lo;
-  int wave_first = 0, wave_tiles = 0, full_begin = 0, full_end = 0;
-  if (t0 < L) {
-    const KeyRange r0 = range(t0), r1 = range(min(t0 + QW - 1, L - 1));
-    wave_first = r0.lo / BN;
-    wave_tiles = (r1.hi + BN - 1) / BN;
-    full_begin = (r1.lo + BN - 1) / BN;
-    full_end = r0.hi / BN;
-  }
-  wave_first = __builtin_amdgcn_readfirstlane(wave_first);
-  wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
-  full_begin = __builtin_amdgcn_readfirstlane(full_begin);
-  full_end = __builtin_amdgcn_readfirstlane(full_end);
+  int lim = 0, lo = 0, wave_first = 0, wave_tiles = 0, full_begin = 0, full_end = 0;
   int j_begin = 0, n_tiles = 0;     // the workgroup's key tiles: [j_begin, n_tiles)
-  if (t0_wg < L) {
-    j_begin = range(t0_wg).lo / BN;
-    n_tiles = (range(min(t0_wg + QW * PB - 1, L - 1)).hi + BN - 1) / BN;
-  }
-  j_begin = __builtin_amdgcn_readfirstlane(j_begin);
-  n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  if (split_blk) {                      // this item's half of the block's key tiles
-    const int j_mid = j_begin + (n_tiles - j_begin + 1) / 2;
-    if (part == 0) n_tiles = j_mid;
-    else j_begin = j_mid;
-    wave_first = max(wave_first, j_begin);
-    wave_tiles = min(wave_tiles, n_tiles);
+  // the workgroup's tile range in shard s (with a split block: this item's half of it)
+  auto wg_tiles = [&](int s) {
+    int tg = t0_wg;
+    if (BATCH) {
+      kv_shard = ((a.q_shard - (sb.k_first + s)) % a.N + a.N) % a.N;
+      __asm__ volatile("" : "+s"(tg));
+    }
+    j_begin = n_tiles = 0;
+    if (tg < L) {
+      j_begin = range(tg).lo / BN;
+      n_tiles = (range(min(tg + QW * PB - 1, L - 1)).hi + BN - 1) / BN;
+    }
+    j_begin = __builtin_amdgcn_readfirstlane(j_begin);
+    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+    if (split_blk) {
+      const int j_mid = j_begin + (n_tiles - j_begin + 1) / 2;
+      if (part == 0) n_tiles = j_mid;
+      else j_begin = j_mid;
+    }
+  };
+  // the rest of shard s's ranges: this lane's keys and this wave's tile classes.  In a batch
+  // the rows pass through an empty asm, so that nothing of the range computation is hoisted
+  // out of the shard loop into registers held through the tile loop.
+  auto row_tiles = [&]() {
+    int tl = t, tw = t0;
+    if (BATCH) __asm__ volatile("" : "+v"(tl), "+s"(tw));
+    const KeyRange rr = tl < L ? range(tl) : KeyRange{0, 0};
+    lim = rr.hi;
+    lo = rr.lo;
+    wave_first = wave_tiles = full_begin = full_end = 0;
+    if (tw < L) {
+      const KeyRange r0 = range(tw), r1 = range(min(tw + QW - 1, L - 1));
+      wave_first = r0.lo / BN;
+      wave_tiles = (r1.hi + BN - 1) / BN;
+      full_begin = (r1.lo + BN - 1) / BN;
+      full_end = r0.hi / BN;
+    }
+    wave_first = __builtin_amdgcn_readfirstlane(wave_first);
+    wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
+    full_begin = __builtin_amdgcn_readfirstlane(full_begin);
+    full_end = __builtin_amdgcn_readfirstlane(full_end);
+    if (split_blk) {
+      wave_first = max(wave_first, j_begin);
+      wave_tiles = min(wave_tiles, n_tiles);
+    }
+  };
+  bool any_tiles = false;
+  int anchor_tile = -1;             // (batch) the wave's first tile of a shard after the first
+  if (BATCH) {
+    for (int s = 0; s < n_shards; ++s) {
+      wg_tiles(s);
+      any_tiles = any_tiles || n_tiles > j_begin;
+    }
+  } else {
+    wg_tiles(0);
+    row_tiles();
+    any_tiles = n_tiles > j_begin;
   }
   // the accumulator this item writes, and (first step only) the second accumulator's LSE
   // where no second item covers the rows: chosen here, so only these stay live in the loop
@@ -207,8 +243,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   auto cast_row = [&](int64_t off, int e, int ib, const f32x4& v) __attribute__((always_inline)) {
     *(bf16x4*)(a.o_out + off + 32 * e + 8 * ib) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
   };
-  // no row of the workgroup sees a key of this shard: merging would leave (O, LSE) as it is
-  if (MODE == MODE_MERGE && n_tiles <= j_begin) {
+  // no row of the workgroup sees a key of the shard(s): merging would leave (O, LSE) as it is
+  if (MODE == MODE_MERGE && !any_tiles) {
     if (a.o_out && t < L) {
       const int64_t off = row_offset();
 #pragma unroll
@@ -251,8 +287,8 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // past the shard end fail the hardware range check and arrive as zeros (always masked).
   const unsigned row_stride = (unsigned)a.n_kv * D * 2;   // bytes between keys in HBM
   const int num_records = (int)((unsigned)(L - 1) * row_stride + ROW_BYTES);
-  const dma_rsrc k_rsrc = make_dma_rsrc(kp + kv_base, (unsigned)num_records);
-  const dma_rsrc v_rsrc = make_dma_rsrc(vp + kv_base, (unsigned)num_records);
+  dma_rsrc k_rsrc = make_dma_rsrc((const __bf16*)(BATCH ? sb.k : a.k) + kv_base, (unsigned)num_records);
+  dma_rsrc v_rsrc = make_dma_rsrc((const __bf16*)(BATCH ? sb.v : a.v) + kv_base, (unsigned)num_records);
   const int ws = wave & 3;
   const unsigned lrow = lane >> 4;                       // row within a 1 KB load
   const unsigned k_dma_off = lrow * row_stride + (unsigned)((lane & 15) ^ ((4 * ws + lrow) & 15)) * 16;
@@ -272,7 +308,7 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // 4 % slower.)  Group 0 stages V tiles, group 1 K tiles.  Loads of tiles past the wave's
   // last one point beyond the buffer (zeros, no memory traffic) into a stage nobody reads
   // again, so every phase issues exactly LOADS_HALF loads and the waits can count them.
-  const dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
+  dma_rsrc my_rsrc = group ? k_rsrc : v_rsrc;
   const unsigned my_dma_off = group ? k_dma_off : v_dma_off;
   const unsigned my_lds = group ? RA_LDS_ADDR(k_lds) : RA_LDS_ADDR(v_lds);
   auto issue_one = [&](int tile, int stage, int t) {
@@ -410,7 +446,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
           if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
     }
-    bool full_path = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    // (in a batch, the first tile of every shard after the first re-anchors m, as a launch
+    // of its own would: see below)
+    const bool anchor = BATCH && j == anchor_tile;
+    bool full_path = anchor || __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     float rs = 0.f;
     if (!full_path) {
       rs = exponentiate(-m_run);
@@ -432,8 +471,15 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
         for (int jj = 2; jj < NB; ++jj) x0 = fmaxf(fmaxf(x0, xm[jj]), sc[jj][15]);
         mx = lane_pair_max(x0) * c2;
       }
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
-        const float m_new = fmaxf(m_run, mx);
+      // Rescale when the maximum has grown by more than TAU, or (anchor) re-anchor m on this
+      // tile's maximum, up or down, as a launch of this shard alone would start: the tile's
+      // largest weight is then exactly 1 and carries no bf16 rounding into P V, which matters
+      // where a few keys dominate a row (with m carried over from an earlier shard it would
+      // be 2^f, rounded, for some f in (-TAU, TAU]).  In re-anchoring, a lane whose tile holds
+      // no key, or whose maximum lies more than 32 below m (the rescale would grow O and l by
+      // more than 2^32), keeps its m.
+      if (anchor || __builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+        const float m_new = !anchor ? fmaxf(m_run, mx) : (mx == -INFINITY || mx < m_run - 32.f) ? m_run : mx;
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -463,6 +509,19 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   // reading the tile.  The prologue loads the first two K tiles and the first V tile
   // completely and starts the third K tile, which group 1's first wait covers; the first
   // matrix phase issues no loads.
+  for (int s = 0; s < n_shards; ++s) {
+  if (BATCH) {
+    // the next shard with a key for this workgroup: its ranges and K/V descriptors
+    wg_tiles(s);
+    if (n_tiles <= j_begin) continue;
+    row_tiles();
+    anchor_tile = s > 0 ? wave_first : -1;
+    k_rsrc = make_dma_rsrc((const __bf16*)((const char*)sb.k + s * sb.stride) + kv_base, (unsigned)num_records);
+    v_rsrc = make_dma_rsrc((const __bf16*)((const char*)sb.v + s * sb.stride) + kv_base, (unsigned)num_records);
+    my_rsrc = group ? k_rsrc : v_rsrc;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) pb[c] = bf16x8{};
+  }
   {
     u32x4* z = (u32x4*)v_lds[2];        // read by the (zero-P) PV of step 0
     for (int i = tid; i < TILE_BYTES / 16; i += THREADS) z[i] = u32x4{};
@@ -501,6 +560,10 @@ __global__ __launch_bounds__(THREADS, 1) void step_fwd_bf16_kernel(StepArgs a, i
   }
   if (group == 0) barrier_no_fence();
   __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): no load into LDS outlives the loop
+  // before the next shard's prologue writes the stages: every wave's loads have landed
+  // (loads past a wave's last tile still write zeros into a stage) and its reads are done
+  if (BATCH) __syncthreads();
+  }   // shard
 
   // ---- epilogue ------------------------------------------------------------------------
   const float l_tot = lane_pair_sum(l_run);
@@ -661,12 +724,9 @@ bool step_splits_bf16(const StepArgs& a) {
   return plan_split(a, g, cu_count()).split_from < g.n_qb;
 }
 
-hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
-  const StepGeometry g = step_geometry_bf16(a);
-  SplitPlan plan{};
-  plan.split_from = g.n_qb;
-  if (a.o_out && a.o2) return hipErrorInvalidValue;   // a split pass ends with the fold instead
-  if (a.o2 && a.lse2) plan = plan_split(a, g, cu_count());
+template <bool BATCH>
+hipError_t launch_fwd(const StepArgs& a, const ShardBatch& sb, const SplitPlan& plan, const StepGeometry& g,
+                      int mode, hipStream_t stream) {
   const int n_items = plan.split_from + 2 * (g.n_qb - plan.split_from);
   const int64_t grid = (int64_t)n_items * g.inner;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -675,20 +735,38 @@ hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
   const bool long_tiles = a.L >= LONG_TILES_MIN_L;
   if (mode == MODE_PART) {
     if (long_tiles)
-      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_PART, BN_LONG>), dim3((unsigned)grid), dim3(THREADS), 0,
-                         stream, a, g.Hw, g.n_qb, g.inner, plan);
+      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_PART, BN_LONG, BATCH>), dim3((unsigned)grid), dim3(THREADS), 0,
+                         stream, a, g.Hw, g.n_qb, g.inner, plan, sb);
     else
-      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_PART, BN_SHORT>), dim3((unsigned)grid), dim3(THREADS), 0,
-                         stream, a, g.Hw, g.n_qb, g.inner, plan);
+      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_PART, BN_SHORT, BATCH>), dim3((unsigned)grid), dim3(THREADS), 0,
+                         stream, a, g.Hw, g.n_qb, g.inner, plan, sb);
   } else {
     if (long_tiles)
-      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_MERGE, BN_LONG>), dim3((unsigned)grid), dim3(THREADS), 0,
-                         stream, a, g.Hw, g.n_qb, g.inner, plan);
+      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_MERGE, BN_LONG, BATCH>), dim3((unsigned)grid), dim3(THREADS), 0,
+                         stream, a, g.Hw, g.n_qb, g.inner, plan, sb);
     else
-      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_MERGE, BN_SHORT>), dim3((unsigned)grid), dim3(THREADS), 0,
-                         stream, a, g.Hw, g.n_qb, g.inner, plan);
+      hipLaunchKernelGGL((step_fwd_bf16_kernel<MODE_MERGE, BN_SHORT, BATCH>), dim3((unsigned)grid), dim3(THREADS), 0,
+                         stream, a, g.Hw, g.n_qb, g.inner, plan, sb);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
+  const StepGeometry g = step_geometry_bf16(a);
+  SplitPlan plan{};
+  plan.split_from = g.n_qb;
+  if (a.o_out && a.o2) return hipErrorInvalidValue;   // a split pass ends with the fold instead
+  if (a.o2 && a.lse2) plan = plan_split(a, g, cu_count());
+  return launch_fwd<false>(a, ShardBatch{}, plan, g, mode, stream);
+}
+
+hipError_t launch_steps_bf16(const StepArgs& a, const ShardBatch& sb, int mode, hipStream_t stream) {
+  // no split of key ranges across workgroups here: every query block runs whole
+  if (a.o2 || a.lse2 || sb.n < 1 || sb.n > kMaxBatch || !sb.k || !sb.v) return hipErrorInvalidValue;
+  const StepGeometry g = step_geometry_bf16(a);
+  SplitPlan plan{};
+  plan.split_from = g.n_qb;
+  return launch_fwd<true>(a, sb, plan, g, mode, stream);
 }
 
 }  // namespace ra

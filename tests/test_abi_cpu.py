@@ -35,10 +35,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def _prob(**kw):
-    base = dict(b=1, L=128, h=4, n_kv=2, d=128, N=4, causal=1, layout=0, dtype=1, scale=0.0)
+    base = dict(b=1, L=128, h=4, n_kv=2, d=128, N=4, causal=1, layout=0, dtype=1, scale=0.0, steps_per_launch=0)
     base.update(kw)
-    return _lib.RaProblem(*[base[k] for k in ("b", "L", "h", "n_kv", "d", "N", "causal",
-                                                "layout", "dtype")], base["scale"])
+    p = _lib.RaProblem(*[base[k] for k in ("b", "L", "h", "n_kv", "d", "N", "causal",
+                                           "layout", "dtype")], base["scale"])
+    p.steps_per_launch = base["steps_per_launch"]
+    return p
 
 
 FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
@@ -91,10 +93,10 @@ def test_bf16_kv_slice_limit():
 
 def test_ring_fwd_rejects_small_workspace():
     lib = _lib.lib()
-    p = _prob()
+    p = _prob(steps_per_launch=1)
     need = lib.ra_ring_fwd_workspace(ctypes.byref(p))
-    # a short bf16 shard: the workspace ends with the optional second accumulator
-    # (fp32 [b][L][h][d] and LSE [b][h][L]); less than the rest is refused
+    # one launch per step, a short bf16 shard: the workspace ends with the optional second
+    # accumulator (fp32 [b][L][h][d] and LSE [b][h][L]); less than the rest is refused
     second = 128 * 4 * 128 * 4 + 4 * 128 * 4
     st = lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1, None, None)
     assert st == _lib.RA_ERR_WORKSPACE
@@ -104,11 +106,26 @@ def test_ring_fwd_rejects_small_workspace():
     assert st == _lib.RA_ERR_WORKSPACE
     assert lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                                  None, None, None) == _lib.RA_ERR_INVALID_ARG
+    # batched steps asked for explicitly: the slots of every remote shard are required
+    pb = _prob(steps_per_launch=2)
+    bneed_f = lib.ra_ring_fwd_workspace(ctypes.byref(pb))
+    assert bneed_f > need - second
+    assert lib.ra_ring_fwd(ctypes.byref(pb), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bneed_f - 1, None,
+                           None) == _lib.RA_ERR_WORKSPACE
+    assert b"steps per launch" in lib.ra_last_error()
+    # the library's choice (0) takes one launch per step when the slots do not fit, so the
+    # one-step minimum still holds
+    p0 = _prob()
+    assert lib.ra_ring_fwd_workspace(ctypes.byref(p0)) == bneed_f
+    assert lib.ra_ring_fwd(ctypes.byref(p0), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1, None,
+                           None) == _lib.RA_ERR_WORKSPACE
     bneed = lib.ra_ring_bwd_workspace(ctypes.byref(p))
     assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  bneed, None, None, None) == _lib.RA_ERR_INVALID_ARG
     assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  bneed - 1, None, None, ctypes.byref(tm)) == _lib.RA_ERR_WORKSPACE
+    assert lib.ra_ring_fwd(ctypes.byref(_prob(steps_per_launch=-2)), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           bneed_f, None, None) == _lib.RA_ERR_INVALID_ARG
 
 
 def _no_hip_device():
@@ -149,20 +166,31 @@ def test_hip_failure_is_reported_as_ra_err_hip():
 
 
 def test_workspace_size_is_two_kv_buffers_plus_fp32_accumulator():
-    """Page 4, memory analysis: a device holds its own and one incoming KV block; here the
-    two staging buffers (K and V each) plus the fp32 output accumulator of bf16 problems, and
-    for short bf16 shards (L <= 4096) the second accumulator with its LSE."""
+    """Page 4, memory analysis: a device holds its own and one incoming KV block.  With one
+    launch per ring step: the two staging buffers (K and V each) plus the fp32 output
+    accumulator of bf16 problems, and for short bf16 shards (L <= 4096) the second
+    accumulator with its LSE.  With bf16 steps batched into launches (the default for N >= 3):
+    a slot for every remote shard's K and V, and the fp32 accumulator."""
     lib = _lib.lib()
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for dtype, esz in ((1, 2), (0, 4)):
         for L in (1000, 5000):
-            p = _prob(dtype=dtype, L=L, b=2)
-            shard = 2 * L * 2 * 128 * esz
-            want = 4 * pad(shard) + (pad(2 * L * 4 * 128 * 4) if dtype == 1 else 0)
-            if dtype == 1 and L <= 4096:
-                want += pad(2 * L * 4 * 128 * 4) + pad(2 * 4 * L * 4)
-            assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == want, (dtype, L)
+            for spl in (0, 1, 2):
+                p = _prob(dtype=dtype, L=L, b=2, steps_per_launch=spl)
+                shard = 2 * L * 2 * 128 * esz
+                acc = pad(2 * L * 4 * 128 * 4) if dtype == 1 else 0
+                if dtype == 1 and spl != 1:      # batched: N - 1 = 3 remote shards
+                    want = 2 * 3 * pad(shard) + acc
+                else:
+                    want = 4 * pad(shard) + acc
+                    if dtype == 1 and L <= 4096:
+                        want += pad(2 * L * 4 * 128 * 4) + pad(2 * 4 * L * 4)
+                assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == want, (dtype, L, spl)
+    # N <= 2: nothing to batch
+    p = _prob(N=2, L=1000)
+    assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == 4 * pad(1000 * 2 * 128 * 2) + pad(1000 * 4 * 128 * 4) * 2 + pad(4 * 1000 * 4)
     assert lib.ra_ring_fwd_workspace(ctypes.byref(_prob(h=3))) == 0
+    assert lib.ra_ring_fwd_workspace(ctypes.byref(_prob(steps_per_launch=-1))) == 0
 
 
 def test_status_strings():

@@ -44,9 +44,17 @@ def test_rejected_calls_write_nothing():
     assert _unchanged(o, lse)
 
     announce("errors: ra_ring_fwd with a workspace one byte short")
-    need = lib.ra_ring_fwd_workspace(ctypes.byref(p))
-    # without the optional second accumulator of short shards (fp32 [b][L][h][d] and LSE)
+    p1 = _lib.RaProblem.from_buffer_copy(p)
+    p1.steps_per_launch = 1
+    need = lib.ra_ring_fwd_workspace(ctypes.byref(p1))
+    # one launch per step (what the library falls back to when the slots of batched steps do
+    # not fit) without the optional second accumulator of short shards (fp32 [b][L][h][d], LSE)
     need_min = need - (b * L * h * d * 4 + b * h * L * 4)
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    o16 = _filled((b, L, h, d), torch.bfloat16)
+    assert lib.ra_ring_fwd(ctypes.byref(p1), 0, _p(q), _p(k_all), _p(v_all), _p(o16), _p(lse), _p(ws),
+                           need_min - 1, s, None) == _lib.RA_ERR_WORKSPACE
+    assert _unchanged(o16, lse)
     ws = torch.empty(need, device="cuda", dtype=torch.uint8)
     o16 = _filled((b, L, h, d), torch.bfloat16)
     assert lib.ra_ring_fwd(ctypes.byref(p), 0, _p(q), _p(k_all), _p(v_all), _p(o16), _p(lse), _p(ws), need_min - 1,

@@ -1,11 +1,13 @@
-"""Ordering of the staging double buffer (page 1, "Practical Implementation Patterns": the
+"""Ordering of the staging buffers (page 1, "Practical Implementation Patterns": the
 incoming block must have arrived before a step reads it, and a buffer is refilled only after
 the step that read it).  The copy stream is held back by a bounded spin before each pass, the
 whole workspace starts as NaN, and with RA_POISON_STAGING=1 every staging buffer is refilled
-with NaN on the copy stream as soon as its step has finished.  A step that read a buffer
-before its copy landed, or after it was consumed, would see NaN; the results must instead be
-bit-identical to a plain pass.  The forward, the backward and the key/value-stationary
-backward are checked, and the test confirms afterwards that the poison really ran."""
+with NaN on the copy stream as soon as its step (or the launch running it) has finished.  A
+step that read a buffer before its copy landed, or after it was consumed, would see NaN; the
+results must instead be bit-identical to a plain pass.  The forward (one launch per step with
+its double buffer, and batched steps with a slot per remote shard), the backward and the
+key/value-stationary backward are checked, and the test confirms afterwards that the poison
+really ran."""
 import ctypes
 
 import numpy as np
@@ -40,27 +42,31 @@ CFG = dict(b=1, L=256, h=8, n_kv=2, d=128, N=6)
 SHARD = 2
 
 
-def _staging_regions(ws, shard_bytes):
+def _staging_regions(ws, shard_bytes, n=4):
     A = (shard_bytes + 255) // 256 * 256
-    return [ws[i * A: i * A + shard_bytes] for i in range(4)]      # K0, V0, K1, V1
+    return [ws[i * A: i * A + shard_bytes] for i in range(n)]
 
 
-def test_forward_order_under_delay_and_poison(monkeypatch):
+@pytest.mark.parametrize("spl", [1, 2, 0])
+def test_forward_order_under_delay_and_poison(monkeypatch, spl):
     inp = make_inputs(**CFG, q_shard=SHARD, seed=1201, dtype="bf16")
     q, k_all, v_all = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all"))
-    announce("ordering: forward, plain pass")
-    o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=SHARD, causal=True, layout="striped")
+    announce("ordering: forward, plain pass, steps per launch", spl)
+    o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=SHARD, causal=True, layout="striped",
+                                 steps_per_launch=spl)
     torch.cuda.synchronize()
-    p = ra.make_problem(**CFG, causal=True, layout="striped", dtype=torch.bfloat16)
+    p = ra.make_problem(**CFG, causal=True, layout="striped", dtype=torch.bfloat16, steps_per_launch=spl)
     ws = _nan_workspace(_lib.lib().ra_ring_fwd_workspace(ctypes.byref(p)))
     monkeypatch.setenv("RA_POISON_STAGING", "1")
-    announce("ordering: forward, copy stream held back, NaN workspace, poison after each step")
+    announce("ordering: forward, copy stream held back, NaN workspace, poison after each launch")
     o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=SHARD, causal=True, layout="striped",
-                         copy_stream=_held_back_stream(), workspace=ws)
+                         copy_stream=_held_back_stream(), workspace=ws, steps_per_launch=spl)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
     shard_bytes = CFG["b"] * CFG["L"] * CFG["n_kv"] * CFG["d"] * 2
-    assert all(_all_ones(r) for r in _staging_regions(ws, shard_bytes)), "staging buffers were not poisoned"
+    # K0, V0, K1, V1 of the double buffer, or the K and V slots of the N - 1 remote shards
+    n_regions = 4 if spl == 1 else 2 * (CFG["N"] - 1)
+    assert all(_all_ones(r) for r in _staging_regions(ws, shard_bytes, n_regions)), "staging buffers were not poisoned"
 
 
 def test_backward_order_under_delay_and_poison(monkeypatch):

@@ -1,9 +1,9 @@
 """Forward passes of short shards with the second accumulator: heavy query blocks run their key
 range as two workgroups merging into two accumulators that the pass folds together (bf16,
-L <= 4096, no packed documents).  Each case first checks, with the device's compute-unit count,
-that the plan really splits blocks in its steps; then the pass must match the oracle, and so
-must the same pass without the second accumulator (every block whole), with the two close to
-each other (they differ only in the order of the fp32 sums)."""
+L <= 4096, no packed documents, one launch per ring step).  Each case first checks, with the
+device's compute-unit count, that the plan really splits blocks in its steps; then the pass
+must match the oracle, and so must the same pass without the second accumulator (every block
+whole), with the two close to each other (they differ only in the order of the fp32 sums)."""
 import numpy as np
 import pytest
 import torch
@@ -38,9 +38,10 @@ def split_blocks(items):
 
 def both_passes(inp, cfg, shard, layout, causal):
     q, k_all, v_all = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all"))
-    o1, l1 = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+    o1, l1 = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, steps_per_launch=1)
     ws = torch.empty(base_workspace(cfg), device="cuda", dtype=torch.uint8)
-    o2, l2 = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws)
+    o2, l2 = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws,
+                         steps_per_launch=1)
     torch.cuda.synchronize()
     return (o1, l1), (o2, l2)
 

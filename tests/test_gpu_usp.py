@@ -71,15 +71,17 @@ def test_usp_f32_every_device(layout):
 
 
 def test_usp_limits_equal_the_ring_and_the_all_to_all_path():
-    """N_h = 1 is the ring (ra_ring_fwd of every shard) and N_s = 1 the all-to-all path
-    (ra_ulysses_fwd of every head group), bit for bit: the same kernels on the same problems."""
+    """N_h = 1 is the ring (ra_ring_fwd of every shard, one launch per ring step as the
+    two-dimensional share runs its ring) and N_s = 1 the all-to-all path (ra_ulysses_fwd of
+    every head group), bit for bit: the same kernels on the same problems."""
     cfg = dict(b=1, L=192, h=8, n_kv=4, d=128, N=4)
     q, k, v = all_devices(**cfg, seed=403, dtype="bf16")
     qg, kg, vg = to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16")
     announce("usp limits: N_h = 1 vs ring, N_s = 1 vs all-to-all")
     out, lse = run_every_share(qg, kg, vg, N_h=1, causal=True, layout="zigzag")
     for j in range(4):
-        o_r, l_r = ra.ring_fwd(qg[j].contiguous(), kg, vg, q_shard=j, causal=True, layout="zigzag")
+        o_r, l_r = ra.ring_fwd(qg[j].contiguous(), kg, vg, q_shard=j, causal=True, layout="zigzag",
+                               steps_per_launch=1)
         torch.cuda.synchronize()
         assert torch.equal(out[j], o_r) and torch.equal(lse[j], l_r)
     out, lse = run_every_share(qg, kg, vg, N_h=4, causal=True, layout="striped")

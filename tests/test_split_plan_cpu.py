@@ -111,8 +111,8 @@ def test_plan_errors_and_workspace_sizes():
     def al(x):
         return -(-x // 256) * 256
 
-    def ws(**cfg):
-        q = ra.make_problem(**cfg, causal=True, layout="striped", dtype=torch.bfloat16)
+    def ws(**cfg):   # one launch per ring step: the pass that may split blocks
+        q = ra.make_problem(**cfg, causal=True, layout="striped", dtype=torch.bfloat16, steps_per_launch=1)
         return lib.ra_ring_fwd_workspace(ctypes.byref(q))
 
     for b, L, h, n_kv in ((1, 2048, 32, 8), (2, 330, 8, 2), (1, 4096, 4, 4), (1, 4097, 4, 4), (1, 8192, 32, 8)):

@@ -1,8 +1,9 @@
 """The allocation-free forward pass (ra_ring_fwd_noalloc) against ra_ring_fwd given a workspace
-of the array's size: the same kernels on the same inputs (with the second accumulator exactly
-when it fits in the array), so outputs must be bit-identical, on calls in a row (each smaller,
-so it runs over what the one before left in the shared scratch array), in bf16 and fp32; a
-problem whose workspace exceeds the array is refused without writing anything."""
+of the array's size: the same kernels on the same inputs (batched steps, or with one launch per
+step the second accumulator, exactly when they fit in the array), so outputs must be
+bit-identical, on calls in a row (each no larger, so it runs over what the one before left in
+the shared scratch array), in bf16 and fp32; a problem whose workspace exceeds the array is
+refused without writing anything."""
 import ctypes
 
 import numpy as np
@@ -22,29 +23,34 @@ def _inputs(cfg, dtype, seed, shard):
 
 
 def test_noalloc_matches_ring_fwd_two_calls():
-    cases = [  # (config, dtype, layout, shard): each call is smaller than the one before
-        # 48 MiB without the second accumulator, 80 MiB with it: runs unsplit
-        (dict(b=1, L=2048, h=32, n_kv=8, d=128, N=4), "bf16", "striped", 1),
+    cases = [  # (config, steps per launch, dtype, layout, shard): each call no larger than the one before
+        # all remote steps in one launch: 6 K/V slots and the accumulator, 56 MiB
+        (dict(b=1, L=2048, h=32, n_kv=8, d=128, N=4), 0, "bf16", "striped", 1),
+        # one launch per step: 48 MiB without the second accumulator, 80 MiB with it: unsplit
+        (dict(b=1, L=2048, h=32, n_kv=8, d=128, N=4), 1, "bf16", "striped", 1),
         # 48 MiB with the second accumulator: the split path
-        (dict(b=1, L=2048, h=16, n_kv=8, d=128, N=4), "bf16", "striped", 2),
-        (dict(b=2, L=330, h=8, n_kv=2, d=128, N=3), "bf16", "zigzag", 2),
-        (dict(b=1, L=256, h=2, n_kv=1, d=64, N=4), "f32", "contiguous", 3),
+        (dict(b=1, L=2048, h=16, n_kv=8, d=128, N=4), 1, "bf16", "striped", 2),
+        (dict(b=2, L=330, h=8, n_kv=2, d=128, N=3), 0, "bf16", "zigzag", 2),
+        (dict(b=1, L=256, h=2, n_kv=1, d=64, N=4), 0, "f32", "contiguous", 3),
     ]
     scratch = _lib.RA_NOALLOC_SCRATCH_BYTES
     ws = torch.empty(scratch, device="cuda", dtype=torch.uint8)
-    for n, (cfg, dtype, layout, shard) in enumerate(cases):
-        p = ra.make_problem(**cfg, causal=True, layout=layout,
+    for n, (cfg, spl, dtype, layout, shard) in enumerate(cases):
+        p = ra.make_problem(**cfg, causal=True, layout=layout, steps_per_launch=spl,
                             dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
         need = _lib.lib().ra_ring_fwd_workspace(ctypes.byref(p))
         assert need > 0
-        if n == 0:
+        if n == 1:
             assert need > scratch      # the second accumulator does not fit
-        elif n == 1:
+        elif n in (0, 2):
             assert need <= scratch
-        announce("ring_fwd_noalloc call", n, cfg, dtype, layout, "shard", shard, "workspace", need)
+        announce("ring_fwd_noalloc call", n, cfg, "steps per launch", spl, dtype, layout, "shard", shard,
+                 "workspace", need)
         inp, (q, k_all, v_all) = _inputs(cfg, dtype, 900 + n, shard)
-        o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout, workspace=ws)
-        o, lse = ra.ring_fwd_noalloc(q, k_all, v_all, q_shard=shard, causal=True, layout=layout)
+        o_ref, lse_ref = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout, workspace=ws,
+                                     steps_per_launch=spl)
+        o, lse = ra.ring_fwd_noalloc(q, k_all, v_all, q_shard=shard, causal=True, layout=layout,
+                                     steps_per_launch=spl)
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
         if dtype == "bf16":
