@@ -139,10 +139,14 @@ ra_status ra_merge_lse(const ra_problem* p, float* o_acc, float* lse_acc, const 
  * ------------------------------------------------------------------------------------- */
 ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_stream stream);
 
-/* Bytes of device workspace for ra_ring_fwd: two KV staging buffers (the double buffer of
- * page 1, "Practical Implementation Patterns"); unless dtype is fp32, an fp32 output
- * accumulator [b][L][h][d]; and, for bf16 without packed documents and L <= 4096, a second
- * fp32 accumulator [b][L][h][d] with its LSE [b][h][L] (each part 256-byte aligned).  With
+/* Bytes of device workspace for ra_ring_fwd (each part 256-byte aligned).  With ring steps
+ * batched into launches (p->steps_per_launch >= 2, or 0 for a bf16 ring of N >= 3): a K/V
+ * slot for each of the N - 1 remote shards and the fp32 output accumulator [b][L][h][d].
+ * With one launch per step: two KV staging buffers (the double buffer of page 1, "Practical
+ * Implementation Patterns"); unless dtype is fp32, the fp32 output accumulator; and, for
+ * bf16 without packed documents and L <= 4096, a second fp32 accumulator [b][L][h][d] with
+ * its LSE [b][h][L].  Given less than the batched size, the library's choice (0) runs one
+ * launch per step.  With
  * the second accumulator the steps of short shards may run the key range of a heavy query
  * block as two workgroups, one merging into each accumulator, and the pass folds the two
  * together at the end (page 2, "FlashAttention Integration": partials over disjoint key
@@ -211,18 +215,20 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
 /* ---------------------------------------------------------------------------------------
  * ra_ring_fwd_noalloc — ra_ring_fwd for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
- * pass, kernels and results as ra_ring_fwd, with its workspace (the KV staging double buffer
- * and the fp32 output accumulator) held in a fixed device array of RA_NOALLOC_SCRATCH_BYTES
+ * pass, kernels and results as ra_ring_fwd, with its workspace (the KV staging buffers or
+ * slots and the fp32 output accumulator) held in a fixed device array of RA_NOALLOC_SCRATCH_BYTES
  * inside the library instead of a caller buffer; the caller passes inputs and outputs only.
  * Runs on the calling thread's current device.  Each device holds its own array from the
  * library's load until the process ends; the first call on a device looks up the array's
  * address and creates the pass's events (no device memory is allocated then or later).
- * Errors: as ra_ring_fwd, and RA_ERR_WORKSPACE (nothing enqueued) when
- * ra_ring_fwd_workspace(p) without its second accumulator exceeds RA_NOALLOC_SCRATCH_BYTES
- * (for bf16 that is 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32,
- * n_kv = 8, d = 128 fits); the second accumulator is used when it fits as well (L = 2048 with
- * h = 16, n_kv = 8), and the results equal ra_ring_fwd's with a workspace of
- * RA_NOALLOC_SCRATCH_BYTES.  Every call on one device shares that device's array and events, and the array
+ * Errors: as ra_ring_fwd, and RA_ERR_WORKSPACE (nothing enqueued) when the workspace of one
+ * launch per step without its second accumulator exceeds RA_NOALLOC_SCRATCH_BYTES (for bf16
+ * that is 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32, n_kv = 8,
+ * d = 128 fits), or when steps_per_launch >= 2 asks for slots that do not fit.  Under the
+ * library's choice the batched steps run when their slots fit (L = 2048 with h = 32,
+ * n_kv = 8, N = 4; L = 1024 with N = 8), else with one launch per step the second
+ * accumulator when it fits (L = 2048 with h = 16, n_kv = 8); the results equal ra_ring_fwd's
+ * with a workspace of RA_NOALLOC_SCRATCH_BYTES.  Every call on one device shares that device's array and events, and the array
  * keeps the last call's contents (each pass overwrites everything it reads, so nothing
  * needs clearing): calls whose work overlaps on one device (different streams, or threads
  * not ordered by the caller) race and give wrong results, so order them, e.g. on one stream.
