@@ -758,8 +758,9 @@ def run_usp(args):
 def run_hbm_kernels(args):
     """The HBM-bound pieces alone, at the S = 262144, N = 8 one-device shapes (L = 32768,
     h = 32, n_kv = 8, d = 128): the standalone LSE merge (ra_merge_lse), the finalize
-    (ra_finalize, fp32 -> bf16), and a device-to-device copy of one K (or V) shard, the same
-    runtime copy the ring's staging issues.  GB/s from HIP events over `steps` calls each."""
+    (ra_finalize, fp32 -> bf16), and a runtime device-to-device copy of one K (or V) shard for
+    reference (the ring stages K and V with its own kernel, whose launches and GB/s the
+    default line's `staging` block reports).  GB/s from HIP events over `steps` calls each."""
     import torch
 
     import ring_attention_long_amd as ra
@@ -1108,18 +1109,23 @@ def main():
     # first: the time (if any) the copies of its shards ran on past the previous launch's end
     intervals = [(tm["step_begin_ms"][k], tm["step_end_ms"][k]) for k in range(N)
                  if tm["launch_steps"][k] > 0]
-    overlapped, exposed = [], []
+    # staging launches: one per step, or one per group of batched steps (its shards report
+    # the same begin and end)
+    copies = {}
     for k in range(1, N):
         cb, ce = tm["copy_begin_ms"][k], tm["copy_end_ms"][k]
         if cb >= 0 and ce > cb:
-            overlapped.append(overlap_fraction(cb, ce, intervals))
+            copies[(cb, ce)] = copies.get((cb, ce), 0) + 1
+    copy_launches = sorted((cb, ce, n) for (cb, ce), n in copies.items())
+    overlapped = [overlap_fraction(cb, ce, intervals) for cb, ce, _ in copy_launches]
+    exposed = []
     starts = [k for k in range(N) if tm["launch_steps"][k] > 0]
     for prev, k in zip(starts, starts[1:]):
         last_copy = max(tm["copy_end_ms"][k:k + tm["launch_steps"][k]])
         exposed.append(max(0.0, last_copy - tm["step_end_ms"][prev]))
     kv_bytes = accounting.kv_bytes_per_step(b, L, n_kv, d, 2)
-    copy_ms = [tm["copy_end_ms"][k] - tm["copy_begin_ms"][k] for k in range(1, N)
-               if tm["copy_begin_ms"][k] >= 0]
+    copy_ms = [ce - cb for cb, ce, _ in copy_launches]
+    receive_ms = [(ce - cb) / n for cb, ce, n in copy_launches for _ in range(n)]   # per shard
     # compute per ring step: a launch's duration spread over the steps it ran
     per_step_ms = [x[2] / x[1] for x in launches for _ in range(x[1])]
     xgmi_ms = kv_bytes / (XGMI_LINK_GBPS * 1e9) * 1e3
@@ -1155,16 +1161,18 @@ def main():
                                       "achieved": round(sum(x[3] for x in launches) / (kern_ms * 1e-3) / 1e12, 2)},
                      "timed_over": f"the {len(timings)} timed passes"},
         "staging": {"kv_bytes_per_step": kv_bytes,
-                    "copy_ms": [round(x, 4) for x in copy_ms],
-                    "copy_GBps": [round(2 * kv_bytes / (x * 1e-3) / 1e9, 1) for x in copy_ms if x > 0],
-                    "overlap_fraction_per_copy": [round(x, 4) for x in overlapped],
+                    "copy_launch_ms": [round(x, 4) for x in copy_ms],
+                    "copy_launch_shards": [n for _, _, n in copy_launches],
+                    "copy_GBps": [round(2 * kv_bytes * n / ((ce - cb) * 1e-3) / 1e9, 1)
+                                  for cb, ce, n in copy_launches],
+                    "overlap_fraction_per_copy_launch": [round(x, 4) for x in overlapped],
                     "exposed_ms_per_launch": [round(x, 4) for x in exposed],
                     "exposed_over_compute_band": exposure_band(sum(exposed), kern_ms),
                     "receive_over_compute": {
                         "definition": "page 3 section 11: median per-step receive time / median per-step "
                                       "compute time (a launch's duration over the ring steps it ran), no "
                                       "overlap subtracted",
-                        "on_gpu_copy": receive_over_compute(copy_ms, per_step_ms) if copy_ms else None,
+                        "on_gpu_copy": receive_over_compute(receive_ms, per_step_ms) if receive_ms else None,
                         "xgmi_link_model": dict(receive_over_compute([xgmi_ms], per_step_ms),
                                                 receive_ms=round(xgmi_ms, 4), link_GBps=XGMI_LINK_GBPS)}},
     }

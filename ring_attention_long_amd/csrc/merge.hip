@@ -12,6 +12,8 @@
 // Each thread owns 4 consecutive floats (16-byte loads and stores); the d/4 threads of a
 // row sit in one wave, so every lane reads the row's old LSE before the lane holding the
 // row's first column overwrites it.
+#include <algorithm>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -121,6 +123,22 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
   if (i < n4) ((f32x4*)dst)[i] = ((const f32x4*)src)[i];
 }
 
+// The K/V receive of ring steps k0 .. k0 + gridDim.y - 1 of device qs: step k gets the shard
+// of device (qs - k) mod N, K into kdst + (k - k0) stride and V into vdst + (k - k0) stride.
+// blockIdx.y: the step, blockIdx.z: K (0) or V (1); 16 bytes per thread and iteration.
+__global__ __launch_bounds__(256) void stage_kv_kernel(char* __restrict__ kdst, char* __restrict__ vdst,
+                                                       const char* __restrict__ k_all,
+                                                       const char* __restrict__ v_all, int64_t shard_bytes,
+                                                       int64_t stride, int N, int qs, int k0) {
+  const int k = k0 + (int)blockIdx.y;
+  const int src = ((qs - k) % N + N) % N;
+  const u32x4* from = (const u32x4*)((blockIdx.z ? v_all : k_all) + (int64_t)src * shard_bytes);
+  u32x4* to = (u32x4*)((blockIdx.z ? vdst : kdst) + (int64_t)blockIdx.y * stride);
+  const int64_t n16 = shard_bytes / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    to[i] = from[i];
+}
+
 __global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -163,6 +181,18 @@ hipError_t launch_fold_second(float* o, float* lse, const float* o2, const float
   else
     hipLaunchKernelGGL(fold_second_kernel<false>, dim3(blocks_for(n8)), dim3(256), 0, s, o, lse, o2, lse2,
                        (__bf16*)nullptr, L, h, d / 8, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_kv(char* kdst, char* vdst, const void* k_all, const void* v_all, int64_t shard_bytes,
+                           int64_t stride, int N, int qs, int k0, int n_steps, hipStream_t s) {
+  if (n_steps <= 0 || shard_bytes <= 0) return hipSuccess;
+  if (shard_bytes % 16 || n_steps > 65535) return hipErrorInvalidValue;
+  // 64 workgroups per shard and tensor: the copy runs beside step kernels that fill every
+  // compute unit, and wider grids slowed them (measured on MI355X)
+  const int64_t blocks = std::min<int64_t>((shard_bytes / 16 + 255) / 256, 64);
+  hipLaunchKernelGGL(stage_kv_kernel, dim3((unsigned)blocks, (unsigned)n_steps, 2), dim3(256), 0, s, kdst, vdst,
+                     (const char*)k_all, (const char*)v_all, shard_bytes, stride, N, qs, k0);
   return hipGetLastError();
 }
 

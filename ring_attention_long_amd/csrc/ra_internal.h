@@ -251,6 +251,11 @@ hipError_t launch_merge(float* o_acc, float* lse_acc, const float* o_part,
 hipError_t launch_finalize(const float* o_acc, void* o, int dtype, int64_t n_elems,
                            hipStream_t s);
 hipError_t launch_fill_lse(float* lse, int64_t n, float value, hipStream_t s);
+// The ring's K/V receive for steps k0 .. k0 + n_steps - 1 of device qs, in one launch: step
+// k copies K and V of shard (qs - k) mod N from k_all, v_all ([N] shards of shard_bytes,
+// a multiple of 16) to kdst and vdst + (k - k0) stride.
+hipError_t launch_stage_kv(char* kdst, char* vdst, const void* k_all, const void* v_all, int64_t shard_bytes,
+                           int64_t stride, int N, int qs, int k0, int n_steps, hipStream_t s);
 // Fold the second accumulator (o2, lse2) of a forward pass into (o, lse), row by row (rows
 // with lse2 = -inf keep (o, lse) and never read o2).  With out null, o is updated in place in
 // fp32; otherwise the folded rows (and the untouched ones) are written to out in bf16 and o is
