@@ -100,8 +100,9 @@ typedef struct ra_problem {
    *      walking its KV shards in ring order with the state on chip and merging once; every
    *      remote shard is staged into a slot of its own (ra_ring_fwd_workspace grows to
    *      2 (N - 1) K/V slots), each launch waiting only for the copies of its own shards.
-   *   0: the library's choice for N >= 3 when the workspace holds the slots: up to 4 steps
-   *      per launch, all N - 1 remote steps with packed documents; else 1.
+   *   0: the library's choice for N >= 3 when the workspace holds the slots: all N - 1
+   *      remote steps in one launch when b h L^2 <= 2^33 (short steps) or with packed
+   *      documents, else up to 4 steps per launch; 1 when the slots do not fit.
    * On a real ring a device forwards each shard as it arrives, so a launch of m steps after
    * step 0 finds its shards staged when m transfers take no longer than step 0's compute. */
   int32_t steps_per_launch;

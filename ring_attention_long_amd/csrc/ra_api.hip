@@ -212,18 +212,24 @@ size_t ring_fwd_base_workspace(const ra_problem* p) {
 // Q load, the fp32 accumulator's read-modify-write and a launch for every step; the staging
 // then gives every remote shard a slot of its own instead of the double buffer.
 // The library's choice (0), from measurement on MI355X (h = 32, n_kv = 8, N = 8, L = 1024 ..
-// 32768): at most kDefaultStepsPerLaunch steps per launch, or all N - 1 remote steps with
-// packed documents.  With a causal mask the query blocks of a launch do unequal work per
-// shard, so the workgroups sharing an XCD's L2 drift apart over the shards and stop sharing
-// K/V tiles: seven steps per launch fetched 2.5-3x the bytes of four at L = 8192 and 16384
-// striped (10.0 against 3.6 GB per pass) and no less time; four also leave fewer copies to
-// wait for before a launch at short shards.  Packed documents bound each block's keys per
-// shard, and there all remote steps in one launch took 4 % less time than four.
+// 32768): all N - 1 remote steps in one launch while a step is short (b h L^2 <= 2^33, i.e.
+// L <= 16384 at b = 1, h = 32) or with packed documents, else at most kDefaultStepsPerLaunch.
+// Short steps: one launch and one wait instead of two took 7 % less time at L = 1024, 4-6 %
+// at 2048 and up to 2 % at 4096-16384 (every layout).  Long steps
+// (L = 32768) measured alike with 4 and 7 per launch (within 0.3 %), and with a causal mask
+// the query blocks of a launch do unequal work per shard, so the workgroups sharing an XCD's
+// L2 drift apart over the shards and stop sharing K/V tiles: seven steps per launch fetched
+// 3x the bytes of four there (33 against 11 GB per pass); four keep the traffic down.
+// Packed documents bound each block's keys per shard, and there all remote steps in one
+// launch took 4 % less time than four at L = 32768.
 constexpr int kDefaultStepsPerLaunch = 4;
 int fwd_steps_per_launch(const ra_problem* p) {
   if (p->dtype != RA_BF16 || p->N < 3) return 1;
   int m = p->steps_per_launch;
-  if (m == 0) m = p->doc_begin ? p->N - 1 : kDefaultStepsPerLaunch;
+  if (m == 0) {
+    const double work = (double)p->b * p->h * (double)p->L * p->L;
+    m = (p->doc_begin || work <= 8589934592.0) ? p->N - 1 : kDefaultStepsPerLaunch;
+  }
   return m < p->N - 1 ? m : p->N - 1;
 }
 size_t batch_workspace(const ra_problem* p) {

@@ -1,5 +1,6 @@
 """Forward passes with ring steps batched into launches (ra_problem.steps_per_launch >= 2, and
-the library's choice 0: up to 4 steps per launch, all remote steps with packed documents):
+the library's choice 0: all remote steps in one launch for short steps or packed documents,
+up to 4 per launch for long steps):
 after step 0 each workgroup walks several KV shards in ring order with its online-softmax
 state (m, l, O) on chip and merges once (page 1, "Blockwise Attention and Online Softmax
 Formulations": the state carried from one block to the next), and every remote shard is
@@ -68,22 +69,22 @@ def test_batched_head_groupings(h, n_kv):
 
 
 def test_batched_default_equals_explicit_and_timed():
-    """The library's choice is up to four steps per launch; the timed pass runs the same
-    launches (step 0, then steps 1..4 and 5) and reports them by their first step."""
+    """Short steps (b h L^2 <= 2^33): the library's choice is all remote steps in one launch;
+    the timed pass runs the same launches and reports them by their first step."""
     cfg = dict(b=1, L=512, h=8, n_kv=2, d=128, N=6)
     inp = make_inputs(**cfg, q_shard=4, seed=1420, dtype="bf16")
     q, k_all, v_all = _tensors(inp)
     o0, l0 = ra.ring_fwd(q, k_all, v_all, q_shard=4, causal=True, layout="striped")
-    o4, l4 = ra.ring_fwd(q, k_all, v_all, q_shard=4, causal=True, layout="striped", steps_per_launch=4)
+    o5, l5 = ra.ring_fwd(q, k_all, v_all, q_shard=4, causal=True, layout="striped", steps_per_launch=5)
     ot, lt, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=4, causal=True, layout="striped")
     o2, l2, tm2 = ra.ring_fwd_timed(q, k_all, v_all, q_shard=4, causal=True, layout="striped", steps_per_launch=2)
     torch.cuda.synchronize()
     announce("timed launches", tm["launch_steps"], tm2["launch_steps"])
-    assert torch.equal(o0, o4) and torch.equal(l0, l4)
+    assert torch.equal(o0, o5) and torch.equal(l0, l5)
     assert torch.equal(o0, ot) and torch.equal(l0, lt)
-    assert tm["launch_steps"] == [1, 4, 0, 0, 0, 1]
+    assert tm["launch_steps"] == [1, 5, 0, 0, 0, 0]
     assert tm2["launch_steps"] == [1, 2, 0, 2, 0, 1]
-    for t, starts in ((tm, [0, 1, 5]), (tm2, [0, 1, 3, 5])):
+    for t, starts in ((tm, [0, 1]), (tm2, [0, 1, 3, 5])):
         for k in range(cfg["N"]):
             timed = t["step_begin_ms"][k] >= 0
             assert timed == (k in starts)
@@ -96,7 +97,23 @@ def test_batched_default_equals_explicit_and_timed():
             n = t["launch_steps"][s]
             assert t["step_begin_ms"][s] >= max(t["copy_end_ms"][s:s + n]) - 1e-3
     O, LSE = oracle_ring(inp, N=cfg["N"], shard=4, layout="striped", causal=True)
+    check_bf16(o0, l0, O, LSE, "library's choice, all remote steps in one launch")
     check_bf16(o2, l2, O, LSE, "timed, 2 steps per launch")
+
+
+def test_batched_default_long_steps_four_per_launch():
+    """Long steps (b h L^2 > 2^33: L = 16448, h = 32): the library's choice is four steps per
+    launch (step 0, ring steps 1..4, then 5), the same launches as steps_per_launch = 4."""
+    L, h, n_kv, d, N = 16448, 32, 8, 128, 6
+    g = torch.Generator(device="cuda").manual_seed(1425)
+    mk = lambda *s: torch.randn(*s, device="cuda", generator=g).to(torch.bfloat16)
+    q, k_all, v_all = mk(1, L, h, d), mk(N, 1, L, n_kv, d), mk(N, 1, L, n_kv, d)
+    announce("long steps, library's choice", dict(L=L, h=h, n_kv=n_kv, N=N))
+    o0, l0, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=2, causal=True, layout="zigzag")
+    o4, l4 = ra.ring_fwd(q, k_all, v_all, q_shard=2, causal=True, layout="zigzag", steps_per_launch=4)
+    torch.cuda.synchronize()
+    assert tm["launch_steps"] == [1, 4, 0, 0, 0, 1]
+    assert torch.equal(o0, o4) and torch.equal(l0, l4)
 
 
 def test_batched_contiguous_dead_groups():
