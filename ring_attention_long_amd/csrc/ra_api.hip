@@ -430,6 +430,8 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   // the workspace for the staging buffers only; the second accumulator (when the problem
   // keeps one) is then (o2_ext, lse2_ext).
   RA_TRY(check_problem(p));
+  // before either path: both keep per-step events in arrays of kMaxRing
+  if (p->N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", p->N, kMaxRing);
   RA_TRY(check_shard(p, qs, "q_shard"));
   RA_TRY(check_ptr(q, "q", 16));
   RA_TRY(check_ptr(k_all, "k_all", 16));
@@ -467,7 +469,6 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   const int N = p->N;
   if (tm && N > RA_MAX_TIMED_STEPS)
     return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
-  if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
 
   const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
   const size_t A = align_up(shard_bytes, 256);

@@ -128,6 +128,25 @@ def test_ring_fwd_rejects_small_workspace():
                            bneed_f, None, None) == _lib.RA_ERR_INVALID_ARG
 
 
+def test_ring_fwd_rejects_ring_above_limit():
+    """N above the driver's limit (128) is refused before anything else, on the one-launch-
+    per-step and the batched path alike (both keep per-step events in fixed arrays)."""
+    lib = _lib.lib()
+    tm = _lib.RaRingTiming()
+    for spl in (0, 1, 4):
+        for dtype in (0, 1):
+            p = _prob(N=129, dtype=dtype, steps_per_launch=spl)
+            ws = lib.ra_ring_fwd_workspace(ctypes.byref(p))
+            assert lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None,
+                                   None) == _lib.RA_ERR_UNSUPPORTED, (spl, dtype)
+            assert b"ring size" in lib.ra_last_error()
+            assert lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None,
+                                         ctypes.byref(tm)) in (_lib.RA_ERR_UNSUPPORTED, _lib.RA_ERR_INVALID_ARG)
+    p = _prob(N=128, steps_per_launch=4)
+    assert lib.ra_ring_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None,
+                           None) == _lib.RA_ERR_WORKSPACE
+
+
 def _no_hip_device():
     """True when the HIP runtime sees no device at all (this container), so a call with
     valid arguments fails at its first HIP call and never touches memory."""
