@@ -98,13 +98,46 @@ def allowed_pairs_packed(doc_begin, doc_end, *, N, q_shard, kv_shard=-1, causal=
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    """Address of a tensor handed to the library, which reads and writes it from its kernels:
+    only a contiguous GPU tensor qualifies (a host or strided one would fault the GPU)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("the library takes GPU tensors only")
+    if not t.is_contiguous():
+        raise ValueError("the library takes contiguous tensors only")
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(s) -> ctypes.c_void_p:
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _one_device(*ts) -> torch.device:
+    """The one GPU all given tensors (None skipped) live on."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors on several devices: {sorted(str(x) for x in devs)}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, not {dev}")
+    return dev
+
+
+def _stream(s, device=None) -> ctypes.c_void_p:
     if s is None:
-        s = torch.cuda.current_stream()
+        s = torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _copy_stream_arg(copy_stream, device):
+    cs = copy_stream_for(device) if copy_stream == "auto" else copy_stream
+    return ctypes.c_void_p(cs.cuda_stream) if cs is not None else None
+
+
+def _run(device, name, *args) -> None:
+    """Call library entry point `name` with `device` current (the pass's events and the
+    default stream belong to it) and raise RaError on a status other than RA_OK."""
+    with torch.cuda.device(device):
+        check(getattr(_lib.lib(), name)(*args), name)
 
 
 def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
@@ -139,8 +172,9 @@ def step_fwd(q, k, v, *, N, q_shard, kv_shard, causal=False, layout="contiguous"
                      dtype=q.dtype, scale=scale, docs=docs)
     o = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
     lse = torch.empty((b, h, L), device=q.device, dtype=torch.float32)
-    check(_lib.lib().ra_step_fwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(o), _ptr(lse), _stream(stream)), "ra_step_fwd")
+    dev = _one_device(q, k, v, *(docs or ()))
+    _run(dev, "ra_step_fwd", ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+         _stream(stream, dev))
     return o, lse
 
 
@@ -152,8 +186,9 @@ def merge_lse(o_acc, lse_acc, o_part, lse_part, *, stream=None):
                       (lse_acc, "lse_acc", (b, h, L)), (lse_part, "lse_part", (b, h, L))):
         _need(t, n, shp, torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=torch.float32)
-    check(_lib.lib().ra_merge_lse(ctypes.byref(p), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
-                                  _ptr(lse_part), _stream(stream)), "ra_merge_lse")
+    dev = _one_device(o_acc, lse_acc, o_part, lse_part)
+    _run(dev, "ra_merge_lse", ctypes.byref(p), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
+         _stream(stream, dev))
     return o_acc, lse_acc
 
 
@@ -163,8 +198,8 @@ def finalize(o_acc, dtype=torch.bfloat16, *, stream=None):
     _need(o_acc, "o_acc", (b, L, h, d), torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=dtype)
     o = torch.empty((b, L, h, d), device=o_acc.device, dtype=dtype)
-    check(_lib.lib().ra_finalize(ctypes.byref(p), _ptr(o_acc), _ptr(o), _stream(stream)),
-          "ra_finalize")
+    dev = _one_device(o_acc)
+    _run(dev, "ra_finalize", ctypes.byref(p), _ptr(o_acc), _ptr(o), _stream(stream, dev))
     return o
 
 
@@ -217,7 +252,8 @@ def _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out, 
                                                           dtype=torch.float32)
     _need(o, "o", (b, L, h, d), q.dtype)
     _need(lse, "lse", (b, h, L), torch.float32)
-    return p, workspace, o, lse
+    dev = _one_device(q, k_all, v_all, o, lse, workspace, *(docs or ()))
+    return p, workspace, o, lse, dev
 
 
 def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", scale=None,
@@ -227,13 +263,10 @@ def ring_fwd(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous", sca
     k_all, v_all [N, b, L, n_kv, d] in ring order.  Returns (o [b, L, h, d] in q's dtype,
     lse [b, h, L] fp32).  copy_stream="auto" stages KV on a side stream; None stages on
     the compute stream."""
-    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
-                                docs, steps_per_launch)
-    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
-    check(_lib.lib().ra_ring_fwd(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
-                                 _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream),
-                                 ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
-          "ra_ring_fwd")
+    p, ws, o, lse, dev = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
+                                     docs, steps_per_launch)
+    _run(dev, "ra_ring_fwd", ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all), _ptr(o), _ptr(lse),
+         _ptr(ws), _nbytes(ws), _stream(stream, dev), _copy_stream_arg(copy_stream, dev))
     return o, lse
 
 
@@ -241,15 +274,12 @@ def ring_fwd_timed(q, k_all, v_all, *, q_shard, causal=False, layout="contiguous
                    stream=None, copy_stream="auto", workspace=None, out=None, lse_out=None, steps_per_launch=0,
                    docs=None):
     """ring_fwd plus timings (ms from entry): returns (o, lse, dict).  Synchronises."""
-    p, ws, o, lse = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
-                                docs, steps_per_launch)
-    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    p, ws, o, lse, dev = _ring_args(q, k_all, v_all, causal, layout, scale, workspace, out, lse_out,
+                                     docs, steps_per_launch)
     tm = RaRingTiming()
-    check(_lib.lib().ra_ring_fwd_timed(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all),
-                                       _ptr(v_all), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
-                                       _stream(stream),
-                                       ctypes.c_void_p(cs.cuda_stream) if cs is not None else None,
-                                       ctypes.byref(tm)), "ra_ring_fwd_timed")
+    _run(dev, "ra_ring_fwd_timed", ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all), _ptr(o),
+         _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev), _copy_stream_arg(copy_stream, dev),
+         ctypes.byref(tm))
     n = tm.n_steps
     timing = {
         "step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
@@ -274,12 +304,9 @@ def ring_fwd_noalloc(q, k_all, v_all, *, q_shard, causal=False, layout="contiguo
     lse = lse_out if lse_out is not None else torch.empty((b, h, L), device=q.device, dtype=torch.float32)
     _need(o, "o", (b, L, h, d), q.dtype)
     _need(lse, "lse", (b, h, L), torch.float32)
-    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
-    with torch.cuda.device(q.device):
-        check(_lib.lib().ra_ring_fwd_noalloc(ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all),
-                                             _ptr(o), _ptr(lse), _stream(stream),
-                                             ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
-              "ra_ring_fwd_noalloc")
+    dev = _one_device(q, k_all, v_all, o, lse, *(docs or ()))
+    _run(dev, "ra_ring_fwd_noalloc", ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all), _ptr(o),
+         _ptr(lse), _stream(stream, dev), _copy_stream_arg(copy_stream, dev))
     return o, lse
 
 
@@ -310,7 +337,8 @@ def _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, ls
                                                          device=q_all.device, dtype=torch.float32)
     _need(o, "o_all", (N, b, L, h, d), q_all.dtype)
     _need(lse, "lse_all", (N, b, h, L), torch.float32)
-    return p, workspace, o, lse
+    dev = _one_device(q_all, k_all, v_all, o, lse, workspace)
+    return p, workspace, o, lse, dev
 
 
 def ulysses_fwd(q_all, k_all, v_all, *, head_group, causal=False, layout="contiguous", scale=None,
@@ -320,10 +348,9 @@ def ulysses_fwd(q_all, k_all, v_all, *, head_group, causal=False, layout="contig
     heads [head_group h/N, (head_group+1) h/N) of every shard into out [N, b, L, h, d]
     (q's dtype) and lse_out [N, b, h, L] fp32 (allocated if None: zeros and -inf elsewhere)
     and returns them; call it for every head group to fill them."""
-    p, ws, o, lse = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
-    check(_lib.lib().ra_ulysses_fwd(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all),
-                                    _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
-          "ra_ulysses_fwd")
+    p, ws, o, lse, dev = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    _run(dev, "ra_ulysses_fwd", ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all), _ptr(o),
+         _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
     return o, lse
 
 
@@ -331,11 +358,10 @@ def ulysses_fwd_timed(q_all, k_all, v_all, *, head_group, causal=False, layout="
                       scale=None, stream=None, workspace=None, out=None, lse_out=None):
     """ulysses_fwd plus the time of its parts: returns (o, lse, dict with gather_ms,
     attend_ms, scatter_ms, total_ms).  Synchronises."""
-    p, ws, o, lse = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
+    p, ws, o, lse, dev = _ulysses_args(q_all, k_all, v_all, causal, layout, scale, workspace, out, lse_out)
     tm = RaUlyssesTiming()
-    check(_lib.lib().ra_ulysses_fwd_timed(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all),
-                                          _ptr(v_all), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
-                                          _stream(stream), ctypes.byref(tm)), "ra_ulysses_fwd_timed")
+    _run(dev, "ra_ulysses_fwd_timed", ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all),
+         _ptr(o), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev), ctypes.byref(tm))
     return o, lse, {"gather_ms": tm.gather_ms, "attend_ms": tm.attend_ms,
                     "scatter_ms": tm.scatter_ms, "total_ms": tm.total_ms}
 
@@ -369,10 +395,10 @@ def ulysses_bwd(q_all, k_all, v_all, o_all, dout_all, lse_all, *, head_group, ca
     _need(dq, "dq_all", (N, b, L, h, d), torch.float32)
     _need(dk, "dk_all", (N, b, L, n_kv, d), torch.float32)
     _need(dv, "dv_all", (N, b, L, n_kv, d), torch.float32)
-    check(_lib.lib().ra_ulysses_bwd(ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all),
-                                    _ptr(o_all), _ptr(dout_all), _ptr(lse_all), _ptr(dq), _ptr(dk),
-                                    _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
-          "ra_ulysses_bwd")
+    dev = _one_device(q_all, k_all, v_all, o_all, dout_all, lse_all, dq, dk, dv, workspace)
+    _run(dev, "ra_ulysses_bwd", ctypes.byref(p), head_group, _ptr(q_all), _ptr(k_all), _ptr(v_all), _ptr(o_all),
+         _ptr(dout_all), _ptr(lse_all), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
+         _stream(stream, dev))
     return dq, dk, dv
 
 
@@ -408,15 +434,15 @@ def usp_fwd(q_all, k_all, v_all, *, n_head_groups, head_group, ring_rank, causal
                                                          dtype=torch.float32)
     _need(o, "o_all", (N, b, L, h, d), q_all.dtype)
     _need(lse, "lse_all", (N, b, h, L), torch.float32)
-    cs = copy_stream_for(q_all.device) if copy_stream == "auto" else copy_stream
+    dev = _one_device(q_all, k_all, v_all, o, lse, workspace)
     args = (ctypes.byref(p), n_head_groups, head_group, ring_rank, _ptr(q_all), _ptr(k_all), _ptr(v_all), _ptr(o),
-            _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
-            ctypes.c_void_p(cs.cuda_stream) if cs is not None else None)
+            _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream, dev),
+            _copy_stream_arg(copy_stream, dev))
     if not timed:
-        check(_lib.lib().ra_usp_fwd(*args), "ra_usp_fwd")
+        _run(dev, "ra_usp_fwd", *args)
         return o, lse
     tm = _lib.RaUspTiming()
-    check(_lib.lib().ra_usp_fwd_timed(*args, ctypes.byref(tm)), "ra_usp_fwd_timed")
+    _run(dev, "ra_usp_fwd_timed", *args, ctypes.byref(tm))
     return o, lse, {k: getattr(tm, k) for k, _ in _lib.RaUspTiming._fields_}
 
 
@@ -427,8 +453,8 @@ def bwd_preprocess(o, dout, *, stream=None):
     _need(dout, "dout", (b, L, h, d), o.dtype)
     p = make_problem(b=b, L=L, h=h, n_kv=h, d=d, N=1, dtype=o.dtype)
     delta = torch.empty((b, h, L), device=o.device, dtype=torch.float32)
-    check(_lib.lib().ra_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta),
-                                       _stream(stream)), "ra_bwd_preprocess")
+    dev = _one_device(o, dout)
+    _run(dev, "ra_bwd_preprocess", ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta), _stream(stream, dev))
     return delta
 
 
@@ -453,9 +479,9 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
     _need(dv_acc, "dv_acc", (b, L, n_kv, d), torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
                      dtype=q.dtype, scale=scale, docs=docs)
-    check(_lib.lib().ra_step_bwd(ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
-                                 _ptr(dv_acc), _stream(stream)), "ra_step_bwd")
+    dev = _one_device(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, *(docs or ()))
+    _run(dev, "ra_step_bwd", ctypes.byref(p), q_shard, kv_shard, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+         _ptr(delta), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _stream(stream, dev))
     return dq_acc, dk_acc, dv_acc
 
 
@@ -501,15 +527,15 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
     if workspace.numel() < need:
         raise RaError(int(_lib.RA_ERR_WORKSPACE), "ra_ring_bwd")
-    cs = copy_stream_for(q.device) if copy_stream == "auto" else copy_stream
+    dev = _one_device(q, k_all, v_all, o, dout, lse, dq, dk, dv, workspace, *(docs or ()))
     args = (ctypes.byref(p), q_shard, _ptr(q), _ptr(k_all), _ptr(v_all), _ptr(o), _ptr(dout), _ptr(lse),
-            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream),
-            ctypes.c_void_p(cs.cuda_stream) if cs is not None else None)
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), _stream(stream, dev),
+            _copy_stream_arg(copy_stream, dev))
     if not timed:
-        check(_lib.lib().ra_ring_bwd(*args), "ra_ring_bwd")
+        _run(dev, "ra_ring_bwd", *args)
         return dq, dk, dv
     tm = RaRingTiming()
-    check(_lib.lib().ra_ring_bwd_timed(*args, ctypes.byref(tm)), "ra_ring_bwd_timed")
+    _run(dev, "ra_ring_bwd_timed", *args, ctypes.byref(tm))
     n = tm.n_steps
     return dq, dk, dv, {"step_begin_ms": list(tm.step_begin_ms[:n]), "step_end_ms": list(tm.step_end_ms[:n]),
                         "copy_begin_ms": list(tm.copy_begin_ms[:n]), "copy_end_ms": list(tm.copy_end_ms[:n]),
@@ -551,12 +577,10 @@ def ring_bwd_kv_stationary(k, v, q_all, dout_all, lse_all, delta_all, *, kv_shar
     _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
     if workspace.numel() < need:
         raise RaError(int(_lib.RA_ERR_WORKSPACE), "ra_ring_bwd_kv_stationary")
-    cs = copy_stream_for(q_all.device) if copy_stream == "auto" else copy_stream
-    check(_lib.lib().ra_ring_bwd_kv_stationary(
-        ctypes.byref(p), kv_shard, _ptr(k), _ptr(v), _ptr(q_all), _ptr(dout_all), _ptr(lse_all),
-        _ptr(delta_all), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-        _stream(stream), ctypes.c_void_p(cs.cuda_stream) if cs is not None else None),
-        "ra_ring_bwd_kv_stationary")
+    dev = _one_device(k, v, q_all, dout_all, lse_all, delta_all, dq, dk, dv, workspace)
+    _run(dev, "ra_ring_bwd_kv_stationary", ctypes.byref(p), kv_shard, _ptr(k), _ptr(v), _ptr(q_all),
+         _ptr(dout_all), _ptr(lse_all), _ptr(delta_all), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+         _nbytes(workspace), _stream(stream, dev), _copy_stream_arg(copy_stream, dev))
     return dq, dk, dv
 
 

@@ -128,6 +128,19 @@ def test_ring_fwd_rejects_small_workspace():
                            bneed_f, None, None) == _lib.RA_ERR_INVALID_ARG
 
 
+def test_binding_pointer_and_device_checks():
+    """The binding's last gate before a library call: only GPU tensors become pointers, and
+    the tensors of one call must share one GPU."""
+    import torch
+
+    import ring_attention_long_amd as ra
+    with pytest.raises(ValueError):
+        ra._ptr(torch.zeros(4))
+    with pytest.raises(ValueError):
+        ra._one_device(torch.zeros(1), None)
+    assert ra._nbytes(torch.zeros(3, dtype=torch.float32)) == 12
+
+
 def test_ring_fwd_rejects_ring_above_limit():
     """N above the driver's limit (128) is refused before anything else, on the one-launch-
     per-step and the batched path alike (both keep per-step events in fixed arrays)."""

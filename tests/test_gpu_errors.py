@@ -85,3 +85,29 @@ def test_rejected_calls_write_nothing():
                                          _p(lse_all2), _p(dl_all), _p(dq_all), _p(dk), _p(dv), _p(sws), need - 1,
                                          s, None) == _lib.RA_ERR_WORKSPACE
     assert _unchanged(dq_all, dk, dv)
+
+
+def test_binding_refuses_host_and_strided_buffers():
+    """The binding hands the library only contiguous GPU tensors of one device: a workspace in
+    host memory or a strided output is refused before any call (the kernels would fault on
+    such addresses), and a workspace of another element type is sized in bytes."""
+    b, L, h, n_kv, d, N = 1, 128, 8, 4, 128, 4
+    q = torch.randn((b, L, h, d), device="cuda", dtype=torch.bfloat16)
+    k_all = torch.randn((N, b, L, n_kv, d), device="cuda", dtype=torch.bfloat16)
+    v_all = torch.randn_like(k_all)
+    kw = dict(q_shard=1, causal=True, layout="striped")
+    need = ra.ring_workspace_bytes(q, k_all, causal=True, layout="striped")
+    announce("binding: host workspace, strided output, fp32 workspace")
+    o_host_ws = _filled((b, L, h, d), torch.bfloat16)
+    with pytest.raises(ValueError):
+        ra.ring_fwd(q, k_all, v_all, **kw, workspace=torch.empty(need, dtype=torch.uint8), out=o_host_ws)
+    assert _unchanged(o_host_ws)
+    o_strided = _filled((b, h, L, d), torch.bfloat16).transpose(1, 2)
+    with pytest.raises(ValueError):
+        ra.ring_fwd(q, k_all, v_all, **kw, out=o_strided)
+    assert _unchanged(o_strided)
+    o_ref, l_ref = ra.ring_fwd(q, k_all, v_all, **kw)
+    ws32 = torch.empty((need + 3) // 4, device="cuda", dtype=torch.float32)
+    o32, l32 = ra.ring_fwd(q, k_all, v_all, **kw, workspace=ws32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ref, o32) and torch.equal(l_ref, l32)
