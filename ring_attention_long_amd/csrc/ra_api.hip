@@ -959,6 +959,11 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     if ((e = ev.make(&consumed[k], false)) != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
   bool live[kMaxRing];
+  int dq_first = -1;                          // the first live step: it stores dQ, later ones add
+  for (int k = 0; k < N; ++k) {
+    live[k] = step_is_live(p, qs, ((qs - k) % N + N) % N);
+    if (live[k] && dq_first < 0) dq_first = k;
+  }
   if (timing) {
     tm->n_steps = N;
     for (int k = 0; k < N; ++k) {
@@ -969,13 +974,19 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
         return hip_fail(e, "hipEventCreate");
     }
   }
-  // zero the gradient outputs, then D = rowsum(dO * O)
-  const int64_t n_q = (int64_t)p->b * p->L * p->h * p->d;
-  if ((e = ra::launch_fill_lse(dq, n_q, 0.f, cs)) != hipSuccess) return hip_fail(e, "fill kernel launch");
-  if ((e = ra::launch_fill_lse(dk_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
+  // The gradient outputs are written, not accumulated into: each KV shard gets the
+  // contributions of exactly one ring step, whose launch stores dK and dV (zeros for keys no
+  // query sees), and the first live step stores dQ; only what no launch stores is zero-filled
+  // (the shards of dead steps, dQ if no step is live).  Then D = rowsum(dO * O).
+  if (dq_first < 0 && (e = ra::launch_fill_lse(dq, (int64_t)p->b * p->L * p->h * p->d, 0.f, cs)) != hipSuccess)
     return hip_fail(e, "fill kernel launch");
-  if ((e = ra::launch_fill_lse(dv_all, (int64_t)shard_elems * N, 0.f, cs)) != hipSuccess)
-    return hip_fail(e, "fill kernel launch");
+  for (int k = 0; k < N; ++k) {
+    if (live[k]) continue;
+    const size_t src = (size_t)(((qs - k) % N + N) % N);
+    if ((e = ra::launch_fill_lse(dk_all + src * shard_elems, (int64_t)shard_elems, 0.f, cs)) != hipSuccess ||
+        (e = ra::launch_fill_lse(dv_all + src * shard_elems, (int64_t)shard_elems, 0.f, cs)) != hipSuccess)
+      return hip_fail(e, "fill kernel launch");
+  }
   if ((e = ra::launch_bwd_preprocess(o, dout, delta, p->b, p->L, p->h, cs)) != hipSuccess)
     return hip_fail(e, "preprocess kernel launch");
   if ((e = hipEventRecord(entry, cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -999,12 +1010,11 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
     const int src = ((qs - k) % N + N) % N;
     const void* kp = k == 0 ? (const void*)(kc + (size_t)qs * shard_bytes) : (const void*)kbuf[k & 1];
     const void* vp = k == 0 ? (const void*)(vc + (size_t)qs * shard_bytes) : (const void*)vbuf[k & 1];
-    live[k] = step_is_live(p, qs, src);
     if (live[k]) {
       if (timing && (e = hipEventRecord(t_sb[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
       const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, nullptr, nullptr);
       if ((e = ra::launch_step_bwd_bf16(a, dout, lse, delta, dq, dk_all + (size_t)src * shard_elems,
-                                        dv_all + (size_t)src * shard_elems, cs)) != hipSuccess)
+                                        dv_all + (size_t)src * shard_elems, cs, k == dq_first, true)) != hipSuccess)
         return hip_fail(e, "backward step kernel launch");
       if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }

@@ -348,8 +348,11 @@ hipError_t launch_ulysses_scatter_rows(void* dst_all, const float* src, int b, i
                                        int Hg, int head0, int d, int dtype, hipStream_t s);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
                                  hipStream_t s);
-// Adds this step's contributions: dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32).
+// Adds this step's contributions to dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32), or,
+// with set_dq / set_dkdv, stores them there in place of what the buffer held (every row of
+// the shard is written, zeros where the step contributes nothing).
 hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float* lse,
-                                const float* delta, float* dq, float* dk, float* dv, hipStream_t s);
+                                const float* delta, float* dq, float* dk, float* dv, hipStream_t s,
+                                bool set_dq = false, bool set_dkdv = false);
 
 }  // namespace ra

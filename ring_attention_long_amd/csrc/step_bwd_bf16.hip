@@ -155,7 +155,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ delta,
                                                                  float* __restrict__ dk, float* __restrict__ dv,
-                                                                 KvForm kf) {
+                                                                 KvForm kf, int set_out) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   // Per row of a staged tile, one more 16-wide k-step for the products S = Q K^T and
   // dP = dO V^T: columns 0 and 1 hold the bf16 pair (hi, lo) of -LSE / scale (S) or -D (dP),
@@ -212,7 +212,20 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     if (range(mid).lo >= u0 + KB) t_top = mid;
     else t_stop = mid + 1;
   }
-  if (t_lo >= t_stop) return;               // no query of this step sees these keys
+  if (t_lo >= t_stop) {                     // no query of this step sees these keys
+    if (set_out && grp == 0 && u < L) {     // their gradients are zero
+      float* kz = dk + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
+      float* vz = dv + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          *(f32x4*)(kz + 32 * e + 8 * ib) = f32x4{};
+          *(f32x4*)(vz + 32 * e + 8 * ib) = f32x4{};
+        }
+    }
+    return;
+  }
   const int qt_first = t_lo / TILE_ROWS;
   const int t_end = (t_stop + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
   const int n_iter = (t_end / TILE_ROWS - qt_first) * G;   // (head, query tile) pairs
@@ -598,7 +611,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
       const f32x4 ov = red[((1 * 4 + e) * 4 + ib) * 64 + lane];
       f32x4* pk = (f32x4*)(krow_out + 32 * e + 8 * ib);
       f32x4* pv = (f32x4*)(vrow_out + 32 * e + 8 * ib);
-      f32x4 vk = *pk, vv = *pv;
+      f32x4 vk = {}, vv = {};
+      if (!set_out) {
+        vk = *pk;
+        vv = *pv;
+      }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         vk[x] += a.scale * (dka[e][4 * ib + x] + ok[x]);
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ delta,
                                                                float* __restrict__ dq, int heads_per_wg,
-                                                               int n_qb, int inner_count) {
+                                                               int n_qb, int inner_count, int set_out) {
   __shared__ __attribute__((aligned(1024))) char k_lds[K_STAGES][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds[V_STAGES][TILE_BYTES];
   const int tid = threadIdx.x;
@@ -681,7 +698,16 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
   full_end = __builtin_amdgcn_readfirstlane(full_end);
   j_begin = __builtin_amdgcn_readfirstlane(j_begin);
   n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
-  if (n_tiles <= j_begin) return;   // uniform over the workgroup: no key of this step is allowed
+  if (n_tiles <= j_begin) {   // uniform over the workgroup: no key of this step is allowed
+    if (set_out && t < L) {    // the rows' gradients are zero
+      float* zr = dq + (((int64_t)bi * L + t) * a.h + hq) * D + 4 * lg;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) *(f32x4*)(zr + 32 * e + 8 * ib) = f32x4{};
+    }
+    return;
+  }
 
   // resident operands: Q^T and dO^T of this lane's query, one row per lane
   const int64_t qrow = (((int64_t)bi * L + tc) * a.h + hq) * D + lg * 8;
@@ -852,7 +878,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       f32x4* p = (f32x4*)(row + 32 * e + 8 * ib);
-      f32x4 v = *p;
+      f32x4 v = {};
+      if (!set_out) v = *p;
 #pragma unroll
       for (int x = 0; x < 4; ++x) v[x] += a.scale * acc[e][4 * ib + x];
       *p = v;
@@ -871,7 +898,8 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 }
 
 hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float* lse,
-                                const float* delta, float* dq, float* dk, float* dv, hipStream_t s) {
+                                const float* delta, float* dq, float* dk, float* dv, hipStream_t s,
+                                bool set_dq, bool set_dkdv) {
   const int G = a.h / a.n_kv;
   const int Hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
   const int PB = 8 / Hw;
@@ -882,12 +910,12 @@ hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float
   const int64_t grid_k = (int64_t)n_kb * a.n_kv * a.b;
   if (grid_q > 0x7fffffff || grid_k > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid_q), dim3(DQ_THREADS), 0, s, a,
-                     (const __bf16*)dout, lse, delta, dq, Hw, n_qb, inner);
+                     (const __bf16*)dout, lse, delta, dq, Hw, n_qb, inner, (int)set_dq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const KvForm kf = make_kv_form(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_k), dim3(KV_THREADS), 0, s, a,
-                     (const __bf16*)dout, lse, delta, dk, dv, kf);
+                     (const __bf16*)dout, lse, delta, dk, dv, kf, (int)set_dkdv);
   return hipGetLastError();
 }
 
