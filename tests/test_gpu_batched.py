@@ -116,6 +116,24 @@ def test_batched_default_long_steps_four_per_launch():
     assert torch.equal(o0, o4) and torch.equal(l0, l4)
 
 
+@pytest.mark.parametrize("N", [16, 32])
+def test_batched_large_ring_one_launch(N):
+    """Rings larger than the measured N = 8: short steps put all N - 1 remote shards in one
+    launch (each workgroup walks up to 31 KV shards with its state on chip)."""
+    cfg = dict(b=1, L=96, h=4, n_kv=2, d=128, N=N)
+    for layout, causal, shard in (("striped", True, N - 1), ("zigzag", True, N // 2), ("contiguous", False, 3),
+                                  ("contiguous", True, N - 2)):
+        announce("large ring", N, layout, causal, "shard", shard)
+        inp = make_inputs(**cfg, q_shard=shard, seed=1470 + N + shard, dtype="bf16")
+        q, k_all, v_all = _tensors(inp)
+        o, lse, tm = ra.ring_fwd_timed(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+        torch.cuda.synchronize()
+        live = [x for x in tm["launch_steps"] if x > 0]
+        assert tm["launch_steps"][0] == 1 and len(live) <= 2 and sum(tm["launch_steps"]) <= N
+        O, LSE = oracle_ring(inp, N=N, shard=shard, layout=layout, causal=causal)
+        check_bf16(o, lse, O, LSE, f"N={N} {layout} causal={causal} shard {shard}")
+
+
 def test_batched_contiguous_dead_groups():
     """Contiguous causal, shard 1 of 6 with 2 steps per launch: the group (1, 2) holds the one
     live remote step, the groups (3, 4) and (5) none, so the group (1, 2) writes the output
