@@ -217,3 +217,23 @@ def test_ring_bwd_timed_matches_untimed():
         assert 0 <= tm["step_begin_ms"][k] < tm["step_end_ms"][k] <= tm["total_ms"]
         if k >= 1:
             assert tm["copy_end_ms"][k] <= tm["step_begin_ms"][k] + 1e-3
+
+
+def test_ring_bwd_overwrites_every_output_element():
+    """ra_ring_bwd writes dq and every shard's dk, dv whatever they held: outputs filled with
+    NaN come back equal to a pass into fresh buffers.  Cases: contiguous causal (dead steps,
+    whose shards are filled with zeros; shard 0 has one live step), striped and zigzag causal
+    (workgroups whose keys no query of the step sees store zeros), a ragged L, GQA 3."""
+    cfg = dict(b=2, L=150, h=6, n_kv=2, d=128, N=4)
+    for layout in ("contiguous", "striped", "zigzag"):
+        for shard in (0, 3):
+            announce("ring_bwd outputs overwritten", layout, "shard", shard)
+            inp = make_inputs(**cfg, q_shard=shard, seed=171 + shard, dtype="bf16", with_dout=True)
+            q, k_all, v_all, dout = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all", "dout"))
+            o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=True, layout=layout)
+            ref = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=True, layout=layout)
+            nan = tuple(torch.full_like(t, float("nan")) for t in ref)
+            got = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=True, layout=layout, out=nan)
+            torch.cuda.synchronize()
+            for a, b in zip(ref, got):
+                assert torch.equal(a, b)
