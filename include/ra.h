@@ -144,17 +144,18 @@ ra_status ra_finalize(const ra_problem* p, const float* o_acc, void* o, ra_strea
  * batched into launches (p->steps_per_launch >= 2, or 0 for a bf16 ring of N >= 3): a K/V
  * slot for each of the N - 1 remote shards and the fp32 output accumulator [b][L][h][d].
  * With one launch per step: two KV staging buffers (the double buffer of page 1, "Practical
- * Implementation Patterns"); unless dtype is fp32, the fp32 output accumulator; and, for
- * bf16 without packed documents and L <= 4096, a second fp32 accumulator [b][L][h][d] with
- * its LSE [b][h][L].  Given less than the batched size, the library's choice (0) runs one
- * launch per step.  With
- * the second accumulator the steps of short shards may run the key range of a heavy query
- * block as two workgroups, one merging into each accumulator, and the pass folds the two
- * together at the end (page 2, "FlashAttention Integration": partials over disjoint key
- * sets merge by their LSE); this evens out the causal imbalance between query blocks and
- * fills the chip when a step has few blocks.  A workspace without the second accumulator is
- * accepted too: the pass then runs every block whole (the same result up to the order of
- * the fp32 sums).  Returns 0 if p is invalid. */
+ * Implementation Patterns") and, unless dtype is fp32, the fp32 output accumulator.  Either
+ * way, for bf16 without packed documents and L <= 4096, then a second fp32 accumulator
+ * [b][L][h][d] with its LSE [b][h][L].  Given less than the batched size (without the
+ * second accumulator), the library's choice (0) runs one launch per step.  With the second
+ * accumulator the launches of short shards may run the key range of a heavy query block as
+ * two workgroups (in a batched launch, each of its KV shards' ranges in two halves), one
+ * merging into each accumulator, and the pass folds the two together at the end (page 2,
+ * "FlashAttention Integration": partials over disjoint key sets merge by their LSE); this
+ * evens out the causal imbalance between query blocks and fills the chip when a launch has
+ * few blocks.  A workspace without the second accumulator is accepted too: the pass then
+ * runs every block whole (the same result up to the order of the fp32 sums).  Returns 0 if
+ * p is invalid. */
 size_t ra_ring_fwd_workspace(const ra_problem* p);
 
 /* ra_fwd_step_plan — how one bf16 forward step of a pass with the second accumulator
@@ -227,7 +228,8 @@ ra_status ra_ring_fwd_timed(const ra_problem* p, int32_t q_shard, const void* q,
  * that is 4 b L n_kv d 2 + 4 b L h d bytes plus alignment: L = 2048 with h = 32, n_kv = 8,
  * d = 128 fits), or when steps_per_launch >= 2 asks for slots that do not fit.  Under the
  * library's choice the batched steps run when their slots fit (L = 2048 with h = 32,
- * n_kv = 8, N = 4; L = 1024 with N = 8), else with one launch per step the second
+ * n_kv = 8, N = 4; L = 1024 with N = 8), with the second accumulator behind them when that
+ * fits too (L = 1024 with h = 32, n_kv = 8, N = 8), else with one launch per step the second
  * accumulator when it fits (L = 2048 with h = 16, n_kv = 8); the results equal ra_ring_fwd's
  * with a workspace of RA_NOALLOC_SCRATCH_BYTES.  Every call on one device shares that device's array and events, and the array
  * keeps the last call's contents (each pass overwrites everything it reads, so nothing

@@ -276,9 +276,13 @@ hipError_t stage_kv(char* kdst, char* vdst, const void* k_all, const void* v_all
 // then the remaining steps, m at a time, each launch after the copies of its shards.  The
 // last launch with a live step writes the bf16 output.  Arguments as ring_fwd_impl's, checked;
 // tm: per-launch and per-copy timings (N <= RA_MAX_TIMED_STEPS), or null.
+// With (o2, lse2), the second accumulator (short shards whose launches leave compute units
+// idle): step 0 and the batched launches may split the key ranges of their query blocks over
+// two workgroups, the second merging into (o2, lse2), and the pass ends by folding it into
+// the output instead of the last launch writing it.
 ra_status ring_fwd_batched(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                            const void* v_all, void* o, float* lse, void* ws, hipStream_t cs, hipStream_t ps,
-                           const RingEvents* pre, int m, ra_ring_timing* tm) {
+                           const RingEvents* pre, int m, ra_ring_timing* tm, float* o2, float* lse2) {
   const int N = p->N;
   const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
   const size_t A = align_up(shard_bytes, 256);
@@ -366,11 +370,15 @@ ra_status ring_fwd_batched(const ra_problem* p, int32_t qs, const void* q, const
     if (timing && (e = hipEventRecord(t_sb[k0], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (k0 == 0) {
       a = step_args(p, qs, qs, q, kc + (size_t)qs * shard_bytes, vc + (size_t)qs * shard_bytes, o_acc, lse);
-      if (last) a.o_out = (__bf16*)o;
+      a.o2 = o2;
+      a.lse2 = lse2;
+      if (last && !o2) a.o_out = (__bf16*)o;
       if ((e = ra::launch_step_bf16(a, ra::MODE_PART, cs)) != hipSuccess) return hip_fail(e, "step kernel launch");
     } else {
       a = step_args(p, qs, qs, q, nullptr, nullptr, o_acc, lse);
-      if (last) a.o_out = (__bf16*)o;
+      a.o2 = o2;
+      a.lse2 = lse2;
+      if (last && !o2) a.o_out = (__bf16*)o;
       ra::ShardBatch sb;
       sb.k = kslot + (size_t)(k0 - 1) * A;
       sb.v = vslot + (size_t)(k0 - 1) * A;
@@ -393,6 +401,8 @@ ra_status ring_fwd_batched(const ra_problem* p, int32_t qs, const void* q, const
     }
     if (k0 == 0) RA_TRY(stage_all());
   }
+  if (o2 && (e = ra::launch_fold_second(o_acc, lse, o2, lse2, o, p->b, p->L, p->h, p->d, cs)) != hipSuccess)
+    return hip_fail(e, "fold kernel launch");
   // Work the caller queues on `compute` after this call must not overtake the copy stream,
   // which still writes the workspace when the last live group ends before the last copy (or
   // when poisoning): join it back.
@@ -421,6 +431,24 @@ ra_status ring_fwd_batched(const ra_problem* p, int32_t qs, const void* q, const
   return RA_OK;
 }
 
+// Whether any launch of a batched pass (step 0, then live groups of m ring steps) would split a
+// query block, given a second accumulator.
+bool batched_splits(const ra_problem* p, int32_t qs, int m) {
+  const int N = p->N;
+  if (ra::step_splits_bf16(step_args(p, qs, qs, nullptr, nullptr, nullptr, nullptr, nullptr))) return true;
+  for (int k = 1; k < N; k += m) {
+    const int k1 = k + m < N ? k + m : N;
+    bool live = false;
+    for (int j = k; j < k1; ++j) live = live || step_is_live(p, qs, ((qs - j) % N + N) % N);
+    if (!live) continue;
+    ra::ShardBatch sb;
+    sb.k_first = k;
+    sb.n = k1 - k;
+    if (ra::steps_split_bf16(step_args(p, qs, qs, nullptr, nullptr, nullptr, nullptr, nullptr), sb)) return true;
+  }
+  return false;
+}
+
 ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all,
                         const void* v_all, void* o, float* lse, void* ws, size_t ws_bytes,
                         ra_stream compute, ra_stream copy, ra_ring_timing* tm,
@@ -446,9 +474,16 @@ ra_status ring_fwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   if (m >= 2) {
     if (tm && p->N > RA_MAX_TIMED_STEPS)
       return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
-    if (ws_bytes >= batch_workspace(p))
+    if (ws_bytes >= batch_workspace(p)) {
+      float* o2 = nullptr;
+      float* lse2 = nullptr;
+      if (fwd_split(p) && ws_bytes >= batch_workspace(p) + second_acc_bytes(p) && batched_splits(p, qs, m)) {
+        o2 = (float*)((char*)ws + batch_workspace(p));
+        lse2 = (float*)((char*)o2 + second_o_bytes(p));
+      }
       return ring_fwd_batched(p, qs, q, k_all, v_all, o, lse, ws, (hipStream_t)compute,
-                              copy ? (hipStream_t)copy : (hipStream_t)compute, pre, m, tm);
+                              copy ? (hipStream_t)copy : (hipStream_t)compute, pre, m, tm, o2, lse2);
+    }
     if (p->steps_per_launch != 0)   // asked for explicitly: the workspace must hold the slots
       return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed for %d steps per launch", ws_bytes,
                   batch_workspace(p), m);
@@ -1177,7 +1212,7 @@ ra_status ra_fwd_step_plan(const ra_problem* p, int32_t q_shard, int32_t kv_shar
 
 size_t ra_ring_fwd_workspace(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
-  return fwd_steps_per_launch(p) >= 2 ? batch_workspace(p) : ring_fwd_base_workspace(p) + second_acc_bytes(p);
+  return (fwd_steps_per_launch(p) >= 2 ? batch_workspace(p) : ring_fwd_base_workspace(p)) + second_acc_bytes(p);
 }
 
 ra_status ra_ring_fwd(const ra_problem* p, int32_t q_shard, const void* q, const void* k_all,

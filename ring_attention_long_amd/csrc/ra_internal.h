@@ -303,9 +303,15 @@ struct StepGeometry {
 };
 StepGeometry step_geometry_bf16(const StepArgs& a);
 SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu);
+// The same for a launch of several ring steps (launch_steps_bf16 with a second accumulator):
+// a split block runs each of its KV shards' key ranges as two halves, one per part.
+SplitPlan plan_split_batch(const StepArgs& a, const ShardBatch& sb, const StepGeometry& g, int n_cu);
 // Whether launch_step_bf16 would split any query block of this step (given a second
 // accumulator) on the current device.
 bool step_splits_bf16(const StepArgs& a);
+// Whether launch_steps_bf16 would split any query block of this batch (given a second
+// accumulator) on the current device.
+bool steps_split_bf16(const StepArgs& a, const ShardBatch& sb);
 
 // Largest shard length for which a forward pass keeps a second accumulator, so that its steps
 // can split the key ranges of their heaviest query blocks (below it a step has too few

@@ -672,24 +672,18 @@ StepGeometry step_geometry_bf16(const StepArgs& a) {
 // longest item shrinks by a tenth.  The host knows every block's tile count from the scalar
 // key limit (not with packed documents, whose bounds live on the device).  Items go out
 // heaviest first (ties: unsplit blocks first).
-SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
+// The plan from each block's cost in tiles: w[qb] tiles whole, wp[qb] tiles for the longer of
+// its two parts.
+SplitPlan plan_from_costs(const int* w, const int* wp, int n_qb, int units) {
   SplitPlan pl{};
-  const int n_qb = g.n_qb;
   pl.split_from = n_qb;
-  if (a.doc_begin || n_qb < 1 || n_qb > kSplitMaxBlocks || n_cu < 1) return pl;
-  const int units = n_cu / g.inner;     // units per copy of the item list
   if (n_qb >= units) return pl;         // the grid fills the chip already
   constexpr int FIXED = 3;              // per-workgroup cost in tile times (Q load, pipeline fill, epilogue)
-  int w[kSplitMaxBlocks];
-  for (int qb = 0; qb < n_qb; ++qb) {
-    const int last = min((qb + 1) * g.rows_wg, a.L) - 1;
-    w[qb] = (kv_limit(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard, last) + BN_SHORT - 1) / BN_SHORT;
-  }
   int pre_max[kSplitMaxBlocks + 1], suf_max[kSplitMaxBlocks + 1];
   pre_max[0] = 0;
   for (int qb = 0; qb < n_qb; ++qb) pre_max[qb + 1] = max(pre_max[qb], w[qb] + FIXED);
   suf_max[n_qb] = 0;
-  for (int qb = n_qb - 1; qb >= 0; --qb) suf_max[qb] = max(suf_max[qb + 1], (w[qb] + 1) / 2 + FIXED);
+  for (int qb = n_qb - 1; qb >= 0; --qb) suf_max[qb] = max(suf_max[qb + 1], wp[qb] + FIXED);
   const int none = pre_max[n_qb];
   int best = n_qb, best_len = none;
   for (int s = n_qb - 1; s >= max(0, 2 * n_qb - units); --s) {   // s + 2 (n_qb - s) items <= units
@@ -706,7 +700,7 @@ SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
   const int n_parts = 2 * (n_qb - best);
   while (u >= 0 || m < n_parts) {
     const int cu = u >= 0 ? w[u] + FIXED : -1;
-    const int cp = m < n_parts ? (w[n_qb - 1 - m / 2] + 1) / 2 + FIXED : -1;
+    const int cp = m < n_parts ? wp[n_qb - 1 - m / 2] + FIXED : -1;
     if (cu >= cp) {
       pl.order[item >> 5] |= 1u << (item & 31);
       --u;
@@ -717,6 +711,43 @@ SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
   }
   pl.split_from = best;
   return pl;
+}
+
+// Tiles of block qb in KV shard ks (no packed documents: the keys of a row are a prefix).
+int block_tiles(const StepArgs& a, const StepGeometry& g, int ks, int qb) {
+  const int last = min((qb + 1) * g.rows_wg, a.L) - 1;
+  return (kv_limit(a.causal, a.layout, a.N, a.L, a.q_shard, ks, last) + BN_SHORT - 1) / BN_SHORT;
+}
+
+SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
+  SplitPlan pl{};
+  pl.split_from = g.n_qb;
+  if (a.doc_begin || g.n_qb < 1 || g.n_qb > kSplitMaxBlocks || n_cu < 1) return pl;
+  int w[kSplitMaxBlocks], wp[kSplitMaxBlocks];
+  for (int qb = 0; qb < g.n_qb; ++qb) {
+    w[qb] = block_tiles(a, g, a.kv_shard, qb);
+    wp[qb] = (w[qb] + 1) / 2;
+  }
+  return plan_from_costs(w, wp, g.n_qb, n_cu / g.inner);
+}
+
+// A launch of several ring steps splits a block's key range in every one of its KV shards: a
+// part's cost is the sum of its halves (the first part takes the odd tile).
+SplitPlan plan_split_batch(const StepArgs& a, const ShardBatch& sb, const StepGeometry& g, int n_cu) {
+  SplitPlan pl{};
+  pl.split_from = g.n_qb;
+  if (a.doc_begin || g.n_qb < 1 || g.n_qb > kSplitMaxBlocks || n_cu < 1 || sb.n < 1) return pl;
+  int w[kSplitMaxBlocks], wp[kSplitMaxBlocks];
+  for (int qb = 0; qb < g.n_qb; ++qb) {
+    w[qb] = wp[qb] = 0;
+    for (int s = 0; s < sb.n; ++s) {
+      const int ks = ((a.q_shard - (sb.k_first + s)) % a.N + a.N) % a.N;
+      const int t = block_tiles(a, g, ks, qb);
+      w[qb] += t;
+      wp[qb] += (t + 1) / 2;
+    }
+  }
+  return plan_from_costs(w, wp, g.n_qb, n_cu / g.inner);
 }
 
 bool step_splits_bf16(const StepArgs& a) {
@@ -761,12 +792,19 @@ hipError_t launch_step_bf16(const StepArgs& a, int mode, hipStream_t stream) {
 }
 
 hipError_t launch_steps_bf16(const StepArgs& a, const ShardBatch& sb, int mode, hipStream_t stream) {
-  // no split of key ranges across workgroups here: every query block runs whole
-  if (a.o2 || a.lse2 || sb.n < 1 || sb.n > kMaxBatch || !sb.k || !sb.v) return hipErrorInvalidValue;
+  if (sb.n < 1 || sb.n > kMaxBatch || !sb.k || !sb.v || !a.o2 != !a.lse2) return hipErrorInvalidValue;
+  if (a.o_out && a.o2) return hipErrorInvalidValue;   // a split pass ends with the fold instead
+  if (a.o2 && mode != MODE_MERGE) return hipErrorInvalidValue;   // the parts merge into (o2, lse2)
   const StepGeometry g = step_geometry_bf16(a);
   SplitPlan plan{};
   plan.split_from = g.n_qb;
+  if (a.o2) plan = plan_split_batch(a, sb, g, cu_count());
   return launch_fwd<true>(a, sb, plan, g, mode, stream);
+}
+
+bool steps_split_bf16(const StepArgs& a, const ShardBatch& sb) {
+  const StepGeometry g = step_geometry_bf16(a);
+  return plan_split_batch(a, sb, g, cu_count()).split_from < g.n_qb;
 }
 
 }  // namespace ra

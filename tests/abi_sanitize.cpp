@@ -71,7 +71,10 @@ int main() {
   expect(ra_finalize(&p, Ff, nullptr, nullptr) == RA_ERR_INVALID_ARG, "finalize null o");
   const size_t ws = ra_ring_fwd_workspace(&p);
   expect(ws > second_acc(p.b, p.L, p.h, p.d), "ring_fwd_workspace");
-  const size_t ws_min = ws - second_acc(p.b, p.L, p.h, p.d);
+  ra_problem p1 = p;   // the smallest workspace: one launch per step, no second accumulator
+  p1.steps_per_launch = 1;
+  const size_t ws_min = ra_ring_fwd_workspace(&p1) - second_acc(p.b, p.L, p.h, p.d);
+  expect(ws_min < ws, "ring_fwd minimum workspace");
   expect(ra_ring_fwd(&p, 0, F, F, F, F, Ff, F, ws_min - 1, nullptr, nullptr) == RA_ERR_WORKSPACE, "ring_fwd workspace");
   ra_ring_timing tm;
   expect(ra_ring_fwd_timed(&p, 0, F, F, F, F, Ff, F, ws_min - 1, nullptr, nullptr, &tm) == RA_ERR_WORKSPACE,

@@ -106,11 +106,12 @@ def test_ring_fwd_rejects_small_workspace():
     assert st == _lib.RA_ERR_WORKSPACE
     assert lib.ra_ring_fwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                                  None, None, None) == _lib.RA_ERR_INVALID_ARG
-    # batched steps asked for explicitly: the slots of every remote shard are required
+    # batched steps asked for explicitly: the slots of every remote shard are required (the
+    # workspace asked for ends with the same optional second accumulator)
     pb = _prob(steps_per_launch=2)
     bneed_f = lib.ra_ring_fwd_workspace(ctypes.byref(pb))
-    assert bneed_f > need - second
-    assert lib.ra_ring_fwd(ctypes.byref(pb), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bneed_f - 1, None,
+    assert bneed_f - second > need - second
+    assert lib.ra_ring_fwd(ctypes.byref(pb), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bneed_f - second - 1, None,
                            None) == _lib.RA_ERR_WORKSPACE
     assert b"steps per launch" in lib.ra_last_error()
     # the library's choice (0) takes one launch per step when the slots do not fit, so the
@@ -202,7 +203,8 @@ def test_workspace_size_is_two_kv_buffers_plus_fp32_accumulator():
     launch per ring step: the two staging buffers (K and V each) plus the fp32 output
     accumulator of bf16 problems, and for short bf16 shards (L <= 4096) the second
     accumulator with its LSE.  With bf16 steps batched into launches (the default for N >= 3):
-    a slot for every remote shard's K and V, and the fp32 accumulator."""
+    a slot for every remote shard's K and V, the fp32 accumulator and, for short shards, the
+    same second accumulator."""
     lib = _lib.lib()
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for dtype, esz in ((1, 2), (0, 4)):
@@ -215,8 +217,8 @@ def test_workspace_size_is_two_kv_buffers_plus_fp32_accumulator():
                     want = 2 * 3 * pad(shard) + acc
                 else:
                     want = 4 * pad(shard) + acc
-                    if dtype == 1 and L <= 4096:
-                        want += pad(2 * L * 4 * 128 * 4) + pad(2 * 4 * L * 4)
+                if dtype == 1 and L <= 4096:
+                    want += pad(2 * L * 4 * 128 * 4) + pad(2 * 4 * L * 4)
                 assert lib.ra_ring_fwd_workspace(ctypes.byref(p)) == want, (dtype, L, spl)
     # N <= 2: nothing to batch
     p = _prob(N=2, L=1000)

@@ -214,3 +214,43 @@ def test_batched_long_tiles_ragged_sampled(layout, causal):
     O, LSE = oracle_ring_rows(inp, N=3, shard=1, layout=layout, causal=causal, rows=rows)
     ri = torch.from_numpy(rows).to(o.device)
     check_bf16(o[:, ri], lse[:, :, ri], O, LSE, f"batched long tiles {layout}")
+
+
+def _second_acc_bytes(cfg):
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    b, L, h, d = cfg["b"], cfg["L"], cfg["h"], cfg["d"]
+    return pad(b * L * h * d * 4) + pad(b * h * L * 4)
+
+
+@pytest.mark.parametrize("layout,causal", [("striped", True), ("contiguous", False), ("zigzag", True),
+                                           ("contiguous", True)])
+def test_batched_split_short_shards(layout, causal):
+    """Short shards whose launches leave compute units idle (2 KV heads x ceil(L / 64) query
+    blocks, far fewer workgroups than units): with the second accumulator in the workspace,
+    step 0 and the batched launch split the key ranges of query blocks over two workgroups
+    (in a batched launch, every KV shard's range of a block in two halves), the second half
+    merging into the second accumulator, and the pass ends by folding it into the output.
+    Against the oracle; against the same pass without the second accumulator in the workspace
+    (every block whole: close, and the LSE differs in its last bits, which shows the split
+    ran); and with the workspace filled with NaN beforehand (bit-identical)."""
+    cfg = dict(b=1, L=250, h=8, n_kv=2, d=128, N=6)
+    for shard in (0, 2, 5):
+        announce("batched split", layout, "causal", causal, "shard", shard, cfg)
+        inp = make_inputs(**cfg, q_shard=shard, seed=1600 + shard, dtype="bf16")
+        q, k_all, v_all = _tensors(inp)
+        full = ra.ring_workspace_bytes(q, k_all, causal=causal, layout=layout)
+        outs = {}
+        for name, nbytes, fill in (("zero", full, 0), ("nan", full, None), ("whole", full - _second_acc_bytes(cfg), 0)):
+            ws = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+            if fill is None:
+                ws.view(-1)[: nbytes // 4 * 4].view(torch.float32).fill_(float("nan"))
+            outs[name] = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws)
+        torch.cuda.synchronize()
+        O, LSE = oracle_ring(inp, N=cfg["N"], shard=shard, layout=layout, causal=causal)
+        o, lse = outs["zero"]
+        check_bf16(o, lse, O, LSE, f"batched split {layout} {causal} shard {shard}")
+        check_bf16(*outs["whole"], O, LSE, f"batched whole blocks {layout} {causal} shard {shard}")
+        assert torch.equal(o, outs["nan"][0]) and torch.equal(lse, outs["nan"][1])
+        assert _close(o, outs["whole"][0], "split vs whole blocks") <= 2e-2
+        assert float((lse - outs["whole"][1]).abs().max()) <= 1e-4
+        assert not torch.equal(lse, outs["whole"][1]), "the second accumulator was not used"

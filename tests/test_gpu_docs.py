@@ -96,20 +96,21 @@ def test_ring_fwd_packed_f32(layout):
 
 
 def test_one_document_matches_no_packing_exactly():
-    """One document over the whole window: the same kernels and tiles as no packing.  With
-    one launch per step the unpacked pass gets a workspace without the second accumulator,
-    which packed passes never keep, so that both run every query block whole; batched steps
-    never split blocks."""
+    """One document over the whole window: the same kernels and tiles as no packing.  The
+    unpacked pass gets a workspace without the second accumulator, which packed passes never
+    keep, so that both run every query block whole (with one launch per step, and with the
+    remote steps batched into one launch)."""
     cfg = dict(b=1, L=256, h=8, n_kv=2, d=128, N=4)
     inp = make_inputs(**cfg, q_shard=1, seed=91, dtype="bf16")
     q, k, v = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all"))
     docs = gpu_docs([np.array([0, 1024], dtype=np.int32)], N=4, L=256, shard=1, layout="striped")
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    ws = torch.empty(4 * pad(256 * 2 * 128 * 2) + pad(256 * 8 * 128 * 4), device="cuda", dtype=torch.uint8)
-    for spl in (1, 0):
+    shard, acc = pad(256 * 2 * 128 * 2), pad(256 * 8 * 128 * 4)
+    for spl, nbytes in ((1, 4 * shard + acc), (0, 2 * 3 * shard + acc)):
         announce("packed single document == unpacked, steps per launch", spl)
+        ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
         o1, l1 = ra.ring_fwd(q, k, v, q_shard=1, causal=True, layout="striped", steps_per_launch=spl,
-                             workspace=ws if spl == 1 else None)
+                             workspace=ws)
         o2, l2 = ra.ring_fwd(q, k, v, q_shard=1, causal=True, layout="striped", docs=docs, steps_per_launch=spl)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
