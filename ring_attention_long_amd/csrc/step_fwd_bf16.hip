@@ -54,7 +54,12 @@
 //    workgroups, dispatched round-robin over the 8 XCDs, put each KV head's tiles into
 //    one XCD's L2.
 #include <atomic>
+#include <algorithm>
+#include <functional>
+#include <mutex>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "ra_internal.h"
 
@@ -672,13 +677,83 @@ StepGeometry step_geometry_bf16(const StepArgs& a) {
 // longest item shrinks by a tenth.  The host knows every block's tile count from the scalar
 // key limit (not with packed documents, whose bounds live on the device).  Items go out
 // heaviest first (ties: unsplit blocks first).
+// Blocks [s, n_qb) split: merge the unsplit blocks (s-1 .. 0) and the parts (2 per block,
+// n_qb-1 .. s), both already in nonincreasing cost, into one nonincreasing launch order.
+SplitPlan order_items(const int* w, const int* wp, int n_qb, int s, int fixed) {
+  SplitPlan pl{};
+  int u = s - 1, m = 0, item = 0;
+  const int n_parts = 2 * (n_qb - s);
+  while (u >= 0 || m < n_parts) {
+    const int cu = u >= 0 ? w[u] + fixed : -1;
+    const int cp = m < n_parts ? wp[n_qb - 1 - m / 2] + fixed : -1;
+    if (cu >= cp) {
+      pl.order[item >> 5] |= 1u << (item & 31);
+      --u;
+    } else {
+      ++m;
+    }
+    ++item;
+  }
+  pl.split_from = s;
+  return pl;
+}
+
+// Longest load of `units` compute units that take the items in launch order, each the next
+// item when it frees up (how the hardware hands out workgroups): blocks [0, s) whole, blocks
+// [s, n_qb) as two parts, in the nonincreasing order order_items launches them.
+int list_makespan(const int* w, const int* wp, int n_qb, int s, int units, int fixed) {
+  std::priority_queue<int, std::vector<int>, std::greater<int>> load;   // free-up times
+  int u = s - 1, m = 0, longest = 0, started = 0;
+  const int n_parts = 2 * (n_qb - s);
+  while (u >= 0 || m < n_parts) {
+    const int cu = u >= 0 ? w[u] + fixed : -1;
+    const int cp = m < n_parts ? wp[n_qb - 1 - m / 2] + fixed : -1;
+    int c;
+    if (cu >= cp) {
+      c = cu;
+      --u;
+    } else {
+      c = cp;
+      ++m;
+    }
+    int t0 = 0;
+    if (started < units) {
+      ++started;
+    } else {
+      t0 = load.top();
+      load.pop();
+    }
+    load.push(t0 + c);
+    longest = max(longest, t0 + c);
+  }
+  return longest;
+}
+
 // The plan from each block's cost in tiles: w[qb] tiles whole, wp[qb] tiles for the longer of
-// its two parts.
-SplitPlan plan_from_costs(const int* w, const int* wp, int n_qb, int units) {
+// its two parts.  by_makespan: choose by the list-scheduling makespan, also when there are
+// more items than units (launches of several ring steps, whose workgroups are long next to
+// their fixed costs); otherwise only plans with at most one item per unit, by the longest item.
+SplitPlan plan_from_costs(const int* w, const int* wp, int n_qb, int units, bool by_makespan = false) {
   SplitPlan pl{};
   pl.split_from = n_qb;
-  if (n_qb >= units) return pl;         // the grid fills the chip already
   constexpr int FIXED = 3;              // per-workgroup cost in tile times (Q load, pipeline fill, epilogue)
+  if (by_makespan) {
+    // every split point by its list schedule: the shortest, fewest splits on a tie, taken if
+    // it beats no split by a tenth
+    if (units < 1) return pl;
+    const int none = list_makespan(w, wp, n_qb, n_qb, units, FIXED);
+    int best = n_qb, best_len = none;
+    for (int s = n_qb - 1; s >= 0; --s) {
+      const int len = list_makespan(w, wp, n_qb, s, units, FIXED);
+      if (len < best_len) {
+        best_len = len;
+        best = s;
+      }
+    }
+    if (best == n_qb || 10 * best_len > 9 * none) return pl;
+    return order_items(w, wp, n_qb, best, FIXED);
+  }
+  if (n_qb >= units) return pl;         // the grid fills the chip already
   int pre_max[kSplitMaxBlocks + 1], suf_max[kSplitMaxBlocks + 1];
   pre_max[0] = 0;
   for (int qb = 0; qb < n_qb; ++qb) pre_max[qb + 1] = max(pre_max[qb], w[qb] + FIXED);
@@ -694,23 +769,7 @@ SplitPlan plan_from_costs(const int* w, const int* wp, int n_qb, int units) {
     }
   }
   if (best == n_qb || 10 * best_len > 9 * none) return pl;
-  // merge the unsplit blocks (best-1 .. 0) and the parts (2 per block, n_qb-1 .. best), both
-  // already in nonincreasing cost, into one nonincreasing order
-  int u = best - 1, m = 0, item = 0;
-  const int n_parts = 2 * (n_qb - best);
-  while (u >= 0 || m < n_parts) {
-    const int cu = u >= 0 ? w[u] + FIXED : -1;
-    const int cp = m < n_parts ? wp[n_qb - 1 - m / 2] + FIXED : -1;
-    if (cu >= cp) {
-      pl.order[item >> 5] |= 1u << (item & 31);
-      --u;
-    } else {
-      ++m;
-    }
-    ++item;
-  }
-  pl.split_from = best;
-  return pl;
+  return order_items(w, wp, n_qb, best, FIXED);
 }
 
 // Tiles of block qb in KV shard ks (no packed documents: the keys of a row are a prefix).
@@ -732,11 +791,32 @@ SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu) {
 }
 
 // A launch of several ring steps splits a block's key range in every one of its KV shards: a
-// part's cost is the sum of its halves (the first part takes the odd tile).
+// part's cost is the sum of its halves (the first part takes the odd tile).  Its workgroups
+// are long next to their fixed costs, so here the plan also balances a grid that fills the
+// chip: it takes the split point whose list schedule over the units (in launch order) is
+// shortest.  Measured on MI355X, striped causal h = 32, n_kv = 8, L = 2048, N = 8 (32 blocks
+// per KV head on 32 units, the heaviest twice the mean): 0.368 -> 0.324 ms per batched pass.
 SplitPlan plan_split_batch(const StepArgs& a, const ShardBatch& sb, const StepGeometry& g, int n_cu) {
   SplitPlan pl{};
   pl.split_from = g.n_qb;
   if (a.doc_begin || g.n_qb < 1 || g.n_qb > kSplitMaxBlocks || n_cu < 1 || sb.n < 1) return pl;
+  // The search runs a list schedule per split point (up to 65 of up to 128 items), so the
+  // plans of recent batch shapes are kept: a pass asks for each launch's plan twice, and a
+  // caller's passes repeat the same shapes.
+  struct Entry {
+    int key[10];
+    SplitPlan plan;
+  };
+  static std::mutex mu;
+  static Entry cache[32];
+  static int n_cached = 0, next_slot = 0;
+  const int key[10] = {a.causal, a.layout, a.N, a.L, a.q_shard, sb.k_first, sb.n, g.rows_wg, g.n_qb,
+                       n_cu / g.inner};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cached; ++i)
+      if (std::equal(key, key + 10, cache[i].key)) return cache[i].plan;
+  }
   int w[kSplitMaxBlocks], wp[kSplitMaxBlocks];
   for (int qb = 0; qb < g.n_qb; ++qb) {
     w[qb] = wp[qb] = 0;
@@ -747,7 +827,14 @@ SplitPlan plan_split_batch(const StepArgs& a, const ShardBatch& sb, const StepGe
       wp[qb] += (t + 1) / 2;
     }
   }
-  return plan_from_costs(w, wp, g.n_qb, n_cu / g.inner);
+  pl = plan_from_costs(w, wp, g.n_qb, n_cu / g.inner, true);
+  std::lock_guard<std::mutex> lock(mu);
+  Entry& e = cache[next_slot];
+  std::copy(key, key + 10, e.key);
+  e.plan = pl;
+  next_slot = (next_slot + 1) % 32;
+  if (n_cached < 32) ++n_cached;
+  return pl;
 }
 
 bool step_splits_bf16(const StepArgs& a) {

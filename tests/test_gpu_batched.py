@@ -254,3 +254,36 @@ def test_batched_split_short_shards(layout, causal):
         assert _close(o, outs["whole"][0], "split vs whole blocks") <= 2e-2
         assert float((lse - outs["whole"][1]).abs().max()) <= 1e-4
         assert not torch.equal(lse, outs["whole"][1]), "the second accumulator was not used"
+
+
+@pytest.mark.parametrize("layout,causal", [("striped", True), ("zigzag", True)])
+def test_batched_split_more_items_than_units(layout, causal):
+    """h = 32, n_kv = 8, L = 2048, N = 8: a batched launch has as many query blocks (32 per KV
+    head) as compute units per KV head, and with a causal mask the heaviest blocks do twice
+    the mean work over the seven shards.  The plan (list schedule over the units, in launch
+    order) then splits blocks although the items outnumber the units.  Sampled rows against
+    the oracle (every 64-row tile class, both ends, the half-shard edge), the whole-block pass
+    close with an LSE that differs in its last bits (the split ran), and a NaN-filled
+    workspace bit-identical."""
+    cfg = dict(b=1, L=2048, h=32, n_kv=8, d=128, N=8)
+    shard = 3
+    announce("batched split, more items than units", layout, cfg)
+    inp = make_inputs(**cfg, q_shard=shard, seed=1700, dtype="bf16")
+    q, k_all, v_all = _tensors(inp)
+    full = ra.ring_workspace_bytes(q, k_all, causal=causal, layout=layout)
+    outs = {}
+    for name, nbytes, nan in (("split", full, False), ("nan", full, True), ("whole", full - _second_acc_bytes(cfg), False)):
+        ws = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+        if nan:
+            ws.view(-1)[: nbytes // 4 * 4].view(torch.float32).fill_(float("nan"))
+        outs[name] = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout, workspace=ws)
+    torch.cuda.synchronize()
+    o, lse = outs["split"]
+    assert torch.equal(o, outs["nan"][0]) and torch.equal(lse, outs["nan"][1])
+    assert _close(o, outs["whole"][0], "split vs whole blocks") <= 2e-2
+    assert float((lse - outs["whole"][1]).abs().max()) <= 1e-4
+    assert not torch.equal(lse, outs["whole"][1]), "the second accumulator was not used"
+    rows = full_size_rows(cfg["L"], 1701)
+    O, LSE = oracle_ring_rows(inp, N=cfg["N"], shard=shard, layout=layout, causal=causal, rows=rows)
+    idx = torch.as_tensor(rows, device="cuda")
+    check_bf16(o[:, idx], lse[:, :, idx], O, LSE, f"batched split {layout}, {rows.size} sampled rows")
