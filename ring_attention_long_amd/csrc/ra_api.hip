@@ -164,13 +164,17 @@ hipError_t poison_after(void* buf, size_t bytes, hipEvent_t consumed, hipStream_
 
 // Event set of one ring pass; destroyed on every exit path.
 struct Events {
-  hipEvent_t e[2 + 2 * kMaxRing + 4 * RA_MAX_TIMED_STEPS] = {};
+  // a pass makes at most entry, done, staged and consumed per step, four timing events per
+  // step (timed passes have N <= RA_MAX_TIMED_STEPS); a full set is an error, not an overrun
+  static constexpr int kCap = 2 + 2 * kMaxRing + 4 * RA_MAX_TIMED_STEPS;
+  hipEvent_t e[kCap] = {};
   int n = 0;
   ~Events() {
     for (int i = 0; i < n; ++i)
       if (e[i]) (void)hipEventDestroy(e[i]);
   }
   hipError_t make(hipEvent_t* out, bool timing) {
+    if (n >= kCap) return hipErrorOutOfMemory;
     hipEvent_t ev = nullptr;
     const hipError_t r = hipEventCreateWithFlags(&ev, timing ? hipEventDefault : hipEventDisableTiming);
     if (r == hipSuccess) {
