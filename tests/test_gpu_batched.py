@@ -12,7 +12,8 @@ order of fp32 sums and in where the merges happen) and the timed pass with the u
 launch; contiguous causal shards whose later groups hold no live step (their copies still
 run); ragged L; several batch rows; 4, 1 and 3 query heads per KV head; packed documents
 (workgroups without any key in a whole batch); large logits (rescaling across shard
-boundaries); 96-key tiles."""
+boundaries); 96-key tiles; short shards whose launches split query blocks over two
+workgroups through the second accumulator (fewer and more work items than compute units)."""
 import numpy as np
 import pytest
 import torch
