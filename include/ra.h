@@ -263,9 +263,18 @@ ra_status ra_step_bwd(const ra_problem* p, int32_t q_shard, int32_t kv_shard, co
                       const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
                       ra_stream stream);
 
-/* Bytes of device workspace ra_ring_bwd needs: two KV staging buffers plus delta.
- * Returns 0 if p is invalid. */
+/* Bytes of device workspace ra_ring_bwd asks for: two KV staging buffers and delta
+ * (ra_ring_bwd_workspace_min), then, for shards of L <= 4096 without packed documents, second
+ * dK and dV buffers (2 x fp32 [b][L][n_kv][d]).  With them the dK/dV kernel of a step may run
+ * the query tiles of a key block as two workgroups when the key blocks leave compute units
+ * idle, the second half's sums added in after the kernel; with a workspace of the minimum size
+ * every key block runs whole (the same gradients up to the order of the fp32 sums).  Returns 0
+ * if p is invalid. */
 size_t ra_ring_bwd_workspace(const ra_problem* p);
+
+/* Smallest workspace ra_ring_bwd accepts: two KV staging buffers plus delta (see
+ * ra_ring_bwd_workspace).  Returns 0 if p is invalid. */
+size_t ra_ring_bwd_workspace_min(const ra_problem* p);
 
 /* ra_ring_bwd — the backward ring pass of device q_shard: given its q, o, dout [b][L][h][d]
  * and lse [b][h][L] from the forward, and every shard's k_all, v_all [N][b][L][n_kv][d],

@@ -485,12 +485,16 @@ def step_bwd(q, k, v, dout, lse, delta, *, N, q_shard, kv_shard, causal=False,
     return dq_acc, dk_acc, dv_acc
 
 
-def ring_bwd_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None) -> int:
-    """Workspace of ring_bwd for q [b, L, h, d], k_all [N, b, L, n_kv, d] (0 if invalid)."""
+def ring_bwd_workspace_bytes(q, k_all, *, causal=False, layout="contiguous", scale=None,
+                             minimum=False) -> int:
+    """Workspace of ring_bwd for q [b, L, h, d], k_all [N, b, L, n_kv, d] (0 if invalid): the
+    size the library asks for, or with minimum=True the smallest it accepts (every key block of
+    the dK/dV kernel then runs whole)."""
     N, b, L, n_kv, d = k_all.shape
     p = make_problem(b=b, L=L, h=q.shape[2], n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
                      dtype=q.dtype, scale=scale)
-    return int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p)))
+    fn = _lib.lib().ra_ring_bwd_workspace_min if minimum else _lib.lib().ra_ring_bwd_workspace
+    return int(fn(ctypes.byref(p)))
 
 
 def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="contiguous",
@@ -510,11 +514,12 @@ def ring_bwd(q, k_all, v_all, o, dout, lse, *, q_shard, causal=False, layout="co
     _need(lse, "lse", (b, h, L), torch.float32)
     p = make_problem(b=b, L=L, h=h, n_kv=n_kv, d=d, N=N, causal=causal, layout=layout,
                      dtype=q.dtype, scale=scale, docs=docs)
-    need = int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p)))
+    need = int(_lib.lib().ra_ring_bwd_workspace_min(ctypes.byref(p)))
     if need == 0:
         raise RaError(int(_lib.RA_ERR_UNSUPPORTED), "ra_ring_bwd_workspace")
     if workspace is None:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        workspace = torch.empty(int(_lib.lib().ra_ring_bwd_workspace(ctypes.byref(p))), device=q.device,
+                                dtype=torch.uint8)
     if out is None:
         dq = torch.empty((b, L, h, d), device=q.device, dtype=torch.float32)
         dk = torch.empty((N, b, L, n_kv, d), device=q.device, dtype=torch.float32)

@@ -73,6 +73,7 @@ SIGNATURES = [
     ("ra_bwd_preprocess", _I, [_P, _V, _V, _V, _V]),
     ("ra_step_bwd", _I, [_P, _I, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     ("ra_ring_bwd_workspace", _S, [_P]),
+    ("ra_ring_bwd_workspace_min", _S, [_P]),
     ("ra_ring_bwd", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V]),
     ("ra_ring_bwd_timed", _I, [_P, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _S, _V, _V,
                                ctypes.POINTER(RaRingTiming)]),

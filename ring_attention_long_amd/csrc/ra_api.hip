@@ -946,10 +946,18 @@ QStage qstage_ws(const ra_problem* p) {
   return w;
 }
 
-size_t ring_bwd_workspace(const ra_problem* p) {
+// Smallest workspace of the backward ring pass: two K/V staging buffers and D.
+size_t ring_bwd_workspace_min(const ra_problem* p) {
   const size_t shard_bytes = (size_t)p->b * p->L * p->n_kv * p->d * elem_size(p);
   return 4 * align_up(shard_bytes, 256) + align_up((size_t)p->b * p->h * p->L * 4, 256);
 }
+// Short shards (no packed documents): second dK, dV buffers, so that the dK/dV kernel may split
+// the query tiles of its key blocks over two workgroups when the blocks leave units idle.
+bool bwd_split(const ra_problem* p) { return !p->doc_begin && p->L <= ra::kSplitMaxL; }
+size_t bwd_second_bytes(const ra_problem* p) {
+  return bwd_split(p) ? 2 * align_up((size_t)p->b * p->L * p->n_kv * p->d * 4, 256) : 0;
+}
+size_t ring_bwd_workspace(const ra_problem* p) { return ring_bwd_workspace_min(p) + bwd_second_bytes(p); }
 
 // The backward ring pass (ra_ring_bwd), optionally timed per step as ra_ring_fwd_timed.
 ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const void* k_all, const void* v_all,
@@ -967,13 +975,20 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
   RA_TRY(check_ptr(dk_all, "dk_all", 16));
   RA_TRY(check_ptr(dv_all, "dv_all", 16));
   RA_TRY(check_ptr(ws, "ws", 16));
-  const size_t need = ring_bwd_workspace(p);
+  const size_t need = ring_bwd_workspace_min(p);
   if (ws_bytes < need) return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
   const int N = p->N;
   if (N > kMaxRing) return fail(RA_ERR_UNSUPPORTED, "ring size N=%d above %d", N, kMaxRing);
   if (tm && N > RA_MAX_TIMED_STEPS)
     return fail(RA_ERR_INVALID_ARG, "timed ring needs N <= %d", RA_MAX_TIMED_STEPS);
   const bool timing = tm != nullptr;
+  // the second dK, dV buffers after the minimum, when the workspace holds them
+  float* dk2 = nullptr;
+  float* dv2 = nullptr;
+  if (bwd_split(p) && ws_bytes >= need + bwd_second_bytes(p)) {
+    dk2 = (float*)((char*)ws + need);
+    dv2 = (float*)((char*)dk2 + bwd_second_bytes(p) / 2);
+  }
 
   const size_t shard_elems = (size_t)p->b * p->L * p->n_kv * p->d;
   const size_t shard_bytes = shard_elems * elem_size(p);
@@ -1053,7 +1068,8 @@ ra_status ring_bwd_impl(const ra_problem* p, int32_t qs, const void* q, const vo
       if (timing && (e = hipEventRecord(t_sb[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
       const ra::StepArgs a = step_args(p, qs, src, q, kp, vp, nullptr, nullptr);
       if ((e = ra::launch_step_bwd_bf16(a, dout, lse, delta, dq, dk_all + (size_t)src * shard_elems,
-                                        dv_all + (size_t)src * shard_elems, cs, k == dq_first, true)) != hipSuccess)
+                                        dv_all + (size_t)src * shard_elems, cs, k == dq_first, true, dk2, dv2)) !=
+          hipSuccess)
         return hip_fail(e, "backward step kernel launch");
       if (timing && (e = hipEventRecord(t_se[k], cs)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
@@ -1287,6 +1303,11 @@ ra_status ra_step_bwd(const ra_problem* p, int32_t q_shard, int32_t kv_shard, co
 size_t ra_ring_bwd_workspace(const ra_problem* p) {
   if (check_bwd_problem(p) != RA_OK) return 0;
   return ring_bwd_workspace(p);
+}
+
+size_t ra_ring_bwd_workspace_min(const ra_problem* p) {
+  if (check_bwd_problem(p) != RA_OK) return 0;
+  return ring_bwd_workspace_min(p);
 }
 
 ra_status ra_ring_bwd(const ra_problem* p, int32_t qs, const void* q, const void* k_all,

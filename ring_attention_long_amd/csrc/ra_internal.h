@@ -303,6 +303,22 @@ struct StepGeometry {
 };
 StepGeometry step_geometry_bf16(const StepArgs& a);
 SplitPlan plan_split(const StepArgs& a, const StepGeometry& g, int n_cu);
+// The plan from per-block costs in tiles (w whole, wp the longer part; both nondecreasing in
+// the block index): with by_makespan the split point of the shortest list schedule over the
+// units, else only while the blocks leave units idle (at most one item per unit).
+SplitPlan plan_from_costs(const int* w, const int* wp, int n_qb, int units, bool by_makespan);
+// Compute units of the current device (looked up once per device; 256 if the query fails).
+inline int device_cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
 // The same for a launch of several ring steps (launch_steps_bf16 with a second accumulator):
 // a split block runs each of its KV shards' key ranges as two halves, one per part.
 SplitPlan plan_split_batch(const StepArgs& a, const ShardBatch& sb, const StepGeometry& g, int n_cu);
@@ -357,8 +373,13 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 // Adds this step's contributions to dq [b][L][h][d], dk and dv [b][L][n_kv][d] (fp32), or,
 // with set_dq / set_dkdv, stores them there in place of what the buffer held (every row of
 // the shard is written, zeros where the step contributes nothing).
+// With dk2, dv2 ([b][L][n_kv][d] fp32, any contents; only with set_dkdv and no packed
+// documents) the dK/dV kernel may run the query tiles of a key block as two workgroups when
+// the key blocks leave compute units idle: the second half's dK, dV go to dk2, dv2 and are
+// added into dk, dv after the kernel.
 hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float* lse,
                                 const float* delta, float* dq, float* dk, float* dv, hipStream_t s,
-                                bool set_dq = false, bool set_dkdv = false);
+                                bool set_dq = false, bool set_dkdv = false, float* dk2 = nullptr,
+                                float* dv2 = nullptr);
 
 }  // namespace ra

@@ -155,7 +155,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ delta,
                                                                  float* __restrict__ dk, float* __restrict__ dv,
-                                                                 KvForm kf, int set_out) {
+                                                                 KvForm kf, int set_out, SplitPlan plan,
+                                                                 float* __restrict__ dk2, float* __restrict__ dv2) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   // Per row of a staged tile, one more 16-wide k-step for the products S = Q K^T and
   // dP = dO V^T: columns 0 and 1 hold the bf16 pair (hi, lo) of -LSE / scale (S) or -D (dP),
@@ -174,7 +175,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
   const int lane = tid & 63, lk = lane & 31, lg = lane >> 5;
   const int L = a.L;
   const int G = a.h / a.n_kv;
-  const int kb = (int)(blockIdx.x / (a.n_kv * a.b));   // keys early in the shard see more queries: first
+  // key blocks heaviest first (keys early in the shard see more queries); a split block runs
+  // the first half of its (head, query tile) iterations as part 0 and the rest as part 1,
+  // which writes its dK, dV into the second buffers
+  const int n_kb = (L + KB - 1) / KB;
+  int kbp, part;
+  split_item(plan, n_kb, (int)(blockIdx.x / (a.n_kv * a.b)), kbp, part);
+  const int kb = n_kb - 1 - kbp;
+  const bool split_blk = kbp >= plan.split_from;
+  if (part) {
+    dk = dk2;
+    dv = dv2;
+  }
   const int g = blockIdx.x % a.n_kv;
   const int bi = (blockIdx.x / a.n_kv) % a.b;
   const int u0 = kb * KB;
@@ -212,7 +224,14 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     if (range(mid).lo >= u0 + KB) t_top = mid;
     else t_stop = mid + 1;
   }
-  if (t_lo >= t_stop) {                     // no query of this step sees these keys
+  const int qt_first = t_lo / TILE_ROWS;
+  const int t_end = (t_stop + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
+  const int n_qt_r = t_end / TILE_ROWS - qt_first;           // query tiles of the range
+  const int n_iter_all = n_qt_r * G;                         // (head, query tile) pairs
+  const int half = (n_iter_all + 1) / 2;
+  const int i_first = split_blk && part ? half : 0;          // this workgroup's iterations
+  const int n_iter = split_blk ? (part ? n_iter_all - half : half) : n_iter_all;
+  if (t_lo >= t_stop || n_iter <= 0) {     // no query of this step (or part) sees these keys
     if (set_out && grp == 0 && u < L) {     // their gradients are zero
       float* kz = dk + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
       float* vz = dv + (((int64_t)bi * L + u) * a.n_kv + g) * D + 4 * lg;
@@ -226,9 +245,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
     }
     return;
   }
-  const int qt_first = t_lo / TILE_ROWS;
-  const int t_end = (t_stop + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS;
-  const int n_iter = (t_end / TILE_ROWS - qt_first) * G;   // (head, query tile) pairs
 
   // resident K rows of this lane's key (B operand [k = d][n = key])
   const int64_t krow = (((int64_t)bi * L + min(u, L - 1)) * a.n_kv + g) * D + lg * 8;
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(StepArgs a, con
       ++c.hq;
     }
   };
-  const Cursor first = {g * G, qt_first * TILE_ROWS};
+  const Cursor first = {g * G + i_first / n_qt_r, (qt_first + i_first % n_qt_r) * TILE_ROWS};
   // Q and dO rows of batch bi: one descriptor each over its L rows of all heads, so that
   // rows past the shard end read zeros; the head and row go into the scalar offset.
   const dma_rsrc q_rsrc = make_dma_rsrc((const __bf16*)a.q + (int64_t)bi * L * a.h * D, (unsigned)L * q_stride);
@@ -886,6 +902,22 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(StepArgs a, const
     }
 }
 
+// dk[bi][u] += dk2[bi][u] and dv likewise for keys u < rows of every batch row (the second
+// halves of split key blocks, which are the first key blocks of the shard); 4 floats a thread.
+__global__ __launch_bounds__(256) void add_second_kernel(float* __restrict__ dk, float* __restrict__ dv,
+                                                        const float* __restrict__ dk2, const float* __restrict__ dv2,
+                                                        int64_t row_floats, int64_t batch_floats, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t per_b = row_floats / 4;
+  const int64_t off = (i / per_b) * batch_floats + (i % per_b) * 4;
+  f32x4 a = *(const f32x4*)(dk + off), b = *(const f32x4*)(dk2 + off);
+  *(f32x4*)(dk + off) = a + b;
+  a = *(const f32x4*)(dv + off);
+  b = *(const f32x4*)(dv2 + off);
+  *(f32x4*)(dv + off) = a + b;
+}
+
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int b, int L, int h,
@@ -899,7 +931,7 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 
 hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float* lse,
                                 const float* delta, float* dq, float* dk, float* dv, hipStream_t s,
-                                bool set_dq, bool set_dkdv) {
+                                bool set_dq, bool set_dkdv, float* dk2, float* dv2) {
   const int G = a.h / a.n_kv;
   const int Hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
   const int PB = 8 / Hw;
@@ -914,8 +946,38 @@ hipError_t launch_step_bwd_bf16(const StepArgs& a, const void* dout, const float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const KvForm kf = make_kv_form(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_k), dim3(KV_THREADS), 0, s, a,
-                     (const __bf16*)dout, lse, delta, dk, dv, kf, (int)set_dkdv);
+  // Key blocks whose (head, query tile) iterations run as two workgroups: only while the key
+  // blocks leave compute units idle (as the forward's steps), from their iteration counts (the
+  // query tiles from the first row that sees the block to the shard end, times G: no packed
+  // documents here, so every row's keys are a prefix).  Item i of the plan's order is key block
+  // n_kb - 1 - (its block index): the heaviest blocks are the first keys.
+  SplitPlan plan{};
+  plan.split_from = n_kb;
+  if (dk2 && dv2 && set_dkdv && !a.doc_begin && n_kb <= kSplitMaxBlocks) {
+    int w[kSplitMaxBlocks], wp[kSplitMaxBlocks];
+    const int n_qt = (a.L + TILE_ROWS - 1) / TILE_ROWS;
+    for (int kbp = 0; kbp < n_kb; ++kbp) {
+      const int u0 = (n_kb - 1 - kbp) * KB;
+      int lo = 0, hi = a.L;             // first row whose key limit passes u0
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (kv_limit(a.causal, a.layout, a.N, a.L, a.q_shard, a.kv_shard, mid) > u0) hi = mid;
+        else lo = mid + 1;
+      }
+      w[kbp] = lo < a.L ? (n_qt - lo / TILE_ROWS) * G : 0;
+      wp[kbp] = (w[kbp] + 1) / 2;
+    }
+    plan = plan_from_costs(w, wp, n_kb, device_cu_count() / (a.n_kv * a.b), false);
+  }
+  const int64_t grid_kp = (int64_t)(plan.split_from + 2 * (n_kb - plan.split_from)) * a.n_kv * a.b;
+  if (grid_kp > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid_kp), dim3(KV_THREADS), 0, s, a,
+                     (const __bf16*)dout, lse, delta, dk, dv, kf, (int)set_dkdv, plan, dk2, dv2);
+  if ((e = hipGetLastError()) != hipSuccess || plan.split_from >= n_kb) return e;
+  const int rows = min(a.L, (n_kb - plan.split_from) * KB);      // keys of the split blocks
+  const int64_t row_floats = (int64_t)rows * a.n_kv * D, n4 = (int64_t)a.b * row_floats / 4;
+  hipLaunchKernelGGL(add_second_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dk, dv, dk2, dv2,
+                     row_floats, (int64_t)a.L * a.n_kv * D, n4);
   return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ int main() {
   expect(ra_finalize(nullptr, Ff, F, nullptr) == RA_ERR_INVALID_ARG, "finalize null problem");
   expect(ra_bwd_preprocess(nullptr, F, F, Ff, nullptr) == RA_ERR_INVALID_ARG, "preprocess null problem");
   expect(ra_ring_fwd_workspace(nullptr) == 0 && ra_ring_bwd_workspace(nullptr) == 0 &&
+             ra_ring_bwd_workspace_min(nullptr) == 0 &&
              ra_ring_bwd_kv_stationary_workspace(nullptr) == 0 && ra_ulysses_fwd_workspace(nullptr) == 0 &&
              ra_ulysses_bwd_workspace(nullptr) == 0,
          "workspace of null problem");
@@ -127,7 +128,8 @@ int main() {
   big.N = 2;
   expect(ra_ring_fwd_workspace(&big) > RA_NOALLOC_SCRATCH_BYTES, "big workspace");
   expect(ra_ring_fwd_noalloc(&big, 0, F, F, F, F, Ff, nullptr, nullptr) == RA_ERR_WORKSPACE, "noalloc oversized");
-  const size_t bws = ra_ring_bwd_workspace(&p);
+  const size_t bws = ra_ring_bwd_workspace_min(&p);
+  expect(ra_ring_bwd_workspace(&p) > bws, "ring_bwd workspace with the second dK, dV buffers");
   expect(ra_ring_bwd(&p, 0, F, F, F, F, F, Ff, Ff, Ff, Ff, F, bws - 1, nullptr, nullptr) == RA_ERR_WORKSPACE,
          "ring_bwd workspace");
   expect(ra_ring_bwd_timed(&p, 0, F, F, F, F, F, Ff, Ff, Ff, Ff, F, bws, nullptr, nullptr, nullptr) ==

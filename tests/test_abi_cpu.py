@@ -120,7 +120,7 @@ def test_ring_fwd_rejects_small_workspace():
     assert lib.ra_ring_fwd_workspace(ctypes.byref(p0)) == bneed_f
     assert lib.ra_ring_fwd(ctypes.byref(p0), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - second - 1, None,
                            None) == _lib.RA_ERR_WORKSPACE
-    bneed = lib.ra_ring_bwd_workspace(ctypes.byref(p))
+    bneed = lib.ra_ring_bwd_workspace_min(ctypes.byref(p))
     assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  bneed, None, None, None) == _lib.RA_ERR_INVALID_ARG
     assert lib.ra_ring_bwd_timed(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -308,19 +308,25 @@ def test_backward_rejects_bad_shards_pointers_and_workspace():
     args[7] = mis                                        # dk_acc misaligned
     assert lib.ra_step_bwd(ctypes.byref(p), 0, 0, *args, None) == _lib.RA_ERR_INVALID_ARG
     assert lib.ra_bwd_preprocess(ctypes.byref(p), FAKE, None, FAKE, None) == _lib.RA_ERR_INVALID_ARG
-    need = lib.ra_ring_bwd_workspace(ctypes.byref(p))
+    need = lib.ra_ring_bwd_workspace_min(ctypes.byref(p))
     st = lib.ra_ring_bwd(ctypes.byref(p), 0, *([FAKE] * 10), need - 1, None, None)
     assert st == _lib.RA_ERR_WORKSPACE
     assert lib.ra_ring_bwd(ctypes.byref(p), -1, *([FAKE] * 10), need, None, None) == _lib.RA_ERR_INVALID_ARG
 
 
 def test_backward_workspace_is_two_kv_buffers_plus_delta():
-    """Double-buffered K and V staging (as in the forward) plus D = rowsum(dO * O)."""
+    """Minimum: double-buffered K and V staging (as in the forward) plus D = rowsum(dO * O).
+    Asked for: for shards of L <= 4096, then second dK and dV buffers (fp32 [b][L][n_kv][d]
+    each) for key blocks whose query tiles run as two workgroups."""
     lib = _lib.lib()
-    p = _prob(L=1000, b=2)
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = 4 * pad(2 * 1000 * 2 * 128 * 2) + pad(2 * 4 * 1000 * 4)
-    assert lib.ra_ring_bwd_workspace(ctypes.byref(p)) == want
+    for L, second in ((1000, True), (4096, True), (4097, False)):
+        p = _prob(L=L, b=2)
+        want = 4 * pad(2 * L * 2 * 128 * 2) + pad(2 * 4 * L * 4)
+        assert lib.ra_ring_bwd_workspace_min(ctypes.byref(p)) == want
+        extra = 2 * pad(2 * L * 2 * 128 * 4) if second else 0
+        assert lib.ra_ring_bwd_workspace(ctypes.byref(p)) == want + extra, L
+    assert lib.ra_ring_bwd_workspace_min(ctypes.byref(_prob(d=64))) == 0
 
 
 # ------------------------------------------------------------------ packed documents (host side)

@@ -12,7 +12,7 @@ import ring_attention_long_amd as ra
 from gpu_helpers import (BWD_FULL, BWD_FULL_KV_HEAD, BWD_FULL_SEED, announce, bwd_full_cols,
                          bwd_full_key_grads, f64, full_size_rows, gather_cols, make_inputs, run_threads,
                          to_gpu)
-from oracle import LAYOUTS, ring_order, shard_dq_rows, shard_grads, shard_tokens
+from oracle import LAYOUTS, key_grads, ring_order, shard_dq_rows, shard_grads, shard_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +26,18 @@ def check_grad(got, ref, what):
     assert err.mean() <= 2e-3 * scale, what
 
 
-def _run(cfg, layout, causal, shard, seed, copy_stream="auto"):
+def _run(cfg, layout, causal, shard, seed, copy_stream="auto", minimum_workspace=False):
     N = cfg["N"]
     inp = make_inputs(**cfg, q_shard=shard, seed=seed, dtype="bf16", with_dout=True)
     q, k_all, v_all = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all"))
     dout = to_gpu(inp["dout"], "bf16")
     o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+    ws = None
+    if minimum_workspace:   # every key block of the dK/dV kernel whole, as in ra_step_bwd
+        n = ra.ring_bwd_workspace_bytes(q, k_all, causal=causal, layout=layout, minimum=True)
+        ws = torch.empty(n, device="cuda", dtype=torch.uint8)
     dq, dk, dv = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal,
-                             layout=layout, copy_stream=copy_stream)
+                             layout=layout, copy_stream=copy_stream, workspace=ws)
     torch.cuda.synchronize()
     return inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv)
 
@@ -105,10 +109,12 @@ def test_ring_bwd_large_logits(layout):
 
 
 def test_step_bwd_sums_to_ring_bwd():
-    """ra_step_bwd over the ring order, with ra_bwd_preprocess, equals ra_ring_bwd."""
+    """ra_step_bwd over the ring order, with ra_bwd_preprocess, equals ra_ring_bwd given the
+    minimum workspace (the same kernels: every key block of the dK/dV kernel whole)."""
     cfg = dict(b=1, L=160, h=8, n_kv=2, d=128, N=4)
     shard = 1
-    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=95)
+    inp, (q, k_all, v_all, dout, o, lse), (dq, dk, dv) = _run(cfg, "striped", True, shard, seed=95,
+                                                              minimum_workspace=True)
     delta = ra.bwd_preprocess(o, dout)
     dq2 = torch.zeros_like(dq)
     dk2 = torch.zeros_like(dk)
@@ -237,3 +243,60 @@ def test_ring_bwd_overwrites_every_output_element():
             torch.cuda.synchronize()
             for a, b in zip(ref, got):
                 assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cfg,layout,causal", [
+    (dict(b=1, L=2048, h=32, n_kv=8, d=128, N=8), "striped", True),     # 16 key blocks x 8 KV heads
+    (dict(b=2, L=700, h=6, n_kv=2, d=128, N=3), "zigzag", True),        # GQA 3, ragged, two batch rows
+    (dict(b=1, L=520, h=8, n_kv=4, d=128, N=4), "contiguous", False),
+    (dict(b=1, L=384, h=4, n_kv=4, d=128, N=4), "contiguous", True),
+])
+def test_ring_bwd_split_key_blocks(cfg, layout, causal):
+    """Short shards whose key blocks leave compute units idle: with the second dK, dV buffers in
+    the workspace the dK/dV kernel runs the query tiles of the heaviest key blocks as two
+    workgroups and adds the halves after the kernel.  Against the oracle (sampled rows and keys
+    at L = 2048, everything below); against the pass with the minimum workspace (whole key
+    blocks: dQ bit-identical, dK and dV close and not identical, which shows the split ran);
+    and with the workspace filled with NaN beforehand (bit-identical)."""
+    N, L = cfg["N"], cfg["L"]
+    shard = N - 1
+    announce("ring_bwd split key blocks", layout, causal, cfg)
+    inp = make_inputs(**cfg, q_shard=shard, seed=2300, dtype="bf16", with_dout=True)
+    q, k_all, v_all, dout = (to_gpu(inp[x], "bf16") for x in ("q", "k_all", "v_all", "dout"))
+    o, lse = ra.ring_fwd(q, k_all, v_all, q_shard=shard, causal=causal, layout=layout)
+    full = ra.ring_bwd_workspace_bytes(q, k_all, causal=causal, layout=layout)
+    small = ra.ring_bwd_workspace_bytes(q, k_all, causal=causal, layout=layout, minimum=True)
+    assert full > small > 0
+    outs = {}
+    for name, nbytes, nan in (("split", full, False), ("nan", full, True), ("whole", small, False)):
+        ws = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+        if nan:
+            ws.view(-1)[: nbytes // 4 * 4].view(torch.float32).fill_(float("nan"))
+        outs[name] = ra.ring_bwd(q, k_all, v_all, o, dout, lse, q_shard=shard, causal=causal, layout=layout,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    dq, dk, dv = outs["split"]
+    assert all(torch.equal(a_, b_) for a_, b_ in zip(outs["split"], outs["nan"]))
+    assert torch.equal(dq, outs["whole"][0])
+    for a_, b_, what in ((dk, outs["whole"][1], "dk"), (dv, outs["whole"][2], "dv")):
+        d = float((a_ - b_).abs().max())
+        announce(f"{what} split vs whole: max |diff| {d:.3e}")
+        assert d <= 1e-3 * max(1.0, float(b_.abs().max()))
+    assert not (torch.equal(dk, outs["whole"][1]) and torch.equal(dv, outs["whole"][2])), "no key block split"
+    x = {k_: inp[k_].astype(np.float64) for k_ in ("q", "k_all", "v_all", "dout")}
+    if L <= 1024:
+        rdq, rdk, rdv = shard_grads(x["q"], x["k_all"], x["v_all"], x["dout"], N=N, shard=shard,
+                                    layout=layout, causal=causal)
+        check_grad(dq, rdq, "split dq")
+        check_grad(dk, rdk, "split dk")
+        check_grad(dv, rdv, "split dv")
+    else:
+        rows = full_size_rows(L, 2301)
+        rdq = oracle_dq_rows(x["q"], x["k_all"], x["v_all"], x["dout"], rows, N=N, shard=shard, layout=layout,
+                             causal=causal)
+        check_grad(dq[:, torch.as_tensor(rows, device="cuda")], rdq, "split dq sampled rows")
+        cols = [(j, c) for j in range(N) for c in (0, 1, 63, 64, 127, 128, 129, L // 2, L - 1)]
+        rdk, rdv = key_grads(x["q"][None], x["dout"][None], x["k_all"], x["v_all"], N=N, query_shards=[shard],
+                             kv_head=3, cols=cols, layout=layout, causal=causal)
+        check_grad(gather_cols(dk, cols, 3), rdk, "split dk sampled keys")
+        check_grad(gather_cols(dv, cols, 3), rdv, "split dv sampled keys")
